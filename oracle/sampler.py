@@ -1,0 +1,67 @@
+"""Float64 oracle of the token sampler (ds4.c 学习笔记, 端到端推理流程,
+阶段四 4.3 采样, with the argmax of 阶段六 温度覆盖 and the function index).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Steps as the page orders them: divide the logits by the temperature, turn
+them into probabilities, keep the most probable tokens until their total
+reaches top_p (sort descending, accumulate, drop the rest), then walk the
+vocabulary with r = u * (sum of kept probabilities), subtracting each
+token's probability until r <= 0.  Temperature 0 means argmax.
+
+Readings where the page is silent:
+  * temperature <= 0: argmax, first index among equal maxima; no draw;
+  * the probabilities are exp((l - max l) / temperature) (the same as
+    exp(l / temperature) up to a common factor);
+  * ties in the descending sort go to the lower index; the token whose
+    probability makes the running total reach top_p is kept, at least one
+    token is kept, top_p >= 1 keeps everything;
+  * the roulette walks the vocabulary in index order and skips tokens the
+    top-p step dropped; if rounding leaves r > 0 after the last kept token,
+    that last kept token is returned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def argmax(logits) -> int:
+    """Greedy pick: the first index of the largest logit."""
+    return int(np.argmax(np.asarray(logits, dtype=np.float64)))
+
+
+def nucleus(q: np.ndarray, top_p: float) -> np.ndarray:
+    """Boolean mask of the tokens top-p keeps.  q: unnormalised weights."""
+    n = q.shape[0]
+    if top_p >= 1.0:
+        return np.ones(n, dtype=bool)
+    order = np.lexsort((np.arange(n), -q))        # q descending, then index
+    cum = np.cumsum(q[order]) / np.sum(q)
+    n_keep = int(np.searchsorted(cum, top_p, side="left")) + 1
+    n_keep = min(max(n_keep, 1), n)
+    keep = np.zeros(n, dtype=bool)
+    keep[order[:n_keep]] = True
+    return keep
+
+
+def sample(logits, temperature: float, top_p: float, u: float) -> dict:
+    """Sample one token id.  u in [0, 1) is the generator's draw.
+
+    Returns dict(token, n_kept, kept_sum, r, gap) where gap is the smallest
+    distance, relative to kept_sum, between r and a running-sum boundary of
+    the roulette; a test uses it to spot draws that sit on a boundary.
+    """
+    l = np.asarray(logits, dtype=np.float64)
+    if temperature <= 0.0:
+        return dict(token=argmax(l), n_kept=1, kept_sum=1.0, r=0.0, gap=np.inf)
+    q = np.exp((l - np.max(l)) / temperature)
+    keep = nucleus(q, top_p)
+    kept_idx = np.nonzero(keep)[0]                 # index order
+    running = np.cumsum(q[kept_idx])
+    S = running[-1]
+    r = u * S
+    pos = int(np.searchsorted(running, r, side="left"))   # first running >= r
+    tok = int(kept_idx[min(pos, kept_idx.size - 1)])
+    gap = float(np.min(np.abs(running - r)) / S)
+    return dict(token=tok, n_kept=int(kept_idx.size), kept_sum=float(S),
+                r=float(r), gap=gap)

@@ -1,0 +1,120 @@
+"""Pins of the oracle's sampler (阶段四 4.3 采样): closed forms on small
+vocabularies, the page's own roulette loop, temperature -> 0 and
+top_p -> 0 limits."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.sampler import sample, nucleus, argmax
+
+
+def _page_roulette(probs, kept, u):
+    # the page's loop: rnd = u * sum; for i: rnd -= probs[i]; if rnd <= 0: return i
+    total = sum(p for p, k in zip(probs, kept) if k)
+    rnd = u * total
+    last = None
+    for i, (p, k) in enumerate(zip(probs, kept)):
+        if not k:
+            continue
+        last = i
+        rnd -= p
+        if rnd <= 0.0:
+            return i
+    return last
+
+
+def test_argmax_first_index():
+    assert argmax([1.0, 3.0, 3.0, 2.0]) == 1
+    assert sample([1.0, 3.0, 3.0], 0.0, 0.9, 0.7)["token"] == 1
+
+
+def test_closed_form_no_top_p():
+    # weights proportional to 1, 2, 3 at temperature 1: boundaries at 1/6, 3/6
+    l = np.log([1.0, 2.0, 3.0])
+    for u, want in ((0.0, 0), (0.1, 0), (0.16, 0), (0.17, 1), (0.49, 1), (0.51, 2), (0.999, 2)):
+        assert sample(l, 1.0, 1.0, u)["token"] == want, u
+
+
+def test_temperature_scales_logits():
+    # at temperature 2 the weights become sqrt(1), sqrt(4), sqrt(9) = 1, 2, 3
+    l = np.log([1.0, 4.0, 9.0])
+    for u, want in ((0.1, 0), (0.3, 1), (0.6, 2)):
+        assert sample(l, 2.0, 1.0, u)["token"] == want
+
+
+def test_top_p_keeps_crossing_token():
+    # weights 1, 2, 3, 4 (sum 10); descending cumulative 0.4, 0.7, 0.9, 1.0
+    q = np.array([1.0, 2.0, 3.0, 4.0])
+    assert nucleus(q, 0.5).tolist() == [False, False, True, True]
+    assert nucleus(q, 0.7).tolist() == [False, False, True, True]   # reaches 0.7 exactly
+    assert nucleus(q, 0.71).tolist() == [False, True, True, True]
+    assert nucleus(q, 0.1).tolist() == [False, False, False, True]
+    assert nucleus(q, 1.0).all()
+    l = np.log(q)
+    # kept {2, 3}, kept sum 7, walked in index order: boundary at 3/7
+    assert sample(l, 1.0, 0.5, 0.42)["token"] == 2
+    assert sample(l, 1.0, 0.5, 0.43)["token"] == 3
+
+
+def test_top_p_ties_go_to_lower_index():
+    q = np.array([2.0, 1.0, 2.0, 1.0])
+    assert nucleus(q, 0.25).tolist() == [True, False, False, False]
+    assert nucleus(q, 0.34).tolist() == [True, False, True, False]
+    assert nucleus(q, 0.7).tolist() == [True, True, True, False]
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_matches_page_loop(seed):
+    r = np.random.default_rng(seed)
+    l = r.normal(size=300) * 3
+    for T, p in ((0.7, 0.95), (1.0, 0.5), (1.5, 1.0)):
+        q = np.exp((l - l.max()) / T)
+        kept = nucleus(q, p)
+        for u in r.random(50):
+            got = sample(l, T, p, u)
+            if got["gap"] < 1e-12:
+                continue
+            assert got["token"] == _page_roulette(q.tolist(), kept.tolist(), u)
+            assert kept[got["token"]]
+
+
+def test_grid_counts_closed_form():
+    r = np.random.default_rng(7)
+    l = r.normal(size=40)
+    T, p, N = 0.8, 0.9, 4096
+    q = np.exp((l - l.max()) / T)
+    kept = nucleus(q, p)
+    idx = np.nonzero(kept)[0]
+    C = np.cumsum(q[idx]) / q[idx].sum()
+    counts = np.zeros(40, dtype=int)
+    for n in range(N):
+        counts[sample(l, T, p, n / N)["token"]] += 1
+    # u = n/N lands on token idx[i] iff C[i-1] < u <= C[i]  (first cum >= u)
+    grid = np.arange(N) / N
+    prev = np.concatenate([[-1.0], C[:-1]])
+    want = np.zeros(40, dtype=int)
+    for i, t in enumerate(idx):
+        want[t] = np.sum((grid > prev[i]) & (grid <= C[i]))
+    np.testing.assert_array_equal(counts, want)
+    assert counts[~kept].sum() == 0
+
+
+def test_low_temperature_and_tiny_top_p_are_argmax():
+    r = np.random.default_rng(8)
+    for _ in range(20):
+        l = r.normal(size=1000)
+        srt = np.sort(l)
+        if srt[-1] - srt[-2] < 1e-2:
+            l[np.argmax(l)] += 1e-2
+        a = argmax(l)
+        for u in (0.0, 0.3, 0.999999):
+            assert sample(l, 1e-4, 0.95, u)["token"] == a
+            assert sample(l, 1.0, 1e-9, u)["token"] == a
+            assert sample(l, 0.0, 0.95, u)["token"] == a
+
+
+def test_underflow_keeps_one_token():
+    l = np.array([0.0, -1e4, -2e4])
+    assert sample(l, 0.5, 0.95, 0.99)["token"] == 0
