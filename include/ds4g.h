@@ -1,0 +1,171 @@
+/*
+ * ds4g -- one DeepSeek-V4-style transformer layer (ds4 / DwarfStar), its
+ * layer-major prefill, its single-token decode, and the lm_head sampler, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed follows the layer pseudo-code on the ds4-learning page
+ * 端到端推理流程 (ds4.c 学习笔记), section 阶段四 4.2 单层前向:
+ *
+ *   x  = RMSNorm(h) * g1
+ *   c  = A x ;  [q | k | v] = B c          low-rank QKV (one shared bottleneck)
+ *   q, k <- RoPE(q, k, pos)                interleaved pairs, theta_i = base^(-2i/rope_dim)
+ *   ring[pos mod W] <- (k, v)              KV cache kept as a W-slot ring
+ *   o  = MQA(q, ring)                      H heads share one K/V; window of W keys incl. self
+ *   h2 = h + W_o o
+ *   y  = RMSNorm(h2) * g2
+ *   s  = W_r y ; p = softmax(s) ; S = top-k(s)          (ties -> lower index)
+ *   out = h2 + sum_{e in S} p_e D_e(silu(G_e y) * U_e y) + D_sh(silu(G_sh y) * U_sh y)
+ *
+ * Prefill runs this for T tokens layer-major (section 阶段三 逐层批处理);
+ * decode is T = 1 (阶段四).  The lm_head and sampler follow 阶段四 4.3 采样:
+ * logits = W_lm RMSNorm(x) * g_f, then temperature, top-p, roulette in
+ * vocabulary order, or argmax at temperature 0.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument named "device" is HIP device memory owned by the
+ *     caller; the library allocates nothing and keeps no global state.
+ *   - Weight matrices are row-major [out, in], all in cfg->wdtype
+ *     (DS4G_BF16: raw bf16 bits; DS4G_F32: float).  Expert stacks are
+ *     [n_experts, out, in].  Gains (norm weights) are in wdtype too.
+ *   - The residual stream x is fp32, updated in place.
+ *   - The KV ring holds K (after RoPE) and V as bf16 [window, head_dim];
+ *     position p lives in slot p % window; *pos (device int64) is the
+ *     position of the next token and is advanced by every call.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  They never synchronise and never call the allocator, so a
+ *     decode step can be captured in a HIP graph and replayed.
+ *   - Every argument check runs on the host before anything is enqueued; on
+ *     an error nothing is written and a negative ds4g_status is returned.
+ *     DS4G_ERR_HIP reports a failed launch (the stream state is then
+ *     undefined).
+ *   - A ring and a workspace must not be used by two calls at once.
+ */
+#ifndef DS4G_H
+#define DS4G_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DS4G_OK = 0,
+  DS4G_ERR_INVALID_ARG = -1,  /* null pointer, non-positive or inconsistent size */
+  DS4G_ERR_UNSUPPORTED = -2,  /* a size outside what the kernels implement      */
+  DS4G_ERR_WORKSPACE = -3,    /* ws_bytes smaller than ds4g_workspace_bytes()   */
+  DS4G_ERR_HIP = -4           /* a HIP launch failed                            */
+} ds4g_status;
+
+typedef enum { DS4G_F32 = 0, DS4G_BF16 = 1 } ds4g_dtype;
+
+/* Layer dimensions.  Supported: head_dim in {64, 128}; rope_dim even and
+ * <= head_dim (0 = head_dim); window in [1, 128]; n_experts in [top_k+1, 512];
+ * top_k in [1, 8]; hidden, qkv_rank, ffn_inter, shared_inter multiples of 64;
+ * n_heads*head_dim a multiple of 64. */
+typedef struct {
+  int32_t hidden;        /* d: residual width (4096)                         */
+  int32_t n_heads;       /* H: query heads (64); one K/V head (MQA)          */
+  int32_t head_dim;      /* dh (128)                                         */
+  int32_t qkv_rank;      /* r: low-rank bottleneck of the QKV projection     */
+  int32_t window;        /* W: sliding-window length (128)                   */
+  int32_t n_experts;     /* E: routed experts (256)                          */
+  int32_t top_k;         /* k: experts per token (6)                         */
+  int32_t ffn_inter;     /* I: SwiGLU inner width of a routed expert         */
+  int32_t shared_inter;  /* inner width of the shared expert                 */
+  int32_t rope_dim;      /* rotated tail of each head; 0 = whole head        */
+  float rope_base;       /* 10000                                            */
+  float rms_eps;         /* 1e-6                                             */
+  int32_t wdtype;        /* ds4g_dtype of every weight                       */
+} ds4g_layer_cfg;
+
+/* Device pointers to one layer's weights ([out, in], wdtype). */
+typedef struct {
+  const void *attn_norm;  /* [d]                     g1                      */
+  const void *qkv_a;      /* [r, d]                  A                       */
+  const void *qkv_b;      /* [H*dh + 2*dh, r]        B: q heads, then k, v   */
+  const void *wo;         /* [d, H*dh]               W_o                     */
+  const void *ffn_norm;   /* [d]                     g2                      */
+  const void *router;     /* [E, d]                  W_r                     */
+  const void *gate;       /* [E, I, d]               G_e                     */
+  const void *up;         /* [E, I, d]               U_e                     */
+  const void *down;       /* [E, d, I]               D_e                     */
+  const void *sh_gate;    /* [Is, d]                                         */
+  const void *sh_up;      /* [Is, d]                                         */
+  const void *sh_down;    /* [d, Is]                                         */
+} ds4g_layer_weights;
+
+/* One layer's KV ring (device memory). */
+typedef struct {
+  void *k;        /* bf16 [window, head_dim], K after RoPE                   */
+  void *v;        /* bf16 [window, head_dim]                                 */
+  int64_t *pos;   /* position of the next token (>= 0)                       */
+} ds4g_kv_ring;
+
+/* Optional routing outputs (device memory; any member may be NULL). */
+typedef struct {
+  int32_t *topk_idx;       /* [T, k]  chosen experts, descending logit       */
+  float *topk_w;           /* [T, k]  their softmax probabilities            */
+  int32_t *expert_count;   /* [E]                                            */
+  int32_t *expert_offset;  /* [E+1]  exclusive scan of expert_count          */
+  int32_t *perm;           /* [T*k]  entries t*k+j grouped by expert, token
+                                     order inside an expert                  */
+  float *router_in;        /* [T, d]  y = RMSNorm(h2)*g2 as the router saw it */
+  float *router_logits;    /* [T, E]  s                                       */
+} ds4g_routing;
+
+/* Bytes of workspace a layer call needs for up to max_tokens tokens, or that
+ * ds4g_lmhead_sample needs for `vocab` (pass cfg = NULL for the lm_head
+ * alone).  Returns 0 on invalid arguments. */
+size_t ds4g_workspace_bytes(const ds4g_layer_cfg *cfg, int32_t max_tokens,
+                            int32_t vocab);
+
+/* Layer-major prefill of T >= 1 tokens at positions *ring->pos ..
+ * *ring->pos + T - 1 (阶段三 逐层批处理; 阶段四 4.2 for the layer).
+ *   x:  device fp32 [T, hidden], the layer input h; overwritten with the
+ *       layer output.
+ *   ring: updated with the last min(T, window) keys/values; *pos += T.
+ *   routing: optional outputs (NULL = none).
+ *   ws: device workspace of at least ds4g_workspace_bytes(cfg, T, 0) bytes,
+ *       256-byte aligned.
+ * Returns DS4G_OK or a negative ds4g_status. */
+int ds4g_layer_prefill(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
+                       ds4g_kv_ring *ring, float *x, int32_t T,
+                       ds4g_routing *routing, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* One decode step (T = 1) of the layer at position *ring->pos (阶段四 4.2).
+ * Same contract as ds4g_layer_prefill with T = 1; uses the bandwidth-bound
+ * decode kernels.  x: device fp32 [hidden]. */
+int ds4g_layer_decode(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
+                      ds4g_kv_ring *ring, float *x, ds4g_routing *routing,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* lm_head + sampler for one token (阶段四 4.3 采样).
+ *   final_norm: device [hidden] gain in wdtype, or NULL to skip the norm.
+ *   w_lm:   device [vocab, hidden] in wdtype.
+ *   x:      device fp32 [hidden].
+ *   temperature <= 0 picks the argmax (first index among equal maxima) and
+ *   leaves *rng_state alone; otherwise q_i = exp((l_i - max l)/temperature),
+ *   top-p keeps the most probable tokens (ties -> lower index) until their
+ *   share reaches top_p (the crossing token is kept; top_p >= 1 keeps all),
+ *   and the roulette walks the vocabulary in index order with
+ *   r = u * (sum of kept q), u from one splitmix64 draw of *rng_state
+ *   (top 24 bits / 2^24).
+ *   rng_state: device uint64 (may be NULL when temperature <= 0).
+ *   logits: device fp32 [vocab] out.  token: device int32 out.
+ *   ws: at least ds4g_workspace_bytes(NULL, 0, vocab) bytes. */
+int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype,
+                       const void *final_norm, float rms_eps, const void *w_lm,
+                       const float *x, float temperature, float top_p,
+                       uint64_t *rng_state, float *logits, int32_t *token,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a ds4g_status value. */
+const char *ds4g_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DS4G_H */

@@ -1,0 +1,189 @@
+"""Python binding of libds4g (include/ds4g.h): argument marshalling only.
+
+Every step of the layer, the lm_head and the sampler runs in the HIP kernels
+of libds4g.so.  torch is used for device memory and streams; this module only
+turns tensors into pointers and sizes and calls the C ABI.  There is no
+fallback: if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libds4g.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+
+# ds4g.h declares these functions; the ABI test checks the header agrees.
+EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_prefill", "ds4g_layer_decode",
+           "ds4g_lmhead_sample", "ds4g_status_string")
+
+
+class LayerCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("qkv_rank", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("ffn_inter", ctypes.c_int32),
+                ("shared_inter", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("wdtype", ctypes.c_int32)]
+
+
+WEIGHT_NAMES = ("attn_norm", "qkv_a", "qkv_b", "wo", "ffn_norm", "router", "gate", "up",
+                "down", "sh_gate", "sh_up", "sh_down")
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+
+
+class KvRing(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
+
+
+ROUTING_NAMES = ("topk_idx", "topk_w", "expert_count", "expert_offset", "perm", "router_in",
+                 "router_logits")
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ROUTING_NAMES]
+
+
+class Ds4gError(RuntimeError):
+    pass
+
+
+def _hip_runtimes():
+    """Distinct HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run moe_dsv4_layer_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    # torch brings its own HIP runtime.  Load it first so that the library's
+    # libamdhip64.so.7 dependency binds to that same runtime (same soname);
+    # loading the library first would map a second HIP/HSA runtime into the
+    # process, and two runtimes cannot share the device.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    rts = _hip_runtimes()
+    if len(rts) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({rts}); import torch before "
+                          "anything that loads /opt/rocm's libamdhip64")
+    P = ctypes.c_void_p
+    lib.ds4g_workspace_bytes.restype = ctypes.c_size_t
+    lib.ds4g_workspace_bytes.argtypes = [ctypes.POINTER(LayerCfg), ctypes.c_int32, ctypes.c_int32]
+    lib.ds4g_layer_prefill.restype = ctypes.c_int
+    lib.ds4g_layer_prefill.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
+                                       ctypes.POINTER(KvRing), P, ctypes.c_int32,
+                                       ctypes.POINTER(Routing), P, ctypes.c_size_t, P]
+    lib.ds4g_layer_decode.restype = ctypes.c_int
+    lib.ds4g_layer_decode.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
+                                      ctypes.POINTER(KvRing), P, ctypes.POINTER(Routing), P,
+                                      ctypes.c_size_t, P]
+    lib.ds4g_lmhead_sample.restype = ctypes.c_int
+    lib.ds4g_lmhead_sample.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
+                                       ctypes.c_float, P, P, ctypes.c_float, ctypes.c_float, P,
+                                       P, P, P, ctypes.c_size_t, P]
+    lib.ds4g_status_string.restype = ctypes.c_char_p
+    lib.ds4g_status_string.argtypes = [ctypes.c_int]
+    return lib
+
+
+lib = _load()
+
+
+def status_string(rc: int) -> str:
+    return lib.ds4g_status_string(rc).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != OK:
+        raise Ds4gError(f"{what}: {status_string(rc)} ({rc})")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_cfg(shape) -> LayerCfg:
+    """ds4g_layer_cfg from any object with the layer's size attributes."""
+    wd = getattr(shape, "wdtype", "bf16")
+    return LayerCfg(shape.hidden, shape.n_heads, shape.head_dim, shape.qkv_rank, shape.window,
+                    shape.n_experts, shape.top_k, shape.ffn_inter,
+                    getattr(shape, "shared_inter", 0) or shape.ffn_inter * getattr(shape, "n_shared", 1),
+                    getattr(shape, "rope_dim", 0) or 0, float(shape.rope_base),
+                    float(shape.rms_eps), BF16 if wd in ("bf16", BF16) else F32)
+
+
+def make_weights(w: Dict[str, "torch.Tensor"]) -> LayerWeights:
+    for n in WEIGHT_NAMES:
+        t = w[n]
+        if not t.is_contiguous():
+            raise ValueError(f"weight {n} must be contiguous")
+    return LayerWeights(*[w[n].data_ptr() for n in WEIGHT_NAMES])
+
+
+def make_ring(k, v, pos) -> KvRing:
+    return KvRing(k.data_ptr(), v.data_ptr(), pos.data_ptr())
+
+
+def make_routing(bufs: Optional[Dict[str, "torch.Tensor"]]) -> Optional[Routing]:
+    if not bufs:
+        return None
+    return Routing(*[_ptr(bufs.get(n)) for n in ROUTING_NAMES])
+
+
+def workspace_bytes(cfg: Optional[LayerCfg], max_tokens: int, vocab: int = 0) -> int:
+    return int(lib.ds4g_workspace_bytes(ctypes.byref(cfg) if cfg is not None else None,
+                                        max_tokens, vocab))
+
+
+def layer_prefill(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x, T: int, ws,
+                  routing: Optional[Routing] = None, stream=None) -> None:
+    rc = lib.ds4g_layer_prefill(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ring),
+                                x.data_ptr(), T,
+                                ctypes.byref(routing) if routing is not None else None,
+                                ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "ds4g_layer_prefill")
+
+
+def layer_decode(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x, ws,
+                 routing: Optional[Routing] = None, stream=None) -> None:
+    rc = lib.ds4g_layer_decode(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ring),
+                               x.data_ptr(),
+                               ctypes.byref(routing) if routing is not None else None,
+                               ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "ds4g_layer_decode")
+
+
+def lmhead_sample(hidden: int, vocab: int, wdtype: int, final_norm, rms_eps: float, w_lm, x,
+                  temperature: float, top_p: float, rng_state, logits, token, ws,
+                  stream=None) -> None:
+    rc = lib.ds4g_lmhead_sample(hidden, vocab, wdtype, _ptr(final_norm), rms_eps,
+                                w_lm.data_ptr(), x.data_ptr(), temperature, top_p,
+                                _ptr(rng_state), logits.data_ptr(), token.data_ptr(),
+                                ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "ds4g_lmhead_sample")
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    """A 256-byte aligned device byte buffer (torch allocations are)."""
+    import torch
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)

@@ -1,0 +1,361 @@
+// The ds4g C ABI (include/ds4g.h): argument checks, workspace layout and the
+// launch sequences of prefill, decode and lm_head + sampling.  Host code only;
+// every step of the math runs in the kernels of this directory.
+#include "../../include/ds4g.h"
+#include "kernels.h"
+
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+
+namespace ds4g {
+namespace {
+
+inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t xn, c, qkv, q, kc, vc, o, yf, yb, logits, tidx, tw, rank, perm, gather, pos_of,
+      count, offset, tiles, ntiles, z, zs, part, total;
+};
+
+// Byte offsets of every workspace buffer for T tokens.  fp32-sized slots are
+// used for buffers that hold bf16 on the MFMA path and fp32 on the SIMT path.
+Layout layout(const ds4g_layer_cfg& c, int T) {
+  const size_t d = c.hidden, r = c.qkv_rank, qd = (size_t)c.n_heads * c.head_dim,
+               qkvd = qd + 2 * (size_t)c.head_dim, E = c.n_experts, k = c.top_k,
+               I = c.ffn_inter, Is = c.shared_inter, dh = c.head_dim;
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = a256(o + bytes); return at; };
+  L.xn = take((size_t)T * d * 4);
+  L.c = take((size_t)T * r * 4);
+  L.qkv = take((size_t)T * qkvd * 4);
+  L.q = take((size_t)T * qd * 4);
+  L.kc = take((size_t)T * dh * 2);
+  L.vc = take((size_t)T * dh * 2);
+  L.o = take((size_t)T * qd * 4);
+  L.yf = take((size_t)T * d * 4);
+  L.yb = take((size_t)T * d * 2);
+  L.logits = take((size_t)T * E * 4);
+  L.tidx = take((size_t)T * k * 4);
+  L.tw = take((size_t)T * k * 4);
+  L.rank = take((size_t)T * k * 4);
+  L.perm = take((size_t)T * k * 4);
+  L.gather = take((size_t)T * k * 4);
+  L.pos_of = take((size_t)T * k * 4);
+  L.count = take(E * 4);
+  L.offset = take((E + 1) * 4);
+  L.tiles = take((E + (size_t)T * k + 1) * 4);
+  L.ntiles = take(4);
+  L.z = take(((size_t)T * k * I + I + Is) * 4);
+  L.zs = take((size_t)T * Is * 4);
+  L.part = take((size_t)T * k * d * 4);
+  L.total = o;
+  return L;
+}
+
+int check_cfg(const ds4g_layer_cfg* c) {
+  if (!c) return DS4G_ERR_INVALID_ARG;
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->qkv_rank <= 0 ||
+      c->window <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->ffn_inter <= 0 ||
+      c->shared_inter <= 0 || c->rope_dim < 0 || !(c->rms_eps >= 0.f) || !(c->rope_base > 0.f))
+    return DS4G_ERR_INVALID_ARG;
+  if (c->wdtype != DS4G_F32 && c->wdtype != DS4G_BF16) return DS4G_ERR_INVALID_ARG;
+  if (c->top_k >= c->n_experts) return DS4G_ERR_INVALID_ARG;
+  const int rd = c->rope_dim ? c->rope_dim : c->head_dim;
+  if (rd > c->head_dim || (rd & 1)) return DS4G_ERR_INVALID_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return DS4G_ERR_UNSUPPORTED;
+  if (c->window > 128 || c->n_experts > 512 || c->top_k > 8) return DS4G_ERR_UNSUPPORTED;
+  if (c->hidden % 64 || c->qkv_rank % 64 || c->ffn_inter % 64 || c->shared_inter % 64 ||
+      (c->n_heads * c->head_dim) % 64)
+    return DS4G_ERR_UNSUPPORTED;
+  if (c->hidden > 16384 || c->qkv_rank > 16384 || c->n_heads * c->head_dim > 16384 ||
+      c->ffn_inter > 2048 || c->shared_inter > 2048)
+    return DS4G_ERR_UNSUPPORTED;
+  if ((long)c->top_k * c->ffn_inter + c->shared_inter > 12288) return DS4G_ERR_UNSUPPORTED;
+  return DS4G_OK;
+}
+
+int check_weights(const ds4g_layer_weights* w) {
+  if (!w || !w->attn_norm || !w->qkv_a || !w->qkv_b || !w->wo || !w->ffn_norm || !w->router ||
+      !w->gate || !w->up || !w->down || !w->sh_gate || !w->sh_up || !w->sh_down)
+    return DS4G_ERR_INVALID_ARG;
+  return DS4G_OK;
+}
+
+int check_ring(const ds4g_kv_ring* r) {
+  if (!r || !r->k || !r->v || !r->pos) return DS4G_ERR_INVALID_ARG;
+  return DS4G_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int hip_status(int launch_rc) {
+  if (launch_rc != 0) return DS4G_ERR_UNSUPPORTED;
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return DS4G_OK;
+  fprintf(stderr, "ds4g: HIP launch error: %s\n", hipGetErrorString(e));
+  return DS4G_ERR_HIP;
+}
+
+// Clear an error left by an earlier, unrelated HIP call so that the check at
+// the end of a call reports only this call's launches.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+// copy an optional routing output
+void copy_out(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  if (dst && bytes) (void)hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+}
+
+// ------------------------------------------------------------------ prefill
+int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring& ring,
+                 float* x, int T, ds4g_routing* routing, void* ws, hipStream_t st) {
+  const Layout L = layout(c, T);
+  const bool bf = c.wdtype == DS4G_BF16;
+  const int d = c.hidden, r = c.qkv_rank, H = c.n_heads, dh = c.head_dim, qd = H * dh,
+            qkvd = qd + 2 * dh, E = c.n_experts, k = c.top_k, I = c.ffn_inter,
+            Is = c.shared_inter;
+  const int rd = c.rope_dim ? c.rope_dim : dh;
+  int rc = 0;
+
+  // x_norm = RMSNorm(h) * g1
+  if (bf)
+    rc |= launch_rmsnorm_rows<uint16_t>(x, T, d, (const uint16_t*)w.attn_norm, c.rms_eps, nullptr,
+                                        at<uint16_t>(ws, L.xn), st);
+  else
+    rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.attn_norm, c.rms_eps,
+                                     at<float>(ws, L.xn), nullptr, st);
+
+  auto gemm = [&](const void* A, int lda, const void* B, int M, int N, int K, int epi, void* C,
+                  int ldc) {
+    GemmArgs g{};
+    g.A = A; g.lda = lda; g.B = B; g.M = M; g.N = N; g.K = K; g.epi = epi; g.C = C; g.ldc = ldc;
+    rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
+  };
+  // c = A x ; qkv = B c
+  gemm(at<void>(ws, L.xn), d, w.qkv_a, T, r, d, bf ? EPI_BF16 : EPI_F32, at<void>(ws, L.c), r);
+  gemm(at<void>(ws, L.c), r, w.qkv_b, T, qkvd, r, EPI_F32, at<void>(ws, L.qkv), qkvd);
+
+  // RoPE, attention over the window, ring update (*pos += T)
+  AttnArgs aa{};
+  aa.qkv = at<float>(ws, L.qkv); aa.T = T; aa.H = H; aa.dh = dh; aa.rd = rd; aa.W = c.window;
+  aa.base = c.rope_base; aa.pos = ring.pos; aa.q = at<void>(ws, L.q); aa.q_bf16 = 0;
+  aa.kc = at<uint16_t>(ws, L.kc); aa.vc = at<uint16_t>(ws, L.vc);
+  aa.ring_k = (uint16_t*)ring.k; aa.ring_v = (uint16_t*)ring.v;
+  aa.o = at<void>(ws, L.o); aa.o_bf16 = bf ? 1 : 0; aa.heads_per_block = H < 64 ? H : 64;
+  rc |= launch_attention(aa, st);
+
+  // h2 = h + W_o o   (in place in x)
+  gemm(at<void>(ws, L.o), qd, w.wo, T, d, qd, EPI_RESID, x, d);
+
+  // y = RMSNorm(h2) * g2 (fp32 for the router, bf16 for the expert GEMMs)
+  if (bf)
+    rc |= launch_rmsnorm_rows<uint16_t>(x, T, d, (const uint16_t*)w.ffn_norm, c.rms_eps,
+                                        at<float>(ws, L.yf), at<uint16_t>(ws, L.yb), st);
+  else
+    rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.ffn_norm, c.rms_eps,
+                                     at<float>(ws, L.yf), nullptr, st);
+
+  // router logits in fp32 (they decide integer expert choices)
+  {
+    GemmArgs g{};
+    g.A = at<void>(ws, L.yf); g.lda = d; g.B = w.router; g.M = T; g.N = E; g.K = d;
+    g.epi = EPI_F32; g.C = at<void>(ws, L.logits); g.ldc = E;
+    rc |= launch_gemm(g, false, bf ? 1 : 0, st);
+  }
+  const int tile_m = bf ? 128 : 64;
+  RouteArgs ra{};
+  ra.logits = at<float>(ws, L.logits); ra.T = T; ra.E = E; ra.k = k;
+  ra.topk_idx = at<int>(ws, L.tidx); ra.topk_w = at<float>(ws, L.tw);
+  ra.count = at<int>(ws, L.count); ra.offset = at<int>(ws, L.offset);
+  ra.rank = at<int>(ws, L.rank); ra.perm = at<int>(ws, L.perm);
+  ra.gather = at<int>(ws, L.gather); ra.pos_of = at<int>(ws, L.pos_of);
+  ra.tiles = at<int>(ws, L.tiles); ra.ntiles = at<int>(ws, L.ntiles); ra.tile_m = tile_m;
+  ra.out_count = routing ? routing->expert_count : nullptr;
+  ra.out_offset = routing ? routing->expert_offset : nullptr;
+  rc |= launch_route(ra, st);
+  const int max_tiles = E + (T * k + tile_m - 1) / tile_m;
+
+  const void* yA = bf ? at<void>(ws, L.yb) : at<void>(ws, L.yf);
+  // routed gate/up + SwiGLU over the permuted rows
+  {
+    GemmArgs g{};
+    g.A = yA; g.lda = d; g.gather = ra.gather; g.B = w.gate; g.B2 = w.up;
+    g.b_stride = (long)I * d; g.N = I; g.K = d; g.tiles = ra.tiles; g.ntiles = ra.ntiles;
+    g.row_off = ra.offset; g.max_tiles = max_tiles;
+    g.epi = bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32; g.C = at<void>(ws, L.z); g.ldc = I;
+    rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
+  }
+  // shared gate/up + SwiGLU over every token
+  {
+    GemmArgs g{};
+    g.A = yA; g.lda = d; g.B = w.sh_gate; g.B2 = w.sh_up; g.M = T; g.N = Is; g.K = d;
+    g.epi = bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32; g.C = at<void>(ws, L.zs); g.ldc = Is;
+    rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
+  }
+  // routed down projections -> part (permuted rows, fp32)
+  {
+    GemmArgs g{};
+    g.A = at<void>(ws, L.z); g.lda = I; g.B = w.down; g.b_stride = (long)d * I; g.N = d;
+    g.K = I; g.tiles = ra.tiles; g.ntiles = ra.ntiles; g.row_off = ra.offset;
+    g.max_tiles = max_tiles; g.epi = EPI_F32; g.C = at<void>(ws, L.part); g.ldc = d;
+    rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
+  }
+  // shared down + combine: x = h2 + shared + sum_j w_j part_j
+  {
+    GemmArgs g{};
+    g.A = at<void>(ws, L.zs); g.lda = Is; g.B = w.sh_down; g.M = T; g.N = d; g.K = Is;
+    g.epi = EPI_COMBINE; g.C = x; g.ldc = d; g.part = at<float>(ws, L.part);
+    g.pos_of = ra.pos_of; g.topk_w = ra.topk_w; g.topk = k; g.ldp = d;
+    rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
+  }
+  if (routing) {
+    copy_out(routing->topk_idx, ra.topk_idx, (size_t)T * k * 4, st);
+    copy_out(routing->topk_w, ra.topk_w, (size_t)T * k * 4, st);
+    copy_out(routing->perm, ra.perm, (size_t)T * k * 4, st);
+    copy_out(routing->router_in, at<void>(ws, L.yf), (size_t)T * d * 4, st);
+    copy_out(routing->router_logits, ra.logits, (size_t)T * E * 4, st);
+  }
+  return hip_status(rc);
+}
+
+// ------------------------------------------------------------------ decode
+template <typename WT>
+int decode_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring& ring,
+                float* x, ds4g_routing* routing, void* ws, hipStream_t st) {
+  const Layout L = layout(c, 1);
+  const int d = c.hidden, r = c.qkv_rank, H = c.n_heads, dh = c.head_dim, qd = H * dh,
+            qkvd = qd + 2 * dh, E = c.n_experts;
+  const int rd = c.rope_dim ? c.rope_dim : dh;
+  int rc = 0;
+  float* cbuf = at<float>(ws, L.c);
+  float* qkv = at<float>(ws, L.qkv);
+  float* logits = at<float>(ws, L.logits);
+  // c = A RMSNorm(h) g1 ; qkv = B c
+  rc |= launch_gemv<WT>((const WT*)w.qkv_a, r, d, x, (const WT*)w.attn_norm, c.rms_eps, cbuf, 0,
+                        nullptr, st);
+  rc |= launch_gemv<WT>((const WT*)w.qkv_b, qkvd, r, cbuf, nullptr, 0.f, qkv, 0, nullptr, st);
+  AttnArgs aa{};
+  aa.qkv = qkv; aa.T = 1; aa.H = H; aa.dh = dh; aa.rd = rd; aa.W = c.window;
+  aa.base = c.rope_base; aa.pos = ring.pos; aa.q = at<void>(ws, L.q); aa.q_bf16 = 0;
+  aa.kc = at<uint16_t>(ws, L.kc); aa.vc = at<uint16_t>(ws, L.vc);
+  aa.ring_k = (uint16_t*)ring.k; aa.ring_v = (uint16_t*)ring.v;
+  aa.o = at<void>(ws, L.o); aa.o_bf16 = 0; aa.heads_per_block = 4;
+  rc |= launch_attention(aa, st);
+  // h2 = h + W_o o
+  rc |= launch_gemv<WT>((const WT*)w.wo, d, qd, at<float>(ws, L.o), nullptr, 0.f, x, 1, nullptr,
+                        st);
+  // router logits on y = RMSNorm(h2) g2
+  rc |= launch_gemv<WT>((const WT*)w.router, E, d, x, (const WT*)w.ffn_norm, c.rms_eps, logits,
+                        0, nullptr, st);
+  MoeDecodeArgs m{};
+  m.h2 = x; m.ffn_norm = w.ffn_norm; m.eps = c.rms_eps; m.logits = logits; m.E = E;
+  m.k = c.top_k; m.d = d; m.I = c.ffn_inter; m.Is = c.shared_inter; m.gate = w.gate;
+  m.up = w.up; m.down = w.down; m.sh_gate = w.sh_gate; m.sh_up = w.sh_up;
+  m.sh_down = w.sh_down; m.z = at<float>(ws, L.z); m.sel = at<int>(ws, L.tidx);
+  m.wsel = at<float>(ws, L.tw);
+  if (routing) {
+    m.topk_idx = routing->topk_idx; m.topk_w = routing->topk_w;
+    m.count = routing->expert_count; m.offset = routing->expert_offset;
+    m.perm = routing->perm; m.router_in = routing->router_in;
+  }
+  rc |= launch_moe_decode<WT>(m, x, st);
+  if (routing) copy_out(routing->router_logits, logits, (size_t)E * 4, st);
+  return hip_status(rc);
+}
+
+}  // namespace
+}  // namespace ds4g
+
+using namespace ds4g;
+
+extern "C" {
+
+size_t ds4g_workspace_bytes(const ds4g_layer_cfg* cfg, int32_t max_tokens, int32_t vocab) {
+  size_t n = 0;
+  if (cfg) {
+    if (check_cfg(cfg) != DS4G_OK || max_tokens <= 0) return 0;
+    n = layout(*cfg, max_tokens).total;
+  }
+  if (vocab > 0) {
+    const size_t s = sample_ws_bytes(vocab);
+    if (s > n) n = s;
+  } else if (vocab < 0) {
+    return 0;
+  }
+  return n;
+}
+
+int ds4g_layer_prefill(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
+                       ds4g_kv_ring* ring, float* x, int32_t T, ds4g_routing* routing, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int s = check_cfg(cfg);
+  if (s != DS4G_OK) return s;
+  if ((s = check_weights(w)) != DS4G_OK) return s;
+  if ((s = check_ring(ring)) != DS4G_OK) return s;
+  if (!x || !ws || T <= 0) return DS4G_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
+  if ((long)T * cfg->top_k >= (1 << 24) || T > (1 << 20)) return DS4G_ERR_UNSUPPORTED;
+  if (ws_bytes < layout(*cfg, T).total) return DS4G_ERR_WORKSPACE;
+  clear_stale_error();
+  return prefill_impl(*cfg, *w, *ring, x, T, routing, ws, (hipStream_t)stream);
+}
+
+int ds4g_layer_decode(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, ds4g_kv_ring* ring,
+                      float* x, ds4g_routing* routing, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_cfg(cfg);
+  if (s != DS4G_OK) return s;
+  if ((s = check_weights(w)) != DS4G_OK) return s;
+  if ((s = check_ring(ring)) != DS4G_OK) return s;
+  if (!x || !ws) return DS4G_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
+  if (ws_bytes < layout(*cfg, 1).total) return DS4G_ERR_WORKSPACE;
+  clear_stale_error();
+  if (cfg->wdtype == DS4G_BF16)
+    return decode_impl<uint16_t>(*cfg, *w, *ring, x, routing, ws, (hipStream_t)stream);
+  return decode_impl<float>(*cfg, *w, *ring, x, routing, ws, (hipStream_t)stream);
+}
+
+int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype, const void* final_norm,
+                       float rms_eps, const void* w_lm, const float* x, float temperature,
+                       float top_p, uint64_t* rng_state, float* logits, int32_t* token, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (hidden <= 0 || vocab <= 0 || !w_lm || !x || !logits || !token || !ws)
+    return DS4G_ERR_INVALID_ARG;
+  if (wdtype != DS4G_F32 && wdtype != DS4G_BF16) return DS4G_ERR_INVALID_ARG;
+  if (!(rms_eps >= 0.f) || temperature != temperature || top_p != top_p)
+    return DS4G_ERR_INVALID_ARG;
+  if (temperature > 0.f && !rng_state) return DS4G_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
+  if (hidden % 8 || hidden > 16384 || vocab > (1 << 18)) return DS4G_ERR_UNSUPPORTED;
+  if (ws_bytes < sample_ws_bytes(vocab)) return DS4G_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int rc = 0;
+  clear_stale_error();
+  if (wdtype == DS4G_BF16)
+    rc |= launch_gemv<uint16_t>((const uint16_t*)w_lm, vocab, hidden, x,
+                                (const uint16_t*)final_norm, rms_eps, logits, 0, nullptr, st);
+  else
+    rc |= launch_gemv<float>((const float*)w_lm, vocab, hidden, x, (const float*)final_norm,
+                             rms_eps, logits, 0, nullptr, st);
+  SampleArgs sa{};
+  sa.logits = logits; sa.V = vocab; sa.temperature = temperature; sa.top_p = top_p;
+  sa.rng = rng_state; sa.token = token; sa.ws = ws;
+  rc |= launch_sample(sa, st);
+  return hip_status(rc);
+}
+
+const char* ds4g_status_string(int status) {
+  switch (status) {
+    case DS4G_OK: return "ok";
+    case DS4G_ERR_INVALID_ARG: return "invalid argument";
+    case DS4G_ERR_UNSUPPORTED: return "unsupported size";
+    case DS4G_ERR_WORKSPACE: return "workspace too small";
+    case DS4G_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

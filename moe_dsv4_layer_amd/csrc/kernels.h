@@ -1,0 +1,118 @@
+// Internal interfaces between the ds4g host code and its HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds4g {
+
+// ---------------------------------------------------------------- GEMM
+enum Epi {
+  EPI_F32 = 0,          // C[r, n] = acc                      (fp32)
+  EPI_BF16 = 1,         // C[r, n] = bf16(acc)
+  EPI_RESID = 2,        // C[r, n] += acc                     (fp32)
+  EPI_SWIGLU_BF16 = 3,  // C[r, n] = bf16(silu(A.G^T) * (A.U^T))
+  EPI_SWIGLU_F32 = 4,   // same, fp32 out
+  EPI_COMBINE = 5       // C[t, n] += acc + sum_j w[t,j] part[pos_of[t*k+j], n]
+};
+
+struct GemmArgs {
+  const void* A;        // activations [rows, K]: bf16 (MFMA) or fp32 (SIMT)
+  int lda;
+  const int* gather;    // optional: A row of output row r is gather[r]
+  const void* B;        // weights [N, K] (group g at B + g*b_stride)
+  const void* B2;       // SwiGLU: up weights (B holds gate)
+  long b_stride;
+  int M, N, K;          // M: rows when not grouped
+  const int* tiles;     // grouped: packed (group << 16 | m_tile), device
+  const int* ntiles;    // grouped: number of valid tiles, device
+  const int* row_off;   // grouped: [G+1] first row of each group, device
+  int max_tiles;        // grouped: grid bound (>= *ntiles)
+  int epi;
+  void* C;
+  int ldc;
+  // EPI_COMBINE
+  const float* part;
+  const int* pos_of;
+  const float* topk_w;
+  int topk;
+  int ldp;
+};
+int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st);
+
+// ---------------------------------------------------------------- GEMV
+template <typename WT>
+int launch_gemv(const WT* W, int N, int K, const float* x, const WT* gamma, float eps,
+                float* out, int accumulate, int64_t* pos_inc, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const float* qkv;     // [T, H*dh + 2*dh] fp32
+  int T, H, dh, rd, W;
+  float base;
+  int64_t* pos;         // device
+  void* q;              // [T, H, dh] rotated (fp32)
+  int q_bf16;
+  uint16_t* kc;         // [T, dh] bf16 rotated keys
+  uint16_t* vc;         // [T, dh] bf16 values
+  uint16_t* ring_k;
+  uint16_t* ring_v;
+  void* o;              // [T, H*dh] attention output
+  int o_bf16;
+  int heads_per_block;
+};
+int launch_attention(const AttnArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- decode MoE
+struct MoeDecodeArgs {
+  const float* h2;        // [d]
+  const void* ffn_norm;   // [d]
+  float eps;
+  const float* logits;    // [E]
+  int E, k, d, I, Is;
+  const void *gate, *up, *down, *sh_gate, *sh_up, *sh_down;
+  float* z;               // [k*I + Is]
+  int* sel;               // [k] workspace
+  float* wsel;            // [k] workspace
+  // optional routing outputs
+  int* topk_idx; float* topk_w; int* count; int* offset; int* perm; float* router_in;
+};
+template <typename WT>
+int launch_moe_decode(const MoeDecodeArgs& a, float* x, hipStream_t st);
+
+// ---------------------------------------------------------------- prefill misc
+template <typename WT>
+int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps,
+                        float* out_f32, uint16_t* out_bf16, hipStream_t st);
+
+struct RouteArgs {
+  const float* logits;  // [T, E]
+  int T, E, k;
+  int* topk_idx;        // [T, k]
+  float* topk_w;        // [T, k]
+  int* count;           // [E]
+  int* offset;          // [E+1]
+  int* rank;            // [T, k] rank of entry inside its expert
+  int* perm;            // [T*k]
+  int* gather;          // [T*k] token of each permuted row
+  int* pos_of;          // [T*k] permuted row of entry t*k+j
+  int* tiles;           // [max_tiles]
+  int* ntiles;          // [1]
+  int tile_m;           // rows per GEMM tile
+  // optional user copies
+  int* out_count; int* out_offset;
+};
+int launch_route(const RouteArgs& r, hipStream_t st);
+
+// ---------------------------------------------------------------- sampler
+struct SampleArgs {
+  const float* logits;
+  int V;
+  float temperature, top_p;
+  uint64_t* rng;
+  int* token;
+  void* ws;             // sampler workspace
+};
+size_t sample_ws_bytes(int V);
+int launch_sample(const SampleArgs& s, hipStream_t st);
+
+}  // namespace ds4g

@@ -1,0 +1,218 @@
+// Prefill helpers: row RMSNorm, router top-k, and the token -> expert grouping
+// that feeds the grouped expert GEMMs.
+//
+// ds4-learning 端到端推理流程, 阶段四 4.2 单层前向: x_norm = RMSNorm(x);
+// scores = x_norm @ W_router (256 experts); top6 = TopK(scores, 6).  The
+// grouping is this build's layout for running each expert once over all of its
+// tokens (阶段三 逐层批处理): entries t*k + j, grouped by expert, in token order
+// inside an expert; built with per-expert prefix sums, so it is deterministic
+// (no atomics decide an order).
+#include "dev.h"
+#include "kernels.h"
+
+namespace ds4g {
+
+// ------------------------------------------------------------ RMSNorm rows
+template <typename WT>
+__global__ void __launch_bounds__(256)
+rmsnorm_rows_kernel(const float* __restrict__ x, int d, const WT* __restrict__ gamma, float eps,
+                    float* __restrict__ of, uint16_t* __restrict__ ob) {
+  __shared__ float red[16];
+  const long t = blockIdx.x;
+  const float* row = x + t * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x * 4; i < d; i += blockDim.x * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(row + i);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = block_sum(ss, red);
+  const float rs = rsqrtf(ss / (float)d + eps);
+  for (int i = threadIdx.x * 4; i < d; i += blockDim.x * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(row + i);
+    float y[4] = {v.x * rs * ldw(gamma, i), v.y * rs * ldw(gamma, i + 1),
+                  v.z * rs * ldw(gamma, i + 2), v.w * rs * ldw(gamma, i + 3)};
+    if (of) *reinterpret_cast<float4*>(of + t * d + i) = make_float4(y[0], y[1], y[2], y[3]);
+    if (ob) {
+      uint2 p;
+      p.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+      p.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+      *reinterpret_cast<uint2*>(ob + t * d + i) = p;
+    }
+  }
+}
+
+template <typename WT>
+int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps, float* of,
+                        uint16_t* ob, hipStream_t st) {
+  if (d % 4) return -1;
+  hipLaunchKernelGGL((rmsnorm_rows_kernel<WT>), dim3(T), dim3(256), 0, st, x, d, gamma, eps, of,
+                     ob);
+  return 0;
+}
+template int launch_rmsnorm_rows<uint16_t>(const float*, int, int, const uint16_t*, float,
+                                           float*, uint16_t*, hipStream_t);
+template int launch_rmsnorm_rows<float>(const float*, int, int, const float*, float, float*,
+                                        uint16_t*, hipStream_t);
+
+// ------------------------------------------------------------ top-k per token
+// One wave per token: k rounds of a wave arg-max (lower index wins ties) over
+// the E logits, and the softmax probability of each pick.
+__global__ void __launch_bounds__(256)
+topk_kernel(const float* __restrict__ logits, int T, int E, int k, int* __restrict__ idx,
+            float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* s = logits + (long)t * E;
+  float v[8];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (e < E) ? s[e] : -INFINITY;
+    m = fmaxf(m, v[i]);
+  }
+  m = wave_max(m);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (lane + 64 * i < E) sum += expf(v[i] - m);
+  sum = wave_sum(sum);
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) {
+      idx[(long)t * k + r] = bi;
+      wts[(long)t * k + r] = expf(bv - m) / sum;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (lane + 64 * i == bi) v[i] = -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------ block scans
+// Exclusive prefix sum of n <= 256*SEG ints in LDS, in place; returns total.
+template <int SEG>
+__device__ int block_excl_scan(int* a, int n, int* wsum /*[4]*/) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int loc[SEG];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < SEG; ++i) {
+    const int j = tid * SEG + i;
+    loc[i] = (j < n) ? a[j] : 0;
+    s += loc[i];
+  }
+  // inclusive wave scan of s
+  int inc = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wid] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += wsum[w];
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  int run = base + inc - s;
+#pragma unroll
+  for (int i = 0; i < SEG; ++i) {
+    const int j = tid * SEG + i;
+    if (j < n) a[j] = run;
+    run += loc[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// ------------------------------------------------------------ expert ranks
+// Block e walks the tokens in order; a token that chose e gets the number of
+// earlier tokens that chose e (a ballot prefix count); count[e] = total.
+__global__ void __launch_bounds__(256)
+expert_rank_kernel(const int* __restrict__ idx, int T, int k, int* __restrict__ rank,
+                   int* __restrict__ count) {
+  __shared__ int wsum[4];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int base = 0;
+  for (int t0 = 0; t0 < T; t0 += 256) {
+    const int t = t0 + threadIdx.x;
+    int slot = -1;
+    if (t < T) {
+      for (int j = 0; j < k; ++j)
+        if (idx[(long)t * k + j] == e) slot = j;
+    }
+    const unsigned long long b = __ballot(slot >= 0);
+    const int before = __popcll(b & ((1ull << lane) - 1ull));
+    __syncthreads();
+    if (lane == 0) wsum[wid] = __popcll(b);
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wid; ++w) wbase += wsum[w];
+    if (slot >= 0) rank[(long)t * k + slot] = base + wbase + before;
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  }
+  if (threadIdx.x == 0) count[e] = base;
+}
+
+// ------------------------------------------------------------ scatter + tiles
+// Every block rebuilds offset[] from count[] (E <= 512) and scatters its
+// entries; block 0 also publishes offset[] and the GEMM tile list.
+__global__ void __launch_bounds__(256)
+route_scatter_kernel(RouteArgs r) {
+  __shared__ int off[513];
+  __shared__ int tl[513];
+  __shared__ int wsum[4];
+  const int E = r.E;
+  for (int e = threadIdx.x; e < E; e += 256) off[e] = r.count[e];
+  __syncthreads();
+  const int total = block_excl_scan<2>(off, E, wsum);
+  if (threadIdx.x == 0) off[E] = total;
+  __syncthreads();
+  const int nent = r.T * r.k;
+  const int ent = blockIdx.x * 256 + threadIdx.x;
+  if (ent < nent) {
+    const int e = r.topk_idx[ent];
+    const int p = off[e] + r.rank[ent];
+    r.perm[p] = ent;
+    r.gather[p] = ent / r.k;
+    r.pos_of[ent] = p;
+  }
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e <= E; e += 256) {
+      r.offset[e] = off[e];
+      if (r.out_offset) r.out_offset[e] = off[e];
+      if (r.out_count && e < E) r.out_count[e] = r.count[e];
+    }
+    for (int e = threadIdx.x; e < E; e += 256) tl[e] = (r.count[e] + r.tile_m - 1) / r.tile_m;
+    __syncthreads();
+    const int nt = block_excl_scan<2>(tl, E, wsum);
+    for (int e = threadIdx.x; e < E; e += 256) {
+      const int n = (r.count[e] + r.tile_m - 1) / r.tile_m;
+      for (int m = 0; m < n; ++m) r.tiles[tl[e] + m] = (e << 16) | m;
+    }
+    if (threadIdx.x == 0) *r.ntiles = nt;
+  }
+}
+
+int launch_route(const RouteArgs& r, hipStream_t st) {
+  if (r.E > 512 || r.k > 8) return -1;
+  hipLaunchKernelGGL(topk_kernel, dim3((r.T + 3) / 4), dim3(256), 0, st, r.logits, r.T, r.E, r.k,
+                     r.topk_idx, r.topk_w);
+  hipLaunchKernelGGL(expert_rank_kernel, dim3(r.E), dim3(256), 0, st, r.topk_idx, r.T, r.k,
+                     r.rank, r.count);
+  const int nent = r.T * r.k;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3((nent + 255) / 256), dim3(256), 0, st, r);
+  return 0;
+}
+
+}  // namespace ds4g
