@@ -1,0 +1,280 @@
+"""Throughput of the ds4g hot path on one MI355X.
+
+Workload (synthetic, seeded, random-init weights of the full-size layer:
+hidden 4096, 64-head MQA head_dim 128, QKV rank 1024, window 128, 256
+experts top-6 + 1 shared, SwiGLU inter 1024, bf16 weights, fp32 accumulate):
+
+  decode   one token through the full-size layer at position >= 128 (full
+           window).  This is the headline `value` (tokens/s).  Four distinct
+           layers' weights rotate so successive steps do not find the
+           previous step's weights in the 256 MB Infinity Cache.
+  prefill  layer-major prefill of 2048 tokens through the same layer
+           (reported as prefill_tok_s).
+  lm_head  final norm + 129280 x 4096 lm_head + temperature 0.7 / top-p
+           0.95 sampler (reported as lmhead_sample_us).
+
+Every input lives in HBM before the timed region starts.  Times come from
+HIP events on the stream the library launches on.  The CPU baseline is the
+float64 oracle on a bounded sample (a few decode tokens), on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def layer_decode_bytes(s) -> int:
+    """Algorithmic HBM bytes of one decode token through one layer: every
+    weight the token needs, read once (6 routed + 1 shared expert), the KV
+    window, and the fp32 activation vector in and out."""
+    d, r, H, dh, I = s.hidden, s.qkv_rank, s.n_heads, s.head_dim, s.ffn_inter
+    w = 2 * (r * d + (H * dh + 2 * dh) * r + d * H * dh + s.n_experts * d
+             + (s.top_k + 1) * 3 * I * d + 2 * d)
+    kv = 2 * 2 * s.window * dh
+    return w + kv + 2 * 4 * d
+
+
+def layer_flops(s, T: int) -> float:
+    """Algorithmic flops of T tokens through one layer (2 per multiply-add)."""
+    d, r, H, dh, I, W = s.hidden, s.qkv_rank, s.n_heads, s.head_dim, s.ffn_inter, s.window
+    dense = r * d + (H * dh + 2 * dh) * r + d * H * dh + s.n_experts * d
+    experts = (s.top_k + 1) * 3 * I * d
+    attn = 2 * H * dh * min(W, T)     # q.k and p.v per key (upper bound)
+    return 2.0 * T * (dense + experts + attn)
+
+
+def dense_gemm_flops(s, T: int) -> float:
+    d, r, H, dh, I = s.hidden, s.qkv_rank, s.n_heads, s.head_dim, s.ffn_inter
+    return 2.0 * T * (r * d + (H * dh + 2 * dh) * r + d * H * dh + 3 * I * d)
+
+
+def prefill_weight_bytes(s) -> int:
+    d, r, H, dh, I = s.hidden, s.qkv_rank, s.n_heads, s.head_dim, s.ffn_inter
+    return 2 * (r * d + (H * dh + 2 * dh) * r + d * H * dh + s.n_experts * d
+                + (s.n_experts + 1) * 3 * I * d + 2 * d)
+
+
+def cpu_baseline(shape, w_dev, h_dev, n_tokens: int):
+    """The float64 oracle decoding `n_tokens` tokens through one full-size
+    layer (ring pre-filled with 128 positions), timed on the host."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    wh = synth.weights_to_host(w_dev)
+    h = h_dev.cpu().numpy()
+    ring = oracle.Ring(shape.window, shape.head_dim)
+    # fill the window (not timed): keys/values of 128 positions
+    oracle.layer_forward(shape, wh, ring, h[:shape.window], rows=[])
+    t0 = time.perf_counter()
+    for i in range(n_tokens):
+        oracle.layer_forward(shape, wh, ring, h[shape.window + i:shape.window + i + 1])
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_tokens} decode tokens through one full-size layer (float64 numpy, "
+                      f"window pre-filled with {shape.window} positions), {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--weight-sets", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--no-graph", action="store_true", help="launch decode eagerly")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import moe_dsv4_layer_amd as ds4g
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS["layer_decode"]
+    s = wl.layer
+    cfg = ds4g.make_cfg(s)
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------ setup
+    layers = []
+    for l in range(args.weight_sets):
+        w = synth.layer_weights(s, wl.seed, layer=l, device=dev)
+        rk = torch.zeros((s.window, s.head_dim), dtype=torch.bfloat16, device=dev)
+        rv = torch.zeros_like(rk)
+        pos = torch.zeros(1, dtype=torch.int64, device=dev)
+        layers.append(dict(w=w, cw=ds4g.make_weights(w), rk=rk, rv=rv, pos=pos,
+                           ring=ds4g.make_ring(rk, rv, pos)))
+    T_pre = synth.WORKLOADS["layer_prefill_2048"].prompt
+    ws = ds4g.alloc_workspace(ds4g.workspace_bytes(cfg, T_pre, 129280))
+    h_all = synth.hidden(s.window + 64, s.hidden, wl.seed, device=dev)
+    # fill each ring with 128 positions (layer-major prefill), keep the
+    # decode inputs resident: one fp32 vector per layer, chained in place
+    xs = []
+    for L in layers:
+        x = h_all[:s.window].clone()
+        ds4g.layer_prefill(cfg, L["cw"], L["ring"], x, s.window, ws, stream=stream)
+        xs.append(h_all[s.window].clone())
+    torch.cuda.synchronize()
+
+    def decode_step(i):
+        L = layers[i % len(layers)]
+        ds4g.layer_decode(cfg, L["cw"], L["ring"], xs[i % len(layers)], ws, stream=stream)
+
+    for i in range(args.warmup):
+        decode_step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        # one graph replays len(layers) decode steps (one per weight set);
+        # positions and ring slots live on the device, so replays advance
+        try:
+            cs = torch.cuda.Stream()
+            cs.wait_stream(stream)
+            with torch.cuda.stream(cs):
+                for i in range(len(layers)):
+                    L = layers[i]
+                    ds4g.layer_decode(cfg, L["cw"], L["ring"], xs[i], ws, stream=cs)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(len(layers)):
+                    L = layers[i]
+                    ds4g.layer_decode(cfg, L["cw"], L["ring"], xs[i], ws, stream=cs)
+            torch.cuda.synchronize()
+            graph = g
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # capture unsupported: report eager numbers
+            print(f"graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            graph = None
+
+    # ------------------------------------------------------------ decode timing
+    nl = len(layers)
+    steps = args.steps
+    if graph is not None:
+        steps = max(nl, (steps // nl) * nl)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    if graph is not None:
+        for _ in range(steps // nl):
+            graph.replay()
+    else:
+        for i in range(steps):
+            decode_step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_decode = e0.elapsed_time(e1) / steps
+    dec_bytes = layer_decode_bytes(s)
+    dec_gbs = dec_bytes / (ms_decode * 1e-3) / 1e9
+
+    # ------------------------------------------------------------ prefill timing
+    hp = synth.hidden(T_pre, s.hidden, synth.WORKLOADS["layer_prefill_2048"].seed, device=dev)
+    xp = hp.clone()
+    for i in range(2):
+        L = layers[i % nl]
+        ds4g.layer_prefill(cfg, L["cw"], L["ring"], xp, T_pre, ws, stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.prefill_steps):
+        L = layers[i % nl]
+        ds4g.layer_prefill(cfg, L["cw"], L["ring"], xp, T_pre, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_prefill = e0.elapsed_time(e1) / args.prefill_steps
+    pre_tflops = layer_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
+    pre_dense_tflops = dense_gemm_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
+
+    # ------------------------------------------------------------ lm_head + sampler
+    V = 129280
+    hw = synth.head_weights(s, V, 1004, device=dev)
+    logits = torch.empty(V, dtype=torch.float32, device=dev)
+    tok = torch.zeros(1, dtype=torch.int32, device=dev)
+    rng = torch.tensor([synth.rng_seed(1004) & 0x7FFFFFFFFFFFFFFF], dtype=torch.int64,
+                       device=dev)
+    xl = xs[0].clone()
+
+    def lm_step():
+        ds4g.lmhead_sample(s.hidden, V, ds4g.BF16, hw["final_norm"], s.rms_eps, hw["lm_head"],
+                           xl, 0.7, 0.95, rng, logits, tok, ws, stream=stream)
+    for _ in range(5):
+        lm_step()
+    torch.cuda.synchronize()
+    n_lm = 50
+    e0.record(stream)
+    for _ in range(n_lm):
+        lm_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_lm = e0.elapsed_time(e1) / n_lm * 1e3
+    lm_bytes = 2 * V * s.hidden + 2 * s.hidden + 4 * V
+
+    rec = {
+        "metric": "decode tok/s + layer-major prefill tok/s; % HBM BW (decode), % MFMA (prefill)",
+        "value": round(1e3 / ms_decode, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_decode, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "one full-size layer, single-token decode at position >= 128 "
+                               "(hidden 4096, 64-head MQA dh 128, QKV rank 1024, window 128, "
+                               "256 experts top-6 + 1 shared, SwiGLU inter 1024, bf16 weights)",
+                   "weight_sets_rotated": nl, "graph": graph is not None,
+                   "global_batch": 1, "seq_len": 1, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": "ds4g_layer_decode (whole layer step)",
+                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": dec_bytes},
+        "prefill": {"workload": "same layer, layer-major prefill of 2048 tokens",
+                    "tok_s": round(T_pre / (ms_prefill * 1e-3), 1),
+                    "ms": round(ms_prefill, 4),
+                    "tflops_all": round(pre_tflops, 1),
+                    "mfma_frac_all": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "weight_bytes": prefill_weight_bytes(s),
+                    "hbm_frac_weights": round(prefill_weight_bytes(s) / (ms_prefill * 1e-3)
+                                              / 1e9 / HBM_PEAK_GBS, 4)},
+        "lmhead_sample": {"workload": "RMSNorm + lm_head 129280x4096 bf16 + T=0.7 top-p 0.95",
+                          "us": round(us_lm, 2),
+                          "hbm_frac": round(lm_bytes / (us_lm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "wall_s_decode": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(s, layers[0]["w"], h_all, args.cpu_tokens)
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -12,7 +12,7 @@ import os
 from typing import Dict, Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libds4g.so")
+LIB_PATH = os.environ.get("DS4G_LIB") or os.path.join(HERE, "libds4g.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1

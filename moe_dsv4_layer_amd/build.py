@@ -22,28 +22,31 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str, defines) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Build the library at `out`; `defines` are extra -D macros (launch-shape
+    knobs of the kernels; the defaults are the shipped choices)."""
+    build_dir = BUILD if out == LIB else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

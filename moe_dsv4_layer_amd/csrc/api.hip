@@ -64,7 +64,8 @@ int check_cfg(const ds4g_layer_cfg* c) {
   const int rd = c->rope_dim ? c->rope_dim : c->head_dim;
   if (rd > c->head_dim || (rd & 1)) return DS4G_ERR_INVALID_ARG;
   if (c->head_dim != 64 && c->head_dim != 128) return DS4G_ERR_UNSUPPORTED;
-  if (c->window > 128 || c->n_experts > 512 || c->top_k > 8) return DS4G_ERR_UNSUPPORTED;
+  if (c->window > 128 || c->n_experts > 512 || c->top_k > 8 || c->n_heads % 4)
+    return DS4G_ERR_UNSUPPORTED;
   if (c->hidden % 64 || c->qkv_rank % 64 || c->ffn_inter % 64 || c->shared_inter % 64 ||
       (c->n_heads * c->head_dim) % 64)
     return DS4G_ERR_UNSUPPORTED;
@@ -233,23 +234,38 @@ int decode_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ri
   float* cbuf = at<float>(ws, L.c);
   float* qkv = at<float>(ws, L.qkv);
   float* logits = at<float>(ws, L.logits);
-  // c = A RMSNorm(h) g1 ; qkv = B c
-  rc |= launch_gemv<WT>((const WT*)w.qkv_a, r, d, x, (const WT*)w.attn_norm, c.rms_eps, cbuf, 0,
-                        nullptr, st);
-  rc |= launch_gemv<WT>((const WT*)w.qkv_b, qkvd, r, cbuf, nullptr, 0.f, qkv, 0, nullptr, st);
+  // c = A RMSNorm(h) g1
+  {
+    GemvArgs g{};
+    g.W = w.qkv_a; g.N = r; g.K = d; g.x = x; g.gamma = w.attn_norm; g.eps = c.rms_eps;
+    g.out = cbuf;
+    rc |= launch_gemv<WT>(g, st);
+  }
+  // [q | k | v] = B c
+  {
+    GemvArgs g{};
+    g.W = w.qkv_b; g.N = qkvd; g.K = r; g.x = cbuf; g.out = qkv;
+    rc |= launch_gemv<WT>(g, st);
+  }
+  // RoPE, ring slot write, windowed MQA
   AttnArgs aa{};
   aa.qkv = qkv; aa.T = 1; aa.H = H; aa.dh = dh; aa.rd = rd; aa.W = c.window;
-  aa.base = c.rope_base; aa.pos = ring.pos; aa.q = at<void>(ws, L.q); aa.q_bf16 = 0;
-  aa.kc = at<uint16_t>(ws, L.kc); aa.vc = at<uint16_t>(ws, L.vc);
-  aa.ring_k = (uint16_t*)ring.k; aa.ring_v = (uint16_t*)ring.v;
-  aa.o = at<void>(ws, L.o); aa.o_bf16 = 0; aa.heads_per_block = 4;
-  rc |= launch_attention(aa, st);
+  aa.base = c.rope_base; aa.pos = ring.pos; aa.ring_k = (uint16_t*)ring.k;
+  aa.ring_v = (uint16_t*)ring.v; aa.o = at<void>(ws, L.o);
+  rc |= launch_attention_decode(aa, st);
   // h2 = h + W_o o
-  rc |= launch_gemv<WT>((const WT*)w.wo, d, qd, at<float>(ws, L.o), nullptr, 0.f, x, 1, nullptr,
-                        st);
+  {
+    GemvArgs g{};
+    g.W = w.wo; g.N = d; g.K = qd; g.x = at<float>(ws, L.o); g.out = x; g.accumulate = 1;
+    rc |= launch_gemv<WT>(g, st);
+  }
   // router logits on y = RMSNorm(h2) g2
-  rc |= launch_gemv<WT>((const WT*)w.router, E, d, x, (const WT*)w.ffn_norm, c.rms_eps, logits,
-                        0, nullptr, st);
+  {
+    GemvArgs g{};
+    g.W = w.router; g.N = E; g.K = d; g.x = x; g.gamma = w.ffn_norm; g.eps = c.rms_eps;
+    g.out = logits;
+    rc |= launch_gemv<WT>(g, st);
+  }
   MoeDecodeArgs m{};
   m.h2 = x; m.ffn_norm = w.ffn_norm; m.eps = c.rms_eps; m.logits = logits; m.E = E;
   m.k = c.top_k; m.d = d; m.I = c.ffn_inter; m.Is = c.shared_inter; m.gate = w.gate;
@@ -261,7 +277,7 @@ int decode_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ri
     m.count = routing->expert_count; m.offset = routing->expert_offset;
     m.perm = routing->perm; m.router_in = routing->router_in;
   }
-  rc |= launch_moe_decode<WT>(m, x, st);
+  rc |= launch_moe_decode<WT>(m, x, ring.pos, st);
   if (routing) copy_out(routing->router_logits, logits, (size_t)E * 4, st);
   return hip_status(rc);
 }
@@ -334,12 +350,12 @@ int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype, const void
   hipStream_t st = (hipStream_t)stream;
   int rc = 0;
   clear_stale_error();
-  if (wdtype == DS4G_BF16)
-    rc |= launch_gemv<uint16_t>((const uint16_t*)w_lm, vocab, hidden, x,
-                                (const uint16_t*)final_norm, rms_eps, logits, 0, nullptr, st);
-  else
-    rc |= launch_gemv<float>((const float*)w_lm, vocab, hidden, x, (const float*)final_norm,
-                             rms_eps, logits, 0, nullptr, st);
+  {
+    GemvArgs g{};
+    g.W = w_lm; g.N = vocab; g.K = hidden; g.x = x; g.gamma = final_norm; g.eps = rms_eps;
+    g.out = logits;
+    rc |= (wdtype == DS4G_BF16) ? launch_gemv<uint16_t>(g, st) : launch_gemv<float>(g, st);
+  }
   SampleArgs sa{};
   sa.logits = logits; sa.V = vocab; sa.temperature = temperature; sa.top_p = top_p;
   sa.rng = rng_state; sa.token = token; sa.ws = ws;

@@ -17,9 +17,8 @@ namespace ds4g {
 //   q  [T, H, dh]  rotated (QT = float or bf16)
 //   kc [T, dh]     rotated, bf16
 //   vc [T, dh]     bf16
-// Pair i of the rotated tail turns by (pos0 + t) * base^(-2i/rd); the angle
-// and its sine/cosine are formed in fp64 (positions reach 1e4..1e6, where an
-// fp32 angle would be off by ~1e-3 rad).  One block per token.
+// Pair i of the rotated tail turns by (pos0 + t) * base^(-2i/rd) (angle in
+// fp64, see rope_cs).  One block per token.
 template <typename QT>
 __global__ void __launch_bounds__(256)
 rope_qkv_kernel(const float* __restrict__ qkv, int T, int H, int dh, int rd, float base,
@@ -29,13 +28,7 @@ rope_qkv_kernel(const float* __restrict__ qkv, int T, int H, int dh, int rd, flo
   const int t = blockIdx.x;
   const long p = *pos + t;
   const int half = rd / 2, off = dh - rd;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    const double inv = pow((double)base, -2.0 * (double)i / (double)rd);
-    double s, c;
-    sincos((double)p * inv, &s, &c);
-    cs[i] = (float)c;
-    sn[i] = (float)s;
-  }
+  for (int i = threadIdx.x; i < half; i += blockDim.x) rope_cs(p, i, rd, base, &cs[i], &sn[i]);
   __syncthreads();
   const int qd = H * dh;
   const float* row = qkv + (long)t * (qd + 2 * dh);
@@ -195,6 +188,166 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
 #undef DS4G_ATT
   hipLaunchKernelGGL(ring_commit_kernel, dim3(1), dim3(256), 0, st, a.kc, a.vc, a.T, a.W, a.dh,
                      a.ring_k, a.ring_v, a.pos);
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention (one token at position p = *pos): RoPE of the token's q
+// heads and k, write (k, v) into ring slot p % W, softmax over the window
+// [max(0, p-W+1), p] of q.k/sqrt(dh), o = sum p_j v_j.
+//
+// One block (256 threads) per head.  The work per head is tiny (2 x 128 x dh
+// multiply-adds), so the kernel is latency-bound: every thread issues all of
+// its K and V loads (straight from the ring into registers) right after
+// reading *pos, and the math needs only a few block barriers.
+//   scores: thread t owns half of key j = t/2 (dh/2 dims), halves meet by
+//           a lane shuffle;
+//   p.v:    thread t owns 8 dims (group t % DG) of KPG keys (group t / DG),
+//           key groups meet in LDS.
+// Slot p % W holds position p - W, outside the window, so block 0 may
+// overwrite it while the other blocks read.  *pos is advanced by a later
+// kernel.
+template <int DH>
+__global__ void __launch_bounds__(256)
+attn_decode_kernel(const float* __restrict__ qkv, int H, int W, int rd, float base,
+                   const int64_t* __restrict__ pos, uint16_t* __restrict__ ring_k,
+                   uint16_t* __restrict__ ring_v, float* __restrict__ o) {
+  constexpr int KC = DH / 16;            // 16-byte K chunks per thread (half a row)
+  constexpr int DG = DH / 8;             // p.v dim groups of 8
+  constexpr int KG = 256 / DG;           // p.v key groups
+  constexpr int KPG = 128 / KG;          // keys per group
+  __shared__ float cs[64], sn[64];
+  __shared__ __align__(16) float qs[DH];
+  __shared__ __align__(16) uint16_t kself[DH];
+  __shared__ __align__(16) uint16_t vself[DH];
+  __shared__ float pr[128];
+  __shared__ float wred[4];
+  __shared__ float red[KG][DH];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int h = blockIdx.x;
+  const long p = *pos;
+  const long lo = p - W + 1 > 0 ? p - W + 1 : 0;
+  const int n = (int)(p - lo + 1);                 // window keys; the token is key n-1
+  const int s0 = (int)(lo % W);
+  // ---- issue every ring load now
+  const int jk = tid >> 1, hk = tid & 1;
+  uint4 kreg[KC];
+  {
+    int slot = s0 + jk;
+    slot = slot >= W ? slot - W : slot;
+    const long at = (jk < n - 1) ? (long)slot * DH + hk * (DH / 2) : 0;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kreg[c] = *reinterpret_cast<const uint4*>(ring_k + at + c * 8);
+  }
+  const int dg = tid % DG, kg = tid / DG;
+  uint4 vreg[KPG];
+#pragma unroll
+  for (int u = 0; u < KPG; ++u) {
+    const int j = kg * KPG + u;
+    int slot = s0 + j;
+    slot = slot >= W ? slot - W : slot;
+    const long at = (j < n - 1) ? (long)slot * DH + dg * 8 : 0;
+    vreg[u] = *reinterpret_cast<const uint4*>(ring_v + at);
+  }
+  // ---- RoPE of q (this head) and k; the token's k, v in bf16 like the ring
+  const int off = DH - rd;
+  for (int i = tid; i < rd / 2; i += 256) rope_cs(p, i, rd, base, &cs[i], &sn[i]);
+  __syncthreads();
+  const int qd = H * DH;
+  if (tid < DH) {   // pairs: tid < DH/2 -> q, else -> k
+    const bool isq = tid < DH / 2;
+    const int e0 = 2 * (isq ? tid : tid - DH / 2);
+    const float* src = isq ? qkv + (long)h * DH : qkv + qd;
+    float a = src[e0], b = src[e0 + 1];
+    if (e0 >= off) {
+      const int i = (e0 - off) / 2;
+      const float c = cs[i], s = sn[i];
+      const float na = a * c - b * s, nb = a * s + b * c;
+      a = na; b = nb;
+    }
+    if (isq) { qs[e0] = a; qs[e0 + 1] = b; }
+    else { kself[e0] = f32_to_bf16(a); kself[e0 + 1] = f32_to_bf16(b); }
+  } else if (tid < 2 * DH) {
+    const int e = tid - DH;
+    vself[e] = f32_to_bf16(qkv[qd + DH + e]);
+  }
+  __syncthreads();
+  if (h == 0) {
+    const long slot = p % W;
+    if (tid < DH) ring_k[slot * DH + tid] = kself[tid];
+    else if (tid < 2 * DH) ring_v[slot * DH + tid - DH] = vself[tid - DH];
+  }
+  // ---- scores
+  float sj;
+  {
+    if (jk == n - 1) {
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        kreg[c] = *reinterpret_cast<const uint4*>(kself + hk * (DH / 2) + c * 8);
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      float f[8];
+      unpack8(kreg[c], f);
+      const float4 q0 = *reinterpret_cast<const float4*>(&qs[hk * (DH / 2) + c * 8]);
+      const float4 q1 = *reinterpret_cast<const float4*>(&qs[hk * (DH / 2) + c * 8 + 4]);
+      acc += q0.x * f[0] + q0.y * f[1] + q0.z * f[2] + q0.w * f[3] +
+             q1.x * f[4] + q1.y * f[5] + q1.z * f[6] + q1.w * f[7];
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    sj = (jk < n) ? acc * rsqrtf((float)DH) : -INFINITY;
+  }
+  // softmax over the window: block max and sum (each key counted by its even lane)
+  const float m = wave_max(sj);
+  if (lane == 0) wred[wid] = m;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+  const float ej = (jk < n) ? expf(sj - mx) : 0.f;
+  const float es = wave_sum(hk == 0 ? ej : 0.f);
+  __syncthreads();
+  if (lane == 0) wred[wid] = es;
+  if (hk == 0) pr[jk] = ej;
+  __syncthreads();
+  const float inv = 1.0f / (wred[0] + wred[1] + wred[2] + wred[3]);
+  // ---- p.v
+  {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) {
+      const int j = kg * KPG + u;
+      if (j < n) {
+        uint4 v4 = vreg[u];
+        if (j == n - 1) v4 = *reinterpret_cast<const uint4*>(vself + dg * 8);
+        float f[8];
+        unpack8(v4, f);
+        const float pj = pr[j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += pj * f[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[kg][dg * 8 + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < DH) {
+    float v = 0.f;
+#pragma unroll
+    for (int g = 0; g < KG; ++g) v += red[g][tid];
+    o[(long)h * DH + tid] = v * inv;
+  }
+}
+
+int launch_attention_decode(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.H);
+  if (a.dh == 128)
+    hipLaunchKernelGGL((attn_decode_kernel<128>), grid, dim3(256), 0, st, a.qkv, a.H, a.W, a.rd,
+                       a.base, a.pos, a.ring_k, a.ring_v, (float*)a.o);
+  else if (a.dh == 64)
+    hipLaunchKernelGGL((attn_decode_kernel<64>), grid, dim3(256), 0, st, a.qkv, a.H, a.W, a.rd,
+                       a.base, a.pos, a.ring_k, a.ring_v, (float*)a.o);
+  else
+    return -1;
   return 0;
 }
 

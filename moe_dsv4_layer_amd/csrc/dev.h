@@ -110,6 +110,18 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// RoPE angle of pair i (of rd rotated dims) at position p: theta =
+// p * base^(-2i/rd).  The angle is formed and reduced modulo 2*pi in fp64
+// (positions reach 1e4..1e6), then sin/cos are taken in fp32 of the reduced
+// angle.  Shared by the prefill and decode kernels so both rotate alike.
+__device__ __forceinline__ void rope_cs(long p, int i, int rd, float base, float* c, float* s) {
+  const double inv = exp2(-(2.0 * (double)i / (double)rd) * log2((double)base));
+  const double th = (double)p * inv;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double red = th - two_pi * rint(th / two_pi);
+  sincosf((float)red, s, c);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 }  // namespace ds4g

@@ -40,9 +40,19 @@ struct GemmArgs {
 int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st);
 
 // ---------------------------------------------------------------- GEMV
+// out[n] (= or +=) sum_k W[n, k] xs[k], xs = x or RMSNorm(x) * gamma.
+struct GemvArgs {
+  const void* W;
+  int N, K;
+  const float* x;
+  const void* gamma;    // optional fused RMSNorm gain
+  float eps;
+  float* out;
+  int accumulate;
+  float* router_in;     // optional copy of xs (block 0)
+};
 template <typename WT>
-int launch_gemv(const WT* W, int N, int K, const float* x, const WT* gamma, float eps,
-                float* out, int accumulate, int64_t* pos_inc, hipStream_t st);
+int launch_gemv(const GemvArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
@@ -61,6 +71,9 @@ struct AttnArgs {
   int heads_per_block;
 };
 int launch_attention(const AttnArgs& a, hipStream_t st);
+// single-token attention: RoPE of q/k at *pos, write (k, v) to the ring
+// slot, attend over the window; o fp32 [H*dh].  Does not advance *pos.
+int launch_attention_decode(const AttnArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- decode MoE
 struct MoeDecodeArgs {
@@ -77,7 +90,7 @@ struct MoeDecodeArgs {
   int* topk_idx; float* topk_w; int* count; int* offset; int* perm; float* router_in;
 };
 template <typename WT>
-int launch_moe_decode(const MoeDecodeArgs& a, float* x, hipStream_t st);
+int launch_moe_decode(const MoeDecodeArgs& a, float* x, int64_t* pos_inc, hipStream_t st);
 
 // ---------------------------------------------------------------- prefill misc
 template <typename WT>
