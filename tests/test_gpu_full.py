@@ -1,0 +1,104 @@
+"""GPU parity at the full layer size (hidden 4096, 64 heads x 128, rank 1024,
+window 128, 256 experts top-6 + 1 shared, inter 1024, bf16 weights).
+
+  decode : 128 positions prefilled, one decode token at position 128;
+  prefill: 2048 tokens layer-major from an empty ring.
+
+Inputs are drawn so every token's router margin (gap between the 6th and 7th
+largest logit, from the oracle) is at least 1e-3: rows below it are redrawn
+(a new candidate row from the seeded generator) until none is left.  The
+oracle evaluates the expert FFNs only for sampled rows (they are the costly
+part); routing, attention and everything before the experts are checked on
+every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.harness import GpuLayer, check_routing, log, rel_l2, to_np
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+LAYER_TOL = 1e-2
+MARGIN = 1e-3
+
+
+def _draw_with_margin(shape, wh, T, seed, max_rounds=60):
+    """h [T, d] on the GPU whose oracle router margins are all >= MARGIN."""
+    attempts = np.zeros(T, dtype=np.int64)
+    for rnd in range(max_rounds):
+        h = synth.hidden(T, shape.hidden, seed, device="cuda", attempts=attempts)
+        r = oracle.layer_forward(shape, wh, oracle.Ring(shape.window, shape.head_dim),
+                                 h.cpu().numpy(), rows=[])
+        low = np.nonzero(r["margin"] < MARGIN)[0]
+        log(f"  margin round {rnd}: {low.size} rows below {MARGIN}")
+        if low.size == 0:
+            return h, attempts
+        attempts[low] += 1
+    raise AssertionError("router margins did not settle")
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    shape = synth.WORKLOADS["layer_prefill_2048"].layer
+    log("full layer: generating weights")
+    gl = GpuLayer(shape, seed=1003, max_tokens=2048)
+    wh = gl.host_weights()
+    return shape, gl, wh
+
+
+def test_full_prefill_2048(full_layer):
+    shape, gl, wh = full_layer
+    T = 2048
+    gl.pos.zero_()
+    h, attempts = _draw_with_margin(shape, wh, T, 1003)
+    log(f"  redrawn rows: {int((attempts > 0).sum())}")
+    x, bufs = gl.prefill(h)
+    rows = sorted({0, 1, 63, 127, 128, 129, 500, 1023, 1024, 1500, 2000, 2046, 2047})
+    ring = oracle.Ring(shape.window, shape.head_dim)
+    orc = oracle.layer_forward(shape, wh, ring, h.cpu().numpy(), rows=rows)
+    c = orc["count"]
+    log(f"  tokens per expert: min {c.min()} max {c.max()}")
+    assert c.min() >= 20 and c.max() <= 80, "workload: every expert gets 20..80 tokens"
+    g = to_np(bufs)
+    out = x.cpu().numpy().astype(np.float64)
+    hh = h.cpu().numpy().astype(np.float64)
+    e_out = rel_l2(out[rows], orc["out"][rows])
+    e_inc = rel_l2(out[rows] - hh[rows], orc["out"][rows] - hh[rows])
+    e_y = rel_l2(g["router_in"], orc["y"])
+    e_lg = rel_l2(g["router_logits"], orc["logits"])
+    st = check_routing(shape, wh, g, orc, label="full prefill")
+    log(f"full prefill: rel_l2 out={e_out:.2e} inc={e_inc:.2e} y={e_y:.2e} logits={e_lg:.2e} {st}")
+    assert e_out < LAYER_TOL and e_inc < LAYER_TOL and e_y < LAYER_TOL
+    assert int(gl.pos.item()) == T
+    rk = gl.ring_k.float().cpu().numpy()
+    assert rel_l2(rk, ring.k) < 1e-2 and rel_l2(gl.ring_v.float().cpu().numpy(), ring.v) < 1e-2
+
+
+def test_full_decode_at_128(full_layer):
+    shape, gl, wh = full_layer
+    gl.pos.zero_()
+    gl.ring_k.zero_()
+    gl.ring_v.zero_()
+    h, _ = _draw_with_margin(shape, wh, 129, 1002)
+    x, _ = gl.prefill(h[:128])
+    xd, bufs = gl.decode(h[128])
+    ring = oracle.Ring(shape.window, shape.head_dim)
+    oracle.layer_forward(shape, wh, ring, h[:128].cpu().numpy(), rows=[])
+    orc = oracle.layer_forward(shape, wh, ring, h[128:129].cpu().numpy())
+    g = to_np(bufs)
+    g = {k: (v.reshape(1, -1) if k in ("topk_idx", "topk_w", "router_in", "router_logits") else v)
+         for k, v in g.items()}
+    out = xd.cpu().numpy().astype(np.float64)[None]
+    hh = h[128:129].cpu().numpy().astype(np.float64)
+    e_out = rel_l2(out, orc["out"])
+    e_inc = rel_l2(out - hh, orc["out"] - hh)
+    st = check_routing(shape, wh, g, orc, label="full decode")
+    log(f"full decode: rel_l2 out={e_out:.2e} inc={e_inc:.2e} {st}")
+    assert e_out < LAYER_TOL and e_inc < LAYER_TOL
+    assert int(gl.pos.item()) == 129
