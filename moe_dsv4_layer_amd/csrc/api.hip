@@ -12,8 +12,18 @@ namespace {
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The prefill router GEMM splits K = hidden into up to this many parts.
+constexpr int kRouterSplit = 8;
+inline int router_split(int hidden) {
+  int s = hidden / 512;
+  if (s < 1) s = 1;
+  if (s > kRouterSplit) s = kRouterSplit;
+  while (hidden % (16 * s)) --s;
+  return s;
+}
+
 struct Layout {
-  size_t xn, c, qkv, q, kc, vc, o, yf, yb, logits, tidx, tw, rank, perm, gather, pos_of,
+  size_t xn, c, qkv, q, kc, vc, o, yf, yb, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
       count, offset, tiles, ntiles, z, zs, part, total;
 };
 
@@ -36,6 +46,7 @@ Layout layout(const ds4g_layer_cfg& c, int T) {
   L.yf = take((size_t)T * d * 4);
   L.yb = take((size_t)T * d * 2);
   L.logits = take((size_t)T * E * 4);
+  L.lpart = take((size_t)T * E * 4 * kRouterSplit);
   L.tidx = take((size_t)T * k * 4);
   L.tw = take((size_t)T * k * 4);
   L.rank = take((size_t)T * k * 4);
@@ -142,11 +153,11 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   // RoPE, attention over the window, ring update (*pos += T)
   AttnArgs aa{};
   aa.qkv = at<float>(ws, L.qkv); aa.T = T; aa.H = H; aa.dh = dh; aa.rd = rd; aa.W = c.window;
-  aa.base = c.rope_base; aa.pos = ring.pos; aa.q = at<void>(ws, L.q); aa.q_bf16 = 0;
+  aa.base = c.rope_base; aa.pos = ring.pos; aa.q = at<void>(ws, L.q); aa.q_bf16 = bf ? 1 : 0;
   aa.kc = at<uint16_t>(ws, L.kc); aa.vc = at<uint16_t>(ws, L.vc);
   aa.ring_k = (uint16_t*)ring.k; aa.ring_v = (uint16_t*)ring.v;
   aa.o = at<void>(ws, L.o); aa.o_bf16 = bf ? 1 : 0; aa.heads_per_block = H < 64 ? H : 64;
-  rc |= launch_attention(aa, st);
+  rc |= bf ? launch_attention_prefill_mfma(aa, st) : launch_attention(aa, st);
 
   // h2 = h + W_o o   (in place in x)
   gemm(at<void>(ws, L.o), qd, w.wo, T, d, qd, EPI_RESID, x, d);
@@ -159,16 +170,20 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.ffn_norm, c.rms_eps,
                                      at<float>(ws, L.yf), nullptr, st);
 
-  // router logits in fp32 (they decide integer expert choices)
+  // router logits in fp32 (they decide integer expert choices): split-K
+  // partial sums, added in split order by the top-k kernel
+  const int rsplit = router_split(d);
   {
     GemmArgs g{};
     g.A = at<void>(ws, L.yf); g.lda = d; g.B = w.router; g.M = T; g.N = E; g.K = d;
-    g.epi = EPI_F32; g.C = at<void>(ws, L.logits); g.ldc = E;
+    g.epi = EPI_F32; g.C = at<void>(ws, L.lpart); g.ldc = E;
+    g.ksplit = rsplit; g.part_stride = (long)T * E;
     rc |= launch_gemm(g, false, bf ? 1 : 0, st);
   }
   const int tile_m = bf ? 128 : 64;
   RouteArgs ra{};
-  ra.logits = at<float>(ws, L.logits); ra.T = T; ra.E = E; ra.k = k;
+  ra.logits = at<float>(ws, L.lpart); ra.nsplit = rsplit;
+  ra.logits_sum = at<float>(ws, L.logits); ra.T = T; ra.E = E; ra.k = k;
   ra.topk_idx = at<int>(ws, L.tidx); ra.topk_w = at<float>(ws, L.tw);
   ra.count = at<int>(ws, L.count); ra.offset = at<int>(ws, L.offset);
   ra.rank = at<int>(ws, L.rank); ra.perm = at<int>(ws, L.perm);
@@ -217,7 +232,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     copy_out(routing->topk_w, ra.topk_w, (size_t)T * k * 4, st);
     copy_out(routing->perm, ra.perm, (size_t)T * k * 4, st);
     copy_out(routing->router_in, at<void>(ws, L.yf), (size_t)T * d * 4, st);
-    copy_out(routing->router_logits, ra.logits, (size_t)T * E * 4, st);
+    copy_out(routing->router_logits, ra.logits_sum, (size_t)T * E * 4, st);
   }
   return hip_status(rc);
 }

@@ -104,7 +104,11 @@ gemm_simt_kernel(GemmArgs g) {
   const int brow = n0 + lr;
 
   float acc[4][4] = {}, acc2[DUAL ? 4 : 1][4] = {};
-  for (int k0 = 0; k0 < g.K; k0 += BK) {
+  // split-K: block z covers k in [z*Kc, (z+1)*Kc)
+  const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
+  const int Kc = g.K / nsplit;
+  const int kbeg = blockIdx.z * Kc, kend = kbeg + Kc;
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
     float4 av = make_float4(0.f, 0.f, 0.f, 0.f);
     if (asrc >= 0) av = *reinterpret_cast<const float4*>(A + asrc + k0 + lk);
     As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
@@ -142,6 +146,8 @@ gemm_simt_kernel(GemmArgs g) {
       const int col = n0 + tx * 4 + j;
       if (col >= g.N) continue;
       if (DUAL) epi_swiglu(g, row, col, acc[i][j], acc2[i][j]);
+      else if (nsplit > 1)
+        static_cast<float*>(g.C)[blockIdx.z * g.part_stride + (long)row * g.ldc + col] = acc[i][j];
       else epi_store(g, row, col, acc[i][j]);
     }
   }
@@ -281,9 +287,11 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
     if (dual) hipLaunchKernelGGL((gemm_mfma_kernel<true>), grid, dim3(256), 0, st, g);
     else hipLaunchKernelGGL((gemm_mfma_kernel<false>), grid, dim3(256), 0, st, g);
   } else {
-    if (g.K % 16) return -1;
+    const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
+    if (g.K % (16 * nsplit)) return -1;
+    if (nsplit > 1 && (dual || g.epi != EPI_F32)) return -1;
     const int mt = g.tiles ? g.max_tiles : (g.M + 63) / 64;
-    dim3 grid((g.N + 63) / 64, mt);
+    dim3 grid((g.N + 63) / 64, mt, nsplit);
     if (wdtype_bf16) {
       if (dual) hipLaunchKernelGGL((gemm_simt_kernel<uint16_t, true>), grid, dim3(256), 0, st, g);
       else hipLaunchKernelGGL((gemm_simt_kernel<uint16_t, false>), grid, dim3(256), 0, st, g);

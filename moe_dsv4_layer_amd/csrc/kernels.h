@@ -36,6 +36,9 @@ struct GemmArgs {
   const float* topk_w;
   int topk;
   int ldp;
+  // SIMT split-K: blockIdx.z of ksplit writes its partial sum to C + z * part_stride
+  int ksplit;
+  long part_stride;
 };
 int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st);
 
@@ -74,6 +77,8 @@ int launch_attention(const AttnArgs& a, hipStream_t st);
 // single-token attention: RoPE of q/k at *pos, write (k, v) to the ring
 // slot, attend over the window; o fp32 [H*dh].  Does not advance *pos.
 int launch_attention_decode(const AttnArgs& a, hipStream_t st);
+// prefill on the matrix cores: bf16 q (q_bf16 = 1) and o (o_bf16 = 1)
+int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- decode MoE
 struct MoeDecodeArgs {
@@ -98,7 +103,9 @@ int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps
                         float* out_f32, uint16_t* out_bf16, hipStream_t st);
 
 struct RouteArgs {
-  const float* logits;  // [T, E]
+  const float* logits;  // nsplit partial sums [nsplit][T][E], added in order
+  int nsplit;
+  float* logits_sum;    // [T, E] the summed logits (router output)
   int T, E, k;
   int* topk_idx;        // [T, k]
   float* topk_w;        // [T, k]

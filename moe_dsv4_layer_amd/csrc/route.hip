@@ -57,19 +57,26 @@ template int launch_rmsnorm_rows<float>(const float*, int, int, const float*, fl
 // ------------------------------------------------------------ top-k per token
 // One wave per token: k rounds of a wave arg-max (lower index wins ties) over
 // the E logits, and the softmax probability of each pick.
+// The logits arrive as nsplit partial sums (split-K GEMM); they are added in
+// split order, so the result does not depend on scheduling.
 __global__ void __launch_bounds__(256)
-topk_kernel(const float* __restrict__ logits, int T, int E, int k, int* __restrict__ idx,
-            float* __restrict__ wts) {
+topk_kernel(const float* __restrict__ logits, int nsplit, float* __restrict__ lsum, int T, int E,
+            int k, int* __restrict__ idx, float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* s = logits + (long)t * E;
   float v[8];
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (e < E) ? s[e] : -INFINITY;
+    float a = -INFINITY;
+    if (e < E) {
+      a = 0.f;
+      for (int z = 0; z < nsplit; ++z) a += logits[((long)z * T + t) * E + e];
+      lsum[(long)t * E + e] = a;
+    }
+    v[i] = a;
     m = fmaxf(m, v[i]);
   }
   m = wave_max(m);
@@ -206,8 +213,8 @@ route_scatter_kernel(RouteArgs r) {
 
 int launch_route(const RouteArgs& r, hipStream_t st) {
   if (r.E > 512 || r.k > 8) return -1;
-  hipLaunchKernelGGL(topk_kernel, dim3((r.T + 3) / 4), dim3(256), 0, st, r.logits, r.T, r.E, r.k,
-                     r.topk_idx, r.topk_w);
+  hipLaunchKernelGGL(topk_kernel, dim3((r.T + 3) / 4), dim3(256), 0, st, r.logits, r.nsplit,
+                     r.logits_sum, r.T, r.E, r.k, r.topk_idx, r.topk_w);
   hipLaunchKernelGGL(expert_rank_kernel, dim3(r.E), dim3(256), 0, st, r.topk_idx, r.T, r.k,
                      r.rank, r.count);
   const int nent = r.T * r.k;
