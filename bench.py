@@ -98,7 +98,7 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--weight-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--cpu-tokens", type=int, default=48)
     ap.add_argument("--no-graph", action="store_true", help="launch decode eagerly")
     args = ap.parse_args()
     if args.gpus != 1:
