@@ -155,12 +155,23 @@ int ds4g_layer_decode(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
  *   (top 24 bits / 2^24).
  *   rng_state: device uint64 (may be NULL when temperature <= 0).
  *   logits: device fp32 [vocab] out.  token: device int32 out.
+ *   embed_table, x_next: optional, both or neither: after sampling, x_next
+ *   (device fp32 [hidden]) receives the embedding of the sampled token
+ *   (table [vocab, hidden] in wdtype), so a decode loop stays on the device.
  *   ws: at least ds4g_workspace_bytes(NULL, 0, vocab) bytes. */
 int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype,
                        const void *final_norm, float rms_eps, const void *w_lm,
                        const float *x, float temperature, float top_p,
                        uint64_t *rng_state, float *logits, int32_t *token,
+                       const void *embed_table, float *x_next,
                        void *ws, size_t ws_bytes, void *stream);
+
+/* Token embedding (阶段四 4.1): x[t] = widen(table[ids[t]]) for t < T.
+ *   table: device [vocab, hidden] in wdtype; ids: device int32 [T];
+ *   x: device fp32 [T, hidden] out.  An id outside [0, vocab) yields a row
+ *   of zeros (the kernel never reads outside the table).  hidden % 8 == 0. */
+int ds4g_embed(int32_t vocab, int32_t hidden, int32_t wdtype, const void *table,
+               const int32_t *ids, int32_t T, float *x, void *stream);
 
 /* Static text for a ds4g_status value. */
 const char *ds4g_status_string(int status);

@@ -19,7 +19,7 @@ F32, BF16 = 0, 1
 
 # ds4g.h declares these functions; the ABI test checks the header agrees.
 EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_prefill", "ds4g_layer_decode",
-           "ds4g_lmhead_sample", "ds4g_status_string")
+           "ds4g_lmhead_sample", "ds4g_embed", "ds4g_status_string")
 
 
 class LayerCfg(ctypes.Structure):
@@ -93,7 +93,10 @@ def _load() -> ctypes.CDLL:
     lib.ds4g_lmhead_sample.restype = ctypes.c_int
     lib.ds4g_lmhead_sample.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
                                        ctypes.c_float, P, P, ctypes.c_float, ctypes.c_float, P,
-                                       P, P, P, ctypes.c_size_t, P]
+                                       P, P, P, P, P, ctypes.c_size_t, P]
+    lib.ds4g_embed.restype = ctypes.c_int
+    lib.ds4g_embed.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
+                               ctypes.c_int32, P, P]
     lib.ds4g_status_string.restype = ctypes.c_char_p
     lib.ds4g_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -175,12 +178,20 @@ def layer_decode(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x, ws,
 
 def lmhead_sample(hidden: int, vocab: int, wdtype: int, final_norm, rms_eps: float, w_lm, x,
                   temperature: float, top_p: float, rng_state, logits, token, ws,
-                  stream=None) -> None:
+                  stream=None, embed_table=None, x_next=None) -> None:
     rc = lib.ds4g_lmhead_sample(hidden, vocab, wdtype, _ptr(final_norm), rms_eps,
                                 w_lm.data_ptr(), x.data_ptr(), temperature, top_p,
                                 _ptr(rng_state), logits.data_ptr(), token.data_ptr(),
+                                _ptr(embed_table), _ptr(x_next),
                                 ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "ds4g_lmhead_sample")
+
+
+def embed(vocab: int, hidden: int, wdtype: int, table, ids, x, stream=None) -> None:
+    """x[t] = table[ids[t]] widened to fp32 (ids: device int32 [T])."""
+    rc = lib.ds4g_embed(vocab, hidden, wdtype, table.data_ptr(), ids.data_ptr(), ids.numel(),
+                        x.data_ptr(), _stream(stream))
+    _check(rc, "ds4g_embed")
 
 
 def alloc_workspace(nbytes: int, device="cuda"):

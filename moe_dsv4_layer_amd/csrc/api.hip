@@ -351,10 +351,12 @@ int ds4g_layer_decode(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, ds
 
 int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype, const void* final_norm,
                        float rms_eps, const void* w_lm, const float* x, float temperature,
-                       float top_p, uint64_t* rng_state, float* logits, int32_t* token, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       float top_p, uint64_t* rng_state, float* logits, int32_t* token,
+                       const void* embed_table, float* x_next, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (hidden <= 0 || vocab <= 0 || !w_lm || !x || !logits || !token || !ws)
     return DS4G_ERR_INVALID_ARG;
+  if ((embed_table == nullptr) != (x_next == nullptr)) return DS4G_ERR_INVALID_ARG;
   if (wdtype != DS4G_F32 && wdtype != DS4G_BF16) return DS4G_ERR_INVALID_ARG;
   if (!(rms_eps >= 0.f) || temperature != temperature || top_p != top_p)
     return DS4G_ERR_INVALID_ARG;
@@ -375,6 +377,19 @@ int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype, const void
   sa.logits = logits; sa.V = vocab; sa.temperature = temperature; sa.top_p = top_p;
   sa.rng = rng_state; sa.token = token; sa.ws = ws;
   rc |= launch_sample(sa, st);
+  if (embed_table)
+    rc |= launch_embed(embed_table, wdtype == DS4G_BF16, token, 1, vocab, hidden, x_next, st);
+  return hip_status(rc);
+}
+
+int ds4g_embed(int32_t vocab, int32_t hidden, int32_t wdtype, const void* table,
+               const int32_t* ids, int32_t T, float* x, void* stream) {
+  if (vocab <= 0 || hidden <= 0 || T <= 0 || !table || !ids || !x) return DS4G_ERR_INVALID_ARG;
+  if (wdtype != DS4G_F32 && wdtype != DS4G_BF16) return DS4G_ERR_INVALID_ARG;
+  if (hidden % 8) return DS4G_ERR_UNSUPPORTED;
+  clear_stale_error();
+  const int rc = launch_embed(table, wdtype == DS4G_BF16, ids, T, vocab, hidden, x,
+                              (hipStream_t)stream);
   return hip_status(rc);
 }
 

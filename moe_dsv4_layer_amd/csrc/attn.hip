@@ -146,24 +146,29 @@ attn_window_kernel(const float* __restrict__ q, const uint16_t* __restrict__ kc,
 
 // ---------------------------------------------------------------------------
 // ring_commit: copy the cached (k, v) of the last min(T, W) tokens into their
-// ring slots, then advance *pos by T.  One block; runs after every reader of
-// the old ring contents and of *pos.
-__global__ void __launch_bounds__(256)
+// ring slots (one block per token row, 16-byte copies).  Runs after every
+// reader of the old ring contents.  *pos is advanced by ring_advance.
+__global__ void __launch_bounds__(64)
 ring_commit_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int T,
                    int W, int dh, uint16_t* __restrict__ ring_k, uint16_t* __restrict__ ring_v,
-                   int64_t* pos) {
-  const long pos0 = *pos;
+                   const int64_t* __restrict__ pos) {
   const int first = T > W ? T - W : 0;
-  const int cnt = T - first;
-  for (int idx = threadIdx.x; idx < cnt * dh; idx += blockDim.x) {
-    const int r = idx / dh, e = idx - r * dh;
-    const int t = first + r;
-    const long slot = (pos0 + t) % W;
-    ring_k[slot * dh + e] = kc[(long)t * dh + e];
-    ring_v[slot * dh + e] = vc[(long)t * dh + e];
+  const int t = first + blockIdx.x;
+  const int slot = (int)((*pos + t) % W);
+  for (int c = threadIdx.x; c < dh / 8; c += blockDim.x) {
+    reinterpret_cast<uint4*>(ring_k + (long)slot * dh)[c] =
+        reinterpret_cast<const uint4*>(kc + (long)t * dh)[c];
+    reinterpret_cast<uint4*>(ring_v + (long)slot * dh)[c] =
+        reinterpret_cast<const uint4*>(vc + (long)t * dh)[c];
   }
-  __syncthreads();
-  if (threadIdx.x == 0) *pos = pos0 + T;
+}
+__global__ void ring_advance_kernel(int64_t* pos, int T) { *pos += T; }
+
+static void ring_commit(const AttnArgs& a, hipStream_t st) {
+  const int cnt = a.T < a.W ? a.T : a.W;
+  hipLaunchKernelGGL(ring_commit_kernel, dim3(cnt), dim3(64), 0, st, a.kc, a.vc, a.T, a.W, a.dh,
+                     a.ring_k, a.ring_v, a.pos);
+  hipLaunchKernelGGL(ring_advance_kernel, dim3(1), dim3(1), 0, st, a.pos, a.T);
 }
 
 int launch_attention(const AttnArgs& a, hipStream_t st) {
@@ -186,8 +191,7 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
     return -1;
   }
 #undef DS4G_ATT
-  hipLaunchKernelGGL(ring_commit_kernel, dim3(1), dim3(256), 0, st, a.kc, a.vc, a.T, a.W, a.dh,
-                     a.ring_k, a.ring_v, a.pos);
+  ring_commit(a, st);
   return 0;
 }
 
@@ -354,11 +358,15 @@ int launch_attention_decode(const AttnArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Prefill attention on the matrix cores (bf16 q, K, V; fp32 accumulate).
 //
-// A block takes BQ = 16 consecutive tokens and 16 heads.  MQA makes every
-// head of a token look at the same keys, so a 16-row MFMA tile is one
-// token's 16 heads and its window mask is one key range: token tl (0..15)
-// of the tile sees block key rows [tl, tl + W - 1] (block key row j is
-// position P0 - W + 1 + j, P0 = position of the tile's first token).  The
+// A block takes the tokens of one 16-position-aligned span of absolute
+// positions [A, A + 16) and 16 heads.  MQA makes every head of a token look
+// at the same keys, so a 16-row MFMA tile is one token's 16 heads and its
+// window mask is one key range: token tl (0..15) of the span sees block key
+// rows [tl, tl + W - 1] (block key row j is position A - W + 1 + j).
+// Aligning spans to absolute positions (not to the batch start) gives every
+// token the same key-to-lane placement and reduction order whatever batch it
+// arrives in, so a prefill resumed from a ring snapshot reproduces the
+// uninterrupted prefill bit for bit.  The
 // block stages its <= 16 + W - 1 keys (bf16, XOR-swizzled rows) and the
 // values transposed (so 8 consecutive keys of one dim are 16 contiguous
 // bytes) in LDS.  Each wave handles 4 tokens one at a time:
@@ -383,9 +391,11 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   __shared__ __align__(16) uint16_t Vt[DH * NKP];       // [dh][key]
   __shared__ __align__(16) uint16_t Ps[4][16 * NKP];    // per wave [head][key]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int t0 = blockIdx.x * BQ, h0 = blockIdx.y * 16;
+  const int h0 = blockIdx.y * 16;
   const long pos0 = *pos;
-  const long P0 = pos0 + t0;
+  const long P0 = (pos0 / BQ) * BQ + (long)blockIdx.x * BQ;   // span start A
+  const long t0 = P0 - pos0;                            // batch row of span position 0 (may be < 0)
+  if (t0 >= T) return;
   const long kbase = P0 - W + 1;                        // position of block key row 0
   const int nkeys = BQ + W - 1;                         // <= 143
   // ---- stage K (swizzled) and V (transposed); rows outside the sequence are 0
@@ -421,8 +431,10 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   uint16_t* P = Ps[wid];
   for (int tt = 0; tt < 4; ++tt) {
     const int tl = wid + 4 * tt;             // token of this wave's tile
-    const int t = t0 + tl;
-    if (t >= T) break;
+    const long tb = t0 + tl;                 // its batch row
+    if (tb >= T) break;
+    if (tb < 0) continue;                    // position before the batch
+    const int t = (int)tb;
     const long pt = P0 + tl;
     // ---- S = Q K^T for the token's 16 heads
     attn_bf16x8 qa[DH / 32];
@@ -514,7 +526,9 @@ int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   if (a.W > 128 || !a.q_bf16 || !a.o_bf16) return -1;
   hipLaunchKernelGGL((rope_qkv_kernel<uint16_t>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
                      a.dh, a.rd, a.base, a.pos, (uint16_t*)a.q, a.kc, a.vc);
-  const dim3 grid((a.T + 15) / 16, (a.H + 15) / 16);
+  // spans are aligned to absolute positions: one extra span covers the
+  // unknown (device-side) offset of the first position within its span
+  const dim3 grid((a.T + 15) / 16 + 1, (a.H + 15) / 16);
   if (a.dh == 128)
     hipLaunchKernelGGL((attn_prefill_mfma<128>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
                        a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
@@ -523,8 +537,7 @@ int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st) {
                        a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
   else
     return -1;
-  hipLaunchKernelGGL(ring_commit_kernel, dim3(1), dim3(256), 0, st, a.kc, a.vc, a.T, a.W, a.dh,
-                     a.ring_k, a.ring_v, a.pos);
+  ring_commit(a, st);
   return 0;
 }
 

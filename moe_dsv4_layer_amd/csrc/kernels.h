@@ -133,6 +133,8 @@ struct SampleArgs {
   void* ws;             // sampler workspace
 };
 size_t sample_ws_bytes(int V);
+int launch_embed(const void* table, int wdtype_bf16, const int* ids, int T, int vocab, int hidden,
+                 float* x, hipStream_t st);
 int launch_sample(const SampleArgs& s, hipStream_t st);
 
 }  // namespace ds4g

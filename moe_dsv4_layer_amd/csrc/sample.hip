@@ -412,4 +412,40 @@ int launch_sample(const SampleArgs& s, hipStream_t st) {
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// Token embedding (ds4-learning 端到端推理流程, 阶段四 4.1): row id of the
+// table, widened to fp32.  One block per token; ids outside the table give a
+// zero row.  `ids` may live on the device only (sampled tokens).
+template <typename WT>
+__global__ void __launch_bounds__(256)
+embed_kernel(const WT* __restrict__ table, const int* __restrict__ ids, int vocab, int hidden,
+             float* __restrict__ x) {
+  const int t = blockIdx.x;
+  const int id = ids[t];
+  const bool ok = id >= 0 && id < vocab;
+  const WT* row = table + (long)(ok ? id : 0) * hidden;
+  float* out = x + (long)t * hidden;
+  for (int c = threadIdx.x; c < hidden / 8; c += blockDim.x) {
+    Chunk8<WT> ch;
+    ch.load(row + c * 8);
+    float f[8];
+    ch.widen(f);
+    float4* o4 = reinterpret_cast<float4*>(out + c * 8);
+    o4[0] = ok ? make_float4(f[0], f[1], f[2], f[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    o4[1] = ok ? make_float4(f[4], f[5], f[6], f[7]) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+int launch_embed(const void* table, int wdtype_bf16, const int* ids, int T, int vocab, int hidden,
+                 float* x, hipStream_t st) {
+  if (hidden % 8 || T <= 0) return -1;
+  if (wdtype_bf16)
+    hipLaunchKernelGGL((embed_kernel<uint16_t>), dim3(T), dim3(256), 0, st,
+                       (const uint16_t*)table, ids, vocab, hidden, x);
+  else
+    hipLaunchKernelGGL((embed_kernel<float>), dim3(T), dim3(256), 0, st, (const float*)table, ids,
+                       vocab, hidden, x);
+  return 0;
+}
+
 }  // namespace ds4g

@@ -91,6 +91,7 @@ def test_prefill_rejects_before_launch():
     assert _prefill(_cfg(wdtype=7), w, ring, 0x1000, 8, 0x1000, ok_ws) == ds4g.ERR_INVALID_ARG
     assert _prefill(_cfg(rope_dim=3), w, ring, 0x1000, 8, 0x1000, ok_ws) == ds4g.ERR_INVALID_ARG
     assert _prefill(_cfg(n_experts=600), w, ring, 0x1000, 8, 0x1000, ok_ws) == ds4g.ERR_UNSUPPORTED
+    assert _prefill(_cfg(n_heads=6), w, ring, 0x1000, 8, 0x1000, ok_ws) == ds4g.ERR_UNSUPPORTED
 
 
 def test_decode_and_sample_reject_before_launch():
@@ -111,7 +112,7 @@ def test_decode_and_sample_reject_before_launch():
         a = dict(args, **kw)
         return L.ds4g_lmhead_sample(a["hidden"], a["vocab"], a["wd"], a["norm"], a["eps"], a["w"],
                                     a["x"], a["T"], a["p"], a["rng"], a["logits"], a["tok"],
-                                    a["ws"], a["n"], None)
+                                    a.get("etab"), a.get("xnext"), a["ws"], a["n"], None)
     assert call(rng=None) == ds4g.ERR_INVALID_ARG          # sampling needs the generator
     assert call(vocab=0) == ds4g.ERR_INVALID_ARG
     assert call(wd=5) == ds4g.ERR_INVALID_ARG
@@ -120,3 +121,11 @@ def test_decode_and_sample_reject_before_launch():
     assert call(vocab=300000) == ds4g.ERR_UNSUPPORTED
     assert call(T=float("nan")) == ds4g.ERR_INVALID_ARG
     assert call(ws=0x1001) == ds4g.ERR_INVALID_ARG
+    assert call(etab=0x1000) == ds4g.ERR_INVALID_ARG        # table without x_next
+    assert call(xnext=0x1000) == ds4g.ERR_INVALID_ARG
+    E = L.ds4g_embed
+    assert E(0, 64, ds4g.BF16, 0x1000, 0x1000, 4, 0x1000, None) == ds4g.ERR_INVALID_ARG
+    assert E(10, 64, ds4g.BF16, None, 0x1000, 4, 0x1000, None) == ds4g.ERR_INVALID_ARG
+    assert E(10, 64, ds4g.BF16, 0x1000, 0x1000, 0, 0x1000, None) == ds4g.ERR_INVALID_ARG
+    assert E(10, 60, ds4g.BF16, 0x1000, 0x1000, 4, 0x1000, None) == ds4g.ERR_UNSUPPORTED
+    assert E(10, 64, 3, 0x1000, 0x1000, 4, 0x1000, None) == ds4g.ERR_INVALID_ARG
