@@ -12,6 +12,12 @@ experts top-6 + 1 shared, SwiGLU inter 1024, bf16 weights, fp32 accumulate):
            (reported as prefill_tok_s).
   lm_head  final norm + 129280 x 4096 lm_head + temperature 0.7 / top-p
            0.95 sampler (reported as lmhead_sample_us).
+  stack43  43 full-size layers (expert inter 512) + embedding + lm_head:
+           prefill of 512 tokens, then decode steps (43 layers + lm_head +
+           sampler + next-token embedding, one graph replay per token) at
+           temperature 0.7 / top-p 0.95; and a 16994-token layer-major
+           prefill, plus the 148-token suffix resumed from a ring snapshot
+           taken at 16846 (reported under "stack43").
 
 Every input lives in HBM before the timed region starts.  Times come from
 HIP events on the stream the library launches on.  The CPU baseline is the
@@ -90,6 +96,108 @@ def cpu_baseline(shape, w_dev, h_dev, n_tokens: int):
                       f"window pre-filled with {shape.window} positions), {dt:.1f} s"}
 
 
+def stack_decode_bytes(s, n_layers: int, vocab: int) -> int:
+    """Per token: every layer's decode bytes, then the final norm and lm_head
+    rows, and the next token's embedding row."""
+    return n_layers * layer_decode_bytes(s) + 2 * vocab * s.hidden + 2 * s.hidden \
+        + 4 * vocab + 2 * s.hidden
+
+
+def bench_stack43(decode_steps: int) -> dict:
+    import torch
+    import numpy as np
+    import synth
+    from moe_dsv4_layer_amd.stack import Stack
+    wl = synth.WORKLOADS["stack43_decode"]
+    wr = synth.WORKLOADS["stack43_resume"]
+    s = wl.layer
+    layers = [synth.layer_weights(s, wl.seed, layer=l, device="cuda") for l in range(wl.n_layers)]
+    head = synth.head_weights(s, wl.vocab, wl.seed, device="cuda")
+    st = Stack(s, layers, head, max_tokens=wr.prompt)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {"workload": "43 full-size layers (expert inter 512) + embedding + lm_head 129280",
+           "weight_bytes": int(sum(t.numel() * t.element_size() for w in layers for t in w.values())
+                               + sum(t.numel() * t.element_size() for t in head.values()))}
+    # ---- prefill of 512 tokens, then graph-replayed decode steps
+    ids = torch.as_tensor(synth.token_ids(wl.prompt, wl.vocab, wl.seed), device="cuda")
+    for rep in range(2):
+        st.reset()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        x = st.embed(ids)
+        st.prefill(x)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms_pre = e0.elapsed_time(e1)
+    out["prefill_512_ms"] = round(ms_pre, 3)
+    out["prefill_512_tok_s"] = round(wl.prompt / (ms_pre * 1e-3), 1)
+    rng = torch.tensor([synth.rng_seed(wl.seed) & 0x7FFFFFFFFFFFFFFF], dtype=torch.int64,
+                       device="cuda")
+    xl = x[-1].clone()
+    st.sample(xl, wl.temperature, wl.top_p, rng, x_next=xl)     # first token from the prompt
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    torch.cuda.synchronize()
+
+    def step():
+        st.decode(xl)
+        st.sample(xl, wl.temperature, wl.top_p, rng, x_next=xl)
+    with torch.cuda.stream(cs):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        step()
+    torch.cuda.synchronize()
+    n = max(1, decode_steps - 2)
+    e0.record(stream)
+    for _ in range(n):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_tok = e0.elapsed_time(e1) / n
+    b = stack_decode_bytes(s, wl.n_layers, wl.vocab)
+    out["decode_ms_per_token"] = round(ms_tok, 4)
+    out["decode_tok_s"] = round(1e3 / ms_tok, 2)
+    out["decode_bytes_per_token"] = b
+    out["decode_hbm_frac"] = round(b / (ms_tok * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    out["positions_after"] = int(st.pos[0].item())
+    # ---- 16994-token prefill, and the 148-token suffix from a snapshot at 16846
+    ids = torch.as_tensor(synth.token_ids(wr.prompt, wl.vocab, wr.seed), device="cuda")
+    P = wr.snapshot_at
+    st.reset()
+    x = st.embed(ids[:P])
+    st.prefill(x)
+    snap = st.snapshot()
+    st.reset()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    x = st.embed(ids)
+    st.prefill(x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_full = e0.elapsed_time(e1)
+    st.restore(snap)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    xs = st.embed(ids[P:])
+    st.prefill(xs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_suf = e0.elapsed_time(e1)
+    fl = wr.n_layers * layer_flops(s, wr.prompt)
+    out["prefill_16994_ms"] = round(ms_full, 2)
+    out["prefill_16994_tok_s"] = round(wr.prompt / (ms_full * 1e-3), 1)
+    out["prefill_16994_tflops"] = round(fl / (ms_full * 1e-3) / 1e12, 1)
+    out["prefill_16994_mfma_frac"] = round(fl / (ms_full * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+    out["resume_suffix_148_ms"] = round(ms_suf, 3)
+    out["resume_suffix_matches_full"] = bool(torch.equal(xs, x[P:]))
+    del st, layers, head
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,8 +206,10 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--weight-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-graph", action="store_true", help="launch decode eagerly")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer workloads")
+    ap.add_argument("--stack-decode-steps", type=int, default=256)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -119,6 +229,7 @@ def main() -> int:
 
     # ------------------------------------------------------------ setup
     layers = []
+    w_cpu = None
     for l in range(args.weight_sets):
         w = synth.layer_weights(s, wl.seed, layer=l, device=dev)
         rk = torch.zeros((s.window, s.head_dim), dtype=torch.bfloat16, device=dev)
@@ -126,6 +237,8 @@ def main() -> int:
         pos = torch.zeros(1, dtype=torch.int64, device=dev)
         layers.append(dict(w=w, cw=ds4g.make_weights(w), rk=rk, rv=rv, pos=pos,
                            ring=ds4g.make_ring(rk, rv, pos)))
+        if l == 0:
+            w_cpu = w
     T_pre = synth.WORKLOADS["layer_prefill_2048"].prompt
     ws = ds4g.alloc_workspace(ds4g.workspace_bytes(cfg, T_pre, 129280))
     h_all = synth.hidden(s.window + 64, s.hidden, wl.seed, device=dev)
@@ -270,8 +383,12 @@ def main() -> int:
                           "hbm_frac": round(lm_bytes / (us_lm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "wall_s_decode": round(t_wall, 3),
     }
+    if not args.no_stack:
+        del layers, xs, ws
+        torch.cuda.empty_cache()
+        rec["stack43"] = bench_stack43(args.stack_decode_steps)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(s, layers[0]["w"], h_all, args.cpu_tokens)
+        rec["cpu_baseline"] = cpu_baseline(s, w_cpu, h_all, args.cpu_tokens)
     print(json.dumps(rec))
     return 0
 
