@@ -180,7 +180,9 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.ksplit = rsplit; g.part_stride = (long)T * E;
     rc |= launch_gemm(g, false, bf ? 1 : 0, st);
   }
-  const int tile_m = bf ? 128 : 64;
+  // tile height of the grouped expert GEMMs: follow the mean rows per expert
+  const int mean_rows = (T * k + E - 1) / E;
+  const int tile_m = (!bf || mean_rows <= 64) ? 64 : 128;
   RouteArgs ra{};
   ra.logits = at<float>(ws, L.lpart); ra.nsplit = rsplit;
   ra.logits_sum = at<float>(ws, L.logits); ra.T = T; ra.E = E; ra.k = k;
@@ -200,7 +202,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     GemmArgs g{};
     g.A = yA; g.lda = d; g.gather = ra.gather; g.B = w.gate; g.B2 = w.up;
     g.b_stride = (long)I * d; g.N = I; g.K = d; g.tiles = ra.tiles; g.ntiles = ra.ntiles;
-    g.row_off = ra.offset; g.max_tiles = max_tiles;
+    g.row_off = ra.offset; g.max_tiles = max_tiles; g.rows_hint = tile_m;
     g.epi = bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32; g.C = at<void>(ws, L.z); g.ldc = I;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
@@ -216,17 +218,18 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     GemmArgs g{};
     g.A = at<void>(ws, L.z); g.lda = I; g.B = w.down; g.b_stride = (long)d * I; g.N = d;
     g.K = I; g.tiles = ra.tiles; g.ntiles = ra.ntiles; g.row_off = ra.offset;
-    g.max_tiles = max_tiles; g.epi = EPI_F32; g.C = at<void>(ws, L.part); g.ldc = d;
+    g.max_tiles = max_tiles; g.rows_hint = tile_m; g.epi = EPI_F32; g.C = at<void>(ws, L.part);
+    g.ldc = d;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
-  // shared down + combine: x = h2 + shared + sum_j w_j part_j
+  // shared down (x = h2 + shared), then combine: x += sum_j w_j part_j
   {
     GemmArgs g{};
     g.A = at<void>(ws, L.zs); g.lda = Is; g.B = w.sh_down; g.M = T; g.N = d; g.K = Is;
-    g.epi = EPI_COMBINE; g.C = x; g.ldc = d; g.part = at<float>(ws, L.part);
-    g.pos_of = ra.pos_of; g.topk_w = ra.topk_w; g.topk = k; g.ldp = d;
+    g.epi = EPI_RESID; g.C = x; g.ldc = d;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
+  rc |= launch_moe_combine(x, at<float>(ws, L.part), ra.pos_of, ra.topk_w, T, d, k, st);
   if (routing) {
     copy_out(routing->topk_idx, ra.topk_idx, (size_t)T * k * 4, st);
     copy_out(routing->topk_w, ra.topk_w, (size_t)T * k * 4, st);

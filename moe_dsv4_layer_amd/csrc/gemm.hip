@@ -154,123 +154,182 @@ gemm_simt_kernel(GemmArgs g) {
 }
 
 // =========================================================================
-// MFMA GEMM (bf16 activations and weights)
+// MFMA GEMM (bf16 activations and weights), v_mfma_f32_32x32x16_bf16.
+//
+// Block tile BM x BN x 64, 4 waves in a WM x WN grid, wave tile TM x TN of
+// 32x32 fragments.  Operand layout of the instruction (lane l):
+//   A: row l%32, k = 8*(l/32) .. +7 of the 16-wide k step (16 bytes)
+//   B: col l%32, same k
+//   C: acc[4j+i] = C[8j + 4*(l/32) + i][l%32]
+// Both operands are K-contiguous in memory and in LDS; an LDS row is 8
+// chunks of 16 bytes and chunk c of row r is stored at c ^ (r & 7), so the
+// 8 rows read by 8 consecutive lanes hit 8 different chunk slots.  Global
+// loads for the next k tile are issued before the current tile's MFMAs;
+// LDS is double buffered (one barrier per k tile).
+// SwiGLU (DUAL): B tile rows come in 32-row blocks alternating gate / up
+// rows of the same output columns, so a wave's fragment pair (fn, fn+1)
+// holds gate and up of the same (row, col) in the same lane.
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-// LDS tile: 128 rows x 64 k of bf16 = 128 rows x 8 chunks of 16 B; chunk c
-// of row r is stored at chunk (c ^ (r & 7)).
-__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+#ifndef DS4G_SWZ_SHIFT
+#define DS4G_SWZ_SHIFT 0
+#endif
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * 8 + (c ^ ((r >> DS4G_SWZ_SHIFT) & 7));
+}
 
-template <bool DUAL>
+template <int BM, int BN, int WM, int WN, bool DUAL>
 __global__ void __launch_bounds__(256)
 gemm_mfma_kernel(GemmArgs g) {
-  constexpr int BM = 128, BN = 128, BK = 64;
+  constexpr int BK = 64;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;
+  static_assert(WM * WN == 4 && FM >= 1 && FN >= 1, "4 waves, 32x32 fragments");
+  static_assert(!DUAL || FN % 2 == 0, "SwiGLU pairs gate/up fragments");
   __shared__ uint4 As[2][BM * 8];
   __shared__ uint4 Bs[2][BN * 8];
   TileInfo ti;
   if (!tile_info(g, blockIdx.y, BM, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WN, wn = wid % WN;
   const uint16_t* A = static_cast<const uint16_t*>(g.A);
   const uint16_t* B = static_cast<const uint16_t*>(g.B) + ti.boff;
   const uint16_t* B2 = DUAL ? static_cast<const uint16_t*>(g.B2) + ti.boff : nullptr;
-  // output columns of this block: BN (plain) or BN/2 (SwiGLU pairs)
   const int ncol0 = blockIdx.x * (DUAL ? BN / 2 : BN);
 
-  // loader: 1024 chunks per operand tile, 4 per thread; chunk q -> row q/8, c q%8
-  const uint16_t* asrc[4];
-  const uint16_t* bsrc[4];
+  const uint16_t* asrc[ACH];
+  const uint16_t* bsrc[BCH];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < ACH; ++i) {
     const int q = tid + 256 * i, r = q >> 3, c = q & 7;
     const int arow = ti.row0 + r;
     asrc[i] = nullptr;
     if (arow < ti.row1) asrc[i] = A + (long)(g.gather ? g.gather[arow] : arow) * g.lda + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < BCH; ++i) {
+    const int q = tid + 256 * i, r = q >> 3, c = q & 7;
     int brow;
     const uint16_t* bb = B;
     if (DUAL) {
-      const int blk = r >> 4;
+      const int blk = r >> 5;
       bb = (blk & 1) ? B2 : B;
-      brow = ncol0 + (blk >> 1) * 16 + (r & 15);
+      brow = ncol0 + (blk >> 1) * 32 + (r & 31);
     } else {
       brow = ncol0 + r;
     }
     bsrc[i] = (brow < g.N) ? bb + (long)brow * g.K + c * 8 : nullptr;
   }
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k0) {
+  uint4 ra[ACH], rb[BCH];
+  auto gload_into = [&](int k0, uint4 (&xa)[ACH], uint4 (&xb)[BCH]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = asrc[i] ? *reinterpret_cast<const uint4*>(asrc[i] + k0) : make_uint4(0, 0, 0, 0);
-      rb[i] = bsrc[i] ? ldg_nt16(bsrc[i] + k0)
-                      : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < ACH; ++i)
+      xa[i] = asrc[i] ? *reinterpret_cast<const uint4*>(asrc[i] + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < BCH; ++i)
+      xb[i] = bsrc[i] ? ldg_nt16(bsrc[i] + k0) : make_uint4(0, 0, 0, 0);
+  };
+  auto lstore_from = [&](int st, const uint4 (&xa)[ACH], const uint4 (&xb)[BCH]) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int q = tid + 256 * i;
+      As[st][swz(q >> 3, q & 7)] = xa[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int q = tid + 256 * i;
+      Bs[st][swz(q >> 3, q & 7)] = xb[i];
     }
   };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-      As[st][swz(r, c)] = ra[i];
-      Bs[st][swz(r, c)] = rb[i];
-    }
-  };
+  auto gload = [&](int k0) { gload_into(k0, ra, rb); };
+  auto lstore = [&](int st) { lstore_from(st, ra, rb); };
 
-  f32x4 acc[4][4];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = g.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int lr = lane & 15, lg = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  const int lr = lane & 31, lg = lane >> 5;
+  auto compute = [&](int st) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[4], bfr[4];
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = As[st][swz(wm * 64 + i * 16 + lr, ks * 4 + lg)];
+      for (int i = 0; i < FM; ++i) {
+        const uint4 v = As[st][swz(wm * TM + i * 32 + lr, ks * 2 + lg)];
         af[i] = *reinterpret_cast<const bf16x8*>(&v);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 v = Bs[st][swz(wn * 64 + j * 16 + lr, ks * 4 + lg)];
+      for (int j = 0; j < FN; ++j) {
+        const uint4 v = Bs[st][swz(wn * TN + j * 32 + lr, ks * 2 + lg)];
         bfr[j] = *reinterpret_cast<const bf16x8*>(&v);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+  };
+#if DS4G_GEMM_PF2
+  // two register sets: tile t is loaded into set t&1 two iterations before
+  // it is computed, and stored to LDS at the end of the iteration before
+  uint4 ra2[ACH], rb2[BCH];
+  gload_into(0, ra, rb);
+  lstore_from(0, ra, rb);
+  if (nk > 1) gload_into(BK, ra2, rb2);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 2 < nk) gload_into((kt + 2) * BK, ra, rb);
+    compute(0);
+    if (kt + 1 < nk) lstore_from(1, ra2, rb2);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    if (kt + 3 < nk) gload_into((kt + 3) * BK, ra2, rb2);
+    compute(1);
+    if (kt + 2 < nk) lstore_from(0, ra, rb);
+    __syncthreads();
+  }
+#else
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+    compute(st);
     if (kt + 1 < nk) lstore(st ^ 1);
     __syncthreads();
   }
+#endif
 
-  // epilogue: acc[i][j][r] is C[row = i*16 + 4*lg + r][col = j*16 + lr] of the wave tile
+  // epilogue
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = ti.row0 + wm * 64 + i * 16 + 4 * lg + r;
-      if (row >= ti.row1) continue;
-      if (DUAL) {
+    for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          const int col = ncol0 + (wn * 2 + (j >> 1)) * 16 + lr;
-          if (col < g.N) epi_swiglu(g, row, col, acc[i][j][r], acc[i][j + 1][r]);
-        }
-      } else {
+      for (int ii = 0; ii < 4; ++ii) {
+        const int row = ti.row0 + wm * TM + i * 32 + 8 * jj + 4 * lg + ii;
+        if (row >= ti.row1) continue;
+        if (DUAL) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = ncol0 + wn * 64 + j * 16 + lr;
-          if (col < g.N) epi_store(g, row, col, acc[i][j][r]);
+          for (int j = 0; j < FN; j += 2) {
+            const int col = ncol0 + (wn * (TN / 2)) + (j >> 1) * 32 + lr;
+            if (col < g.N) epi_swiglu(g, row, col, acc[i][j][4 * jj + ii], acc[i][j + 1][4 * jj + ii]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = ncol0 + wn * TN + j * 32 + lr;
+            if (col < g.N) epi_store(g, row, col, acc[i][j][4 * jj + ii]);
+          }
         }
       }
     }
@@ -281,11 +340,27 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
   const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
   if (mfma) {
     if (g.K % 64) return -1;
-    const int bn = dual ? 64 : 128;
-    const int mt = g.tiles ? g.max_tiles : (g.M + 127) / 128;
-    dim3 grid((g.N + bn - 1) / bn, mt);
-    if (dual) hipLaunchKernelGGL((gemm_mfma_kernel<true>), grid, dim3(256), 0, st, g);
-    else hipLaunchKernelGGL((gemm_mfma_kernel<false>), grid, dim3(256), 0, st, g);
+    // rows per tile: follow the rows a group (or the whole problem) has
+    int rows = g.M;
+    if (g.tiles) rows = g.rows_hint > 0 ? g.rows_hint : 128;
+#define DS4G_MF(BM_, BN_, WM_, WN_)                                                      \
+  {                                                                                      \
+    const int bn_out = dual ? BN_ / 2 : BN_;                                             \
+    const int mt = g.tiles ? g.max_tiles : (g.M + BM_ - 1) / BM_;                        \
+    dim3 grid((g.N + bn_out - 1) / bn_out, mt);                                          \
+    if (dual) hipLaunchKernelGGL((gemm_mfma_kernel<BM_, BN_, WM_, WN_, true>), grid, dim3(256), 0, st, g);  \
+    else hipLaunchKernelGGL((gemm_mfma_kernel<BM_, BN_, WM_, WN_, false>), grid, dim3(256), 0, st, g);      \
+    return 0;                                                                            \
+  }
+    if (g.tiles) {   // the tile list was built for exactly rows_hint rows per tile
+      if (rows == 64) DS4G_MF(64, 256, 1, 4)
+      if (rows == 128) DS4G_MF(128, 128, 2, 2)
+      return -1;
+    }
+    // 256x128 tiles measured slower than 128x128 on every layer shape
+    if (rows <= 64) DS4G_MF(64, 256, 1, 4)
+    DS4G_MF(128, 128, 2, 2)
+#undef DS4G_MF
   } else {
     const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
     if (g.K % (16 * nsplit)) return -1;

@@ -27,6 +27,7 @@ struct GemmArgs {
   const int* ntiles;    // grouped: number of valid tiles, device
   const int* row_off;   // grouped: [G+1] first row of each group, device
   int max_tiles;        // grouped: grid bound (>= *ntiles)
+  int rows_hint;        // grouped: expected rows per group (picks the tile height)
   int epi;
   void* C;
   int ldc;
@@ -122,6 +123,9 @@ struct RouteArgs {
   int* out_count; int* out_offset;
 };
 int launch_route(const RouteArgs& r, hipStream_t st);
+// x[t] += sum_j w[t,j] part[pos_of[t*k+j]] (fixed j order)
+int launch_moe_combine(float* x, const float* part, const int* pos_of, const float* w, int T,
+                       int d, int k, hipStream_t st);
 
 // ---------------------------------------------------------------- sampler
 struct SampleArgs {

@@ -222,4 +222,36 @@ int launch_route(const RouteArgs& r, hipStream_t st) {
   return 0;
 }
 
+// ------------------------------------------------------------ MoE combine
+// x[t] += sum_j w[t, j] * part[pos_of[t*k + j]], j = 0..k-1 in order, where
+// x already holds h2 + shared-expert output.  One block per token: the k
+// expert-output rows are read whole (contiguous), 4 floats per thread.
+__global__ void __launch_bounds__(256)
+moe_combine_kernel(float* __restrict__ x, const float* __restrict__ part,
+                   const int* __restrict__ pos_of, const float* __restrict__ w, int d, int k) {
+  const int t = blockIdx.x;
+  __shared__ int rows[8];
+  __shared__ float ws[8];
+  if (threadIdx.x < k) {
+    rows[threadIdx.x] = pos_of[t * k + threadIdx.x];
+    ws[threadIdx.x] = w[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    float4 a = *reinterpret_cast<const float4*>(x + (long)t * d + c);
+    for (int j = 0; j < k; ++j) {
+      const float4 p = *reinterpret_cast<const float4*>(part + (long)rows[j] * d + c);
+      a.x += ws[j] * p.x; a.y += ws[j] * p.y; a.z += ws[j] * p.z; a.w += ws[j] * p.w;
+    }
+    *reinterpret_cast<float4*>(x + (long)t * d + c) = a;
+  }
+}
+
+int launch_moe_combine(float* x, const float* part, const int* pos_of, const float* w, int T,
+                       int d, int k, hipStream_t st) {
+  if (d % 4 || k > 8) return -1;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, st, x, part, pos_of, w, d, k);
+  return 0;
+}
+
 }  // namespace ds4g
