@@ -3,6 +3,7 @@
 // every step of the math runs in the kernels of this directory.
 #include "../../include/ds4g.h"
 #include "kernels.h"
+#include <algorithm>
 
 #include <hip/hip_runtime.h>
 #include <stdio.h>
@@ -332,6 +333,13 @@ int ds4g_layer_prefill(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
   if (!x || !ws || T <= 0) return DS4G_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
   if ((long)T * cfg->top_k >= (1 << 24) || T > (1 << 20)) return DS4G_ERR_UNSUPPORTED;
+  if (cfg->wdtype == DS4G_BF16) {
+    // the MFMA GEMMs address their bf16 operands with 32-bit byte offsets
+    const double widest = std::max({(double)cfg->hidden, (double)cfg->n_heads * cfg->head_dim,
+                                    (double)cfg->qkv_rank, (double)cfg->shared_inter,
+                                    (double)cfg->top_k * cfg->ffn_inter});
+    if ((double)T * widest * 2.0 >= 4294967296.0) return DS4G_ERR_UNSUPPORTED;
+  }
   if (ws_bytes < layout(*cfg, T).total) return DS4G_ERR_WORKSPACE;
   clear_stale_error();
   return prefill_impl(*cfg, *w, *ring, x, T, routing, ws, (hipStream_t)stream);

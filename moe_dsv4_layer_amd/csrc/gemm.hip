@@ -1,10 +1,9 @@
 // GEMMs of the layer-major prefill: C = A . B^T with A the activations
 // [rows, K] and B the weights [N, K] (both K-contiguous).
 //
-//   gemm_mfma  bf16 x bf16 -> fp32 on the gfx950 matrix cores
-//              (v_mfma_f32_16x16x32_bf16), 128x128x64 tiles, 4 waves of
-//              64x64, LDS double buffer with an XOR swizzle so the 16-byte
-//              operand reads of 8 consecutive rows hit distinct banks.
+//   gemm_dma   bf16 x bf16 -> fp32 on the gfx950 matrix cores
+//              (v_mfma_f32_32x32x16_bf16), BM x BN x 64 tiles, 4 or 8 waves,
+//              an S-stage LDS ring filled by direct global -> LDS loads.
 //   gemm_simt  fp32 activations x (fp32 | bf16) weights on the vector ALUs,
 //              64x64x16 tiles, 4x4 outputs per thread.  Used where the
 //              activations must stay fp32 (the router logits decide integer
@@ -13,7 +12,7 @@
 // Both take the same arguments: an optional row gather of A, optional
 // grouping (one weight matrix per expert, rows of an expert contiguous in
 // "permuted" order, a device tile list), and fused epilogues (fp32 store,
-// bf16 store, residual add, SwiGLU of a (gate, up) pair, MoE combine).
+// bf16 store, residual add, SwiGLU of a (gate, up) pair).
 //
 // The layer-major prefill (ds4-learning 端到端推理流程, 阶段三 逐层批处理) runs
 // every token through one weight matrix before the next, which is what turns
@@ -31,17 +30,6 @@ __device__ __forceinline__ void epi_store(const GemmArgs& g, int row, int col, f
     case EPI_RESID: {
       float* c = static_cast<float*>(g.C) + (long)row * g.ldc + col;
       *c = *c + v;
-      break;
-    }
-    case EPI_COMBINE: {
-      // x[t] = h2[t] + shared[t] + sum_j w[t, j] * part[pos_of[t*k + j]]
-      float* c = static_cast<float*>(g.C) + (long)row * g.ldc + col;
-      float acc = *c + v;
-      for (int j = 0; j < g.topk; ++j) {
-        const int e = row * g.topk + j;
-        acc += g.topk_w[e] * g.part[(long)g.pos_of[e] * g.ldp + col];
-      }
-      *c = acc;
       break;
     }
     default: break;
@@ -156,95 +144,190 @@ gemm_simt_kernel(GemmArgs g) {
 // =========================================================================
 // MFMA GEMM (bf16 activations and weights), v_mfma_f32_32x32x16_bf16.
 //
-// Block tile BM x BN x 64, 4 waves in a WM x WN grid, wave tile TM x TN of
-// 32x32 fragments.  Operand layout of the instruction (lane l):
+// Block tile BM x BN x 64 with WM x WN waves, wave tile TM x TN of 32x32
+// fragments.  Operand layout of the instruction (lane l):
 //   A: row l%32, k = 8*(l/32) .. +7 of the 16-wide k step (16 bytes)
 //   B: col l%32, same k
 //   C: acc[4j+i] = C[8j + 4*(l/32) + i][l%32]
-// Both operands are K-contiguous in memory and in LDS; an LDS row is 8
-// chunks of 16 bytes and chunk c of row r is stored at c ^ (r & 7), so the
-// 8 rows read by 8 consecutive lanes hit 8 different chunk slots.  Global
-// loads for the next k tile are issued before the current tile's MFMAs;
-// LDS is double buffered (one barrier per k tile).
-// SwiGLU (DUAL): B tile rows come in 32-row blocks alternating gate / up
-// rows of the same output columns, so a wave's fragment pair (fn, fn+1)
+// Both operands are K-contiguous in memory and in LDS.  Rows past the end of
+// the tile (ragged M, N) load a clamped valid row, so no load is
+// conditional; their results are never stored.  Every output element sums
+// its K products in the same order whatever the tiling of M, which keeps a
+// prefill split into chunks bit-identical to the whole.
+// SwiGLU (EPI_SWIGLU_*): B tile rows come in 32-row blocks alternating gate /
+// up rows of the same output columns, so a wave's fragment pair (fn, fn+1)
 // holds gate and up of the same (row, col) in the same lane.
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-#ifndef DS4G_SWZ_SHIFT
-#define DS4G_SWZ_SHIFT 0
-#endif
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * 8 + (c ^ ((r >> DS4G_SWZ_SHIFT) & 7));
+template <int EPI>
+__device__ __forceinline__ void epi_store_t(const GemmArgs& g, int row, int col, float v) {
+  if (EPI == EPI_F32) static_cast<float*>(g.C)[(long)row * g.ldc + col] = v;
+  if (EPI == EPI_BF16) static_cast<uint16_t*>(g.C)[(long)row * g.ldc + col] = f32_to_bf16(v);
+  if (EPI == EPI_RESID) {
+    float* c = static_cast<float*>(g.C) + (long)row * g.ldc + col;
+    *c = *c + v;
+  }
 }
 
-template <int BM, int BN, int WM, int WN, bool DUAL>
-__global__ void __launch_bounds__(256)
-gemm_mfma_kernel(GemmArgs g) {
-  constexpr int BK = 64;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;
-  static_assert(WM * WN == 4 && FM >= 1 && FN >= 1, "4 waves, 32x32 fragments");
+// Epilogue of a wave tile: rows row0 + 32 i + 8 jj + 4 (lane/32) + ii, columns
+// col0 + 32 j + lane%32 (SwiGLU: fragment pairs (j, j+1) give one column
+// block).  For the residual add the 16 old values of a fragment are loaded
+// before any of them is stored, so the loads overlap instead of alternating
+// with the stores.
+template <int EPI, int FM, int FN>
+__device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, const f32x16 (&acc)[FM][FN],
+                                              int row0, int row1, int col0, int lane) {
+  constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32);
+  const int lr = lane & 31, lg = lane >> 5;
+  if (EPI == EPI_RESID) {
+    float* C = static_cast<float*>(g.C);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = col0 + j * 32 + lr;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float old[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = min(row0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3), row1 - 1);
+          old[e] = C[(long)row * g.ldc + col];
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = row0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+          if (row < row1) C[(long)row * g.ldc + col] = old[e] + acc[i][j][e];
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = row0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+      if (row >= row1) continue;
+      if (DUAL) {
+#pragma unroll
+        for (int j = 0; j < FN; j += 2) {
+          const int col = col0 + (j >> 1) * 32 + lr;
+          if (col < g.N) epi_swiglu(g, row, col, acc[i][j][e], acc[i][j + 1][e]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = col0 + j * 32 + lr;
+          if (col < g.N) epi_store_t<EPI>(g, row, col, acc[i][j][e]);
+        }
+      }
+    }
+}
+
+// =========================================================================
+// MFMA GEMM with an S-stage LDS ring filled by direct global -> LDS loads
+// (buffer_load_dwordx4 ... lds): each lane's 16 bytes land in a fixed LDS
+// slot (wave base in M0 + 16 * lane), so the swizzle is applied on the
+// global side: LDS slot s of row r receives logical chunk s ^ f(r).  No
+// registers stage the tiles and tile t+S-1 is in flight while tile t is
+// multiplied.  The loads are issued from inline assembly and counted with
+// explicit vmcnt waits: the compiler's own LDS-DMA tracking would wait for
+// every outstanding load before any LDS read, which defeats the pipeline.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+  r.z = -1;                 // num_records: offsets are bounded by the caller (32-bit)
+  r.w = 0x00020000;         // raw dword access
+  return r;
+}
+__device__ __forceinline__ void dma16(i32x4_t rs, uint32_t lds_byte, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_byte), "v"(voff), "s"(rs) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+
+// row swizzle of the 8 16-byte chunks of a 128-byte LDS row: conflict-free
+// for the fragment reads (32 rows x 2 chunks per instruction)
+__device__ __forceinline__ int swz1(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+template <int BM, int BN, int WM, int WN, int S, int EPI>
+__global__ void __launch_bounds__(64 * WM * WN)
+gemm_dma_kernel(GemmArgs g) {
+  constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32);
+  constexpr int NW = WM * WN, BK = 64;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int ROWS = BM + BN;              // LDS rows per stage (A rows, then B rows)
+  constexpr int NDMA = ROWS / (8 * NW);      // 1 KB loads per wave per stage
+  static_assert(FM >= 1 && FN >= 1 && TM * WM == BM && TN * WN == BN, "32x32 fragments");
+  static_assert(NDMA * 8 * NW == ROWS && BM % 8 == 0, "whole 8-row loads per wave");
   static_assert(!DUAL || FN % 2 == 0, "SwiGLU pairs gate/up fragments");
-  __shared__ uint4 As[2][BM * 8];
-  __shared__ uint4 Bs[2][BN * 8];
+  static_assert(S >= 2 && (S - 2) * NDMA <= 63, "vmcnt range");
+  __shared__ u32x4_t smem[S][ROWS * 8];
   TileInfo ti;
   if (!tile_info(g, blockIdx.y, BM, ti)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / WN, wn = wid % WN;
-  const uint16_t* A = static_cast<const uint16_t*>(g.A);
-  const uint16_t* B = static_cast<const uint16_t*>(g.B) + ti.boff;
-  const uint16_t* B2 = DUAL ? static_cast<const uint16_t*>(g.B2) + ti.boff : nullptr;
   const int ncol0 = blockIdx.x * (DUAL ? BN / 2 : BN);
+  const uint16_t* Bp = static_cast<const uint16_t*>(g.B) + ti.boff;
+  const uint16_t* B2p = DUAL ? static_cast<const uint16_t*>(g.B2) + ti.boff : nullptr;
+  const i32x4_t rsA = buffer_rsrc(g.A), rsB = buffer_rsrc(Bp);
+  const i32x4_t rsB2 = DUAL ? buffer_rsrc(B2p) : rsB;
 
-  const uint16_t* asrc[ACH];
-  const uint16_t* bsrc[BCH];
+  // per load j of this wave: source descriptor choice and byte offset at k = 0
+  uint32_t voff[NDMA];
+  int which[NDMA];   // 0: A, 1: B, 2: B2 (wave-uniform)
+  int arow[NDMA];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-    const int arow = ti.row0 + r;
-    asrc[i] = nullptr;
-    if (arow < ti.row1) asrc[i] = A + (long)(g.gather ? g.gather[arow] : arow) * g.lda + c * 8;
+  for (int j = 0; j < NDMA; ++j)
+    arow[j] = min(ti.row0 + (wid * NDMA + j) * 8 + (lane >> 3), ti.row1 - 1);
+  if (g.gather) {   // all gather loads issued together
+    int src[NDMA];
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) src[j] = g.gather[arow[j]];
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) arow[j] = src[j];
   }
 #pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-    int brow;
-    const uint16_t* bb = B;
-    if (DUAL) {
-      const int blk = r >> 5;
-      bb = (blk & 1) ? B2 : B;
-      brow = ncol0 + (blk >> 1) * 32 + (r & 31);
+  for (int j = 0; j < NDMA; ++j) {
+    const int I = wid * NDMA + j;            // stage rows 8I .. 8I+7
+    const int row = I * 8 + (lane >> 3), slot = lane & 7;
+    const int c = slot ^ ((row >> 1) & 7);   // logical chunk stored in this slot
+    if (I * 8 < BM) {
+      voff[j] = (uint32_t)(((long)arow[j] * g.lda + c * 8) * 2);
+      which[j] = 0;
     } else {
-      brow = ncol0 + r;
+      const int r = row - BM;
+      int brow;
+      if (DUAL) {
+        const int blk = r >> 5;
+        which[j] = (blk & 1) ? 2 : 1;
+        brow = ncol0 + (blk >> 1) * 32 + (r & 31);
+      } else {
+        which[j] = 1;
+        brow = ncol0 + r;
+      }
+      voff[j] = (uint32_t)(((long)min(brow, g.N - 1) * g.K + c * 8) * 2);
     }
-    bsrc[i] = (brow < g.N) ? bb + (long)brow * g.K + c * 8 : nullptr;
   }
-  uint4 ra[ACH], rb[BCH];
-  auto gload_into = [&](int k0, uint4 (&xa)[ACH], uint4 (&xb)[BCH]) {
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(&smem[0][0]);
+  auto issue = [&](int kt, int st) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      xa[i] = asrc[i] ? *reinterpret_cast<const uint4*>(asrc[i] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i)
-      xb[i] = bsrc[i] ? ldg_nt16(bsrc[i] + k0) : make_uint4(0, 0, 0, 0);
-  };
-  auto lstore_from = [&](int st, const uint4 (&xa)[ACH], const uint4 (&xb)[BCH]) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int q = tid + 256 * i;
-      As[st][swz(q >> 3, q & 7)] = xa[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int q = tid + 256 * i;
-      Bs[st][swz(q >> 3, q & 7)] = xb[i];
+    for (int j = 0; j < NDMA; ++j) {
+      const uint32_t dst = lds0 + (uint32_t)(st * ROWS * 128 + (wid * NDMA + j) * 1024);
+      const i32x4_t rs = which[j] == 0 ? rsA : (which[j] == 1 ? rsB : rsB2);
+      dma16(rs, __builtin_amdgcn_readfirstlane(dst), voff[j] + (uint32_t)(kt * BK * 2));
     }
   };
-  auto gload = [&](int k0) { gload_into(k0, ra, rb); };
-  auto lstore = [&](int st) { lstore_from(st, ra, rb); };
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -257,19 +340,17 @@ gemm_mfma_kernel(GemmArgs g) {
   const int nk = g.K / BK;
   const int lr = lane & 31, lg = lane >> 5;
   auto compute = [&](int st) {
+    const u32x4_t* As = &smem[st][0];
+    const u32x4_t* Bs = &smem[st][BM * 8];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
       bf16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const uint4 v = As[st][swz(wm * TM + i * 32 + lr, ks * 2 + lg)];
-        af[i] = *reinterpret_cast<const bf16x8*>(&v);
-      }
+      for (int i = 0; i < FM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, As[swz1(wm * TM + i * 32 + lr, ks * 2 + lg)]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint4 v = Bs[st][swz(wn * TN + j * 32 + lr, ks * 2 + lg)];
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&v);
-      }
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8, Bs[swz1(wn * TN + j * 32 + lr, ks * 2 + lg)]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -277,90 +358,67 @@ gemm_mfma_kernel(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   };
-#if DS4G_GEMM_PF2
-  // two register sets: tile t is loaded into set t&1 two iterations before
-  // it is computed, and stored to LDS at the end of the iteration before
-  uint4 ra2[ACH], rb2[BCH];
-  gload_into(0, ra, rb);
-  lstore_from(0, ra, rb);
-  if (nk > 1) gload_into(BK, ra2, rb2);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) gload_into((kt + 2) * BK, ra, rb);
-    compute(0);
-    if (kt + 1 < nk) lstore_from(1, ra2, rb2);
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) gload_into((kt + 3) * BK, ra2, rb2);
-    compute(1);
-    if (kt + 2 < nk) lstore_from(0, ra, rb);
-    __syncthreads();
-  }
-#else
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    compute(st);
-    if (kt + 1 < nk) lstore(st ^ 1);
-    __syncthreads();
-  }
-#endif
 
-  // epilogue
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int row = ti.row0 + wm * TM + i * 32 + 8 * jj + 4 * lg + ii;
-        if (row >= ti.row1) continue;
-        if (DUAL) {
-#pragma unroll
-          for (int j = 0; j < FN; j += 2) {
-            const int col = ncol0 + (wn * (TN / 2)) + (j >> 1) * 32 + lr;
-            if (col < g.N) epi_swiglu(g, row, col, acc[i][j][4 * jj + ii], acc[i][j + 1][4 * jj + ii]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int col = ncol0 + wn * TN + j * 32 + lr;
-            if (col < g.N) epi_store(g, row, col, acc[i][j][4 * jj + ii]);
-          }
-        }
-      }
-    }
+  for (int t = 0; t < S - 1; ++t)
+    if (t < nk) issue(t, t);
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt has landed once at most min(S-2, nk-1-kt) later tiles are pending
+    if (kt + S - 2 < nk) wait_vm<(S - 2) * NDMA>();
+    else wait_vm<0>();
+    barrier_lds();   // every wave: tile kt visible, and done reading the stage refilled next
+    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+    compute(kt % S);
   }
+
+  mfma_epilogue<EPI, FM, FN>(g, acc, ti.row0 + wm * TM, ti.row1,
+                             ncol0 + wn * (DUAL ? TN / 2 : TN), lane);
+}
+
+template <int BM, int BN, int WM, int WN, int S>
+int launch_dma_cfg(const GemmArgs& g, hipStream_t st) {
+  const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
+  const int bn_out = dual ? BN / 2 : BN;
+  const int mt = g.tiles ? g.max_tiles : (g.M + BM - 1) / BM;
+  const dim3 grid((g.N + bn_out - 1) / bn_out, mt), block(64 * WM * WN);
+  switch (g.epi) {
+    case EPI_F32:
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_F32>), grid, block, 0, st, g);
+      break;
+    case EPI_BF16:
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_BF16>), grid, block, 0, st, g);
+      break;
+    case EPI_RESID:
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_RESID>), grid, block, 0, st, g);
+      break;
+    case EPI_SWIGLU_BF16:
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_SWIGLU_BF16>), grid, block, 0, st,
+                         g);
+      break;
+    default: return -1;
+  }
+  return 0;
 }
 
 int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
   const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
   if (mfma) {
     if (g.K % 64) return -1;
-    // rows per tile: follow the rows a group (or the whole problem) has
-    int rows = g.M;
-    if (g.tiles) rows = g.rows_hint > 0 ? g.rows_hint : 128;
-#define DS4G_MF(BM_, BN_, WM_, WN_)                                                      \
-  {                                                                                      \
-    const int bn_out = dual ? BN_ / 2 : BN_;                                             \
-    const int mt = g.tiles ? g.max_tiles : (g.M + BM_ - 1) / BM_;                        \
-    dim3 grid((g.N + bn_out - 1) / bn_out, mt);                                          \
-    if (dual) hipLaunchKernelGGL((gemm_mfma_kernel<BM_, BN_, WM_, WN_, true>), grid, dim3(256), 0, st, g);  \
-    else hipLaunchKernelGGL((gemm_mfma_kernel<BM_, BN_, WM_, WN_, false>), grid, dim3(256), 0, st, g);      \
-    return 0;                                                                            \
-  }
+    // byte offsets of the direct loads are 32-bit
+    if ((double)g.N * g.K * 2 >= 4294967296.0) return -1;
     if (g.tiles) {   // the tile list was built for exactly rows_hint rows per tile
-      if (rows == 64) DS4G_MF(64, 256, 1, 4)
-      if (rows == 128) DS4G_MF(128, 128, 2, 2)
+      if (g.rows_hint == 64) return launch_dma_cfg<64, 256, 1, 4, 3>(g, st);
+      if (g.rows_hint == 128) return launch_dma_cfg<128, 256, 2, 4, 3>(g, st);
       return -1;
     }
-    // 256x128 tiles measured slower than 128x128 on every layer shape
-    if (rows <= 64) DS4G_MF(64, 256, 1, 4)
-    DS4G_MF(128, 128, 2, 2)
-#undef DS4G_MF
+    const long nout = dual ? g.N * 2L : g.N;           // B rows per output row
+    const long big_blocks = ((g.M + 255) / 256) * ((nout + 255) / 256);
+    if (big_blocks >= 512) return launch_dma_cfg<256, 256, 2, 4, 2>(g, st);
+    if (g.M <= 64) return launch_dma_cfg<64, 256, 1, 4, 3>(g, st);
+    const long blocks = ((g.M + 127) / 128) * ((nout + 127) / 128);
+    // one block per CU either way: spend the LDS on a deeper pipeline
+    if (blocks <= 256) return launch_dma_cfg<128, 128, 2, 2, 3>(g, st);
+    return launch_dma_cfg<128, 128, 2, 2, 2>(g, st);
   } else {
     const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
     if (g.K % (16 * nsplit)) return -1;

@@ -11,8 +11,7 @@ enum Epi {
   EPI_BF16 = 1,         // C[r, n] = bf16(acc)
   EPI_RESID = 2,        // C[r, n] += acc                     (fp32)
   EPI_SWIGLU_BF16 = 3,  // C[r, n] = bf16(silu(A.G^T) * (A.U^T))
-  EPI_SWIGLU_F32 = 4,   // same, fp32 out
-  EPI_COMBINE = 5       // C[t, n] += acc + sum_j w[t,j] part[pos_of[t*k+j], n]
+  EPI_SWIGLU_F32 = 4    // same, fp32 out
 };
 
 struct GemmArgs {
@@ -31,12 +30,6 @@ struct GemmArgs {
   int epi;
   void* C;
   int ldc;
-  // EPI_COMBINE
-  const float* part;
-  const int* pos_of;
-  const float* topk_w;
-  int topk;
-  int ldp;
   // SIMT split-K: blockIdx.z of ksplit writes its partial sum to C + z * part_stride
   int ksplit;
   long part_stride;
