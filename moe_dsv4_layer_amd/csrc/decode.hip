@@ -31,38 +31,49 @@
 namespace ds4g {
 
 // ---------------------------------------------------------------------------
-// Router selection: top-k of E logits (descending, ties to the lower index)
-// and the softmax probabilities of the chosen ones.  Run by one wave.
-__device__ void route_one(const float* logits, int E, int k, int* sel, float* wsel) {
+// Router selection: top-k of the E <= 512 logits (descending, ties to the
+// lower index) and the softmax probabilities of the chosen ones, by one wave
+// with the logits in registers (element lane + 64 i).  Each lane keeps its
+// best remaining element (first maximum in i order, so the lowest index among
+// its equal values); a round takes the wave max of those, then the lowest
+// index among the lanes that hold it, and only the winning lane rescans.
+// This runs before the first routed weight load, so it is kept short: a
+// rolled loop over the k rounds, two DPP reductions each.  Lane 0 writes the
+// choices to sel / wsel (this wave's own LDS slots).
+__device__ __forceinline__ void route_wave(const float (&lg)[8], int E, int k, int* sel,
+                                           float* wsel) {
   const int lane = threadIdx.x & 63;
   float v[8];
-  float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = (e < E) ? logits[e] : -INFINITY;
-    m = fmaxf(m, v[i]);
-  }
-  m = wave_max(m);
+  for (int i = 0; i < 8; ++i) v[i] = (lane + 64 * i < E) ? lg[i] : -INFINITY;
+  auto best = [&](float& bv, int& bi) {
+    bv = v[0];
+    bi = lane;
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+      if (v[i] > bv) { bv = v[i]; bi = lane + 64 * i; }
+  };
+  float bv;
+  int bi;
+  best(bv, bi);
+  const float m = wave_max(bv);
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (lane + 64 * i < E) s += expf(v[i] - m);
+  for (int i = 0; i < 8; ++i) s += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
   s = wave_sum(s);
+#pragma unroll 1
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    const float top = (r == 0) ? m : wave_max(bv);
+    const int idx = wave_min(bv == top ? bi : 0x7fffffff);
+    if (lane == 0) { sel[r] = idx; wsel[r] = expf(top - m) / s; }
+    if (lane == (idx & 63)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+      for (int i = 0; i < 8; ++i)
+        if (lane + 64 * i == idx) v[i] = -INFINITY;
+      best(bv, bi);
     }
-    wave_argmax(bv, bi);
-    if (lane == 0) { sel[r] = bi; wsel[r] = expf(bv - m) / s; }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (lane + 64 * i == bi) v[i] = -INFINITY;
   }
+  wave_lds_sync();
 }
 
 // ---------------------------------------------------------------------------
@@ -217,20 +228,35 @@ template int launch_gemv<float>(const GemvArgs&, hipStream_t);
 // MoE gate/up for one token: for each chosen expert slot s (k routed + the
 // shared expert) and inner row i:  z[s, i] = silu(G y) * (U y) with
 // y = RMSNorm(h2) * g2.  Blocks (4 waves splitting K = hidden) stride over
-// RB (gate, up) row pairs.  Task order puts the shared expert first: its
-// rows do not depend on the routing, so blocks that start there issue their
-// loads before the top-k is known.  Every block routes for itself (wave 0);
-// block 0 publishes the routing for the down kernel and the caller.
+// RB (gate, up) row pairs, shared-expert rows first.  Every wave routes for
+// itself from the logits in its registers (no block barrier before its
+// routed loads); block 0 publishes the routing for the down kernel and the
+// caller.
 template <typename WT, int CPL, int RB>
 __global__ void __launch_bounds__(256)
 moe_gateup_decode(MoeDecodeArgs a) {
-  __shared__ int sel[8];
-  __shared__ float wsel[8];
   __shared__ float ssq[4];
   __shared__ float red[4][RB][2];
+  __shared__ int wsel_idx[4][8];
+  __shared__ float wsel_w[4][8];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nchunk = a.d >> 3;
   const int ntask = a.k * a.I + a.Is;
+
+  // The reads every block needs (router logits, h2) go out first, ahead of
+  // any weight traffic: the routed rows cannot be loaded before they return.
+  float lg[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lg[i] = a.logits[min(lane + 64 * i, a.E - 1)];
+  float yv[CPL][8];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = (wid * CPL + i) * 64 + lane;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) yv[i][e] = (c < nchunk) ? a.h2[c * 8 + e] : 0.f;
+  }
+  const int* sel = wsel_idx[wid];     // this wave's routing (its own LDS slots)
+  const float* wsel = wsel_w[wid];
 
   Chunk8<WT> cg[RB][CPL], cu[RB][CPL];
   // task t < Is: shared row t; else routed slot s = (t - Is) / I, row i
@@ -259,26 +285,18 @@ moe_gateup_decode(MoeDecodeArgs a) {
   };
   int t0 = blockIdx.x * RB;
   const int stride = gridDim.x * RB;
-  const bool early = t0 + RB <= a.Is;   // first group is all shared rows
-  if (early) load_tasks(t0);
-  if (wid == 0) route_one(a.logits, a.E, a.k, sel, wsel);
+  route_wave(lg, a.E, a.k, wsel_idx[wid], wsel_w[wid]);   // every wave routes for itself
+  if (t0 < ntask) load_tasks(t0);
 
-  // y slice (wave w holds chunks [w*CPL*64, (w+1)*CPL*64))
-  float yv[CPL][8];
+  // y = RMSNorm(h2) * g2 (wave w holds chunks [w*CPL*64, (w+1)*CPL*64))
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = (wid * CPL + i) * 64 + lane;
+  for (int i = 0; i < CPL; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      yv[i][e] = (c < nchunk) ? a.h2[c * 8 + e] : 0.f;
-      ss += yv[i][e] * yv[i][e];
-    }
-  }
+    for (int e = 0; e < 8; ++e) ss += yv[i][e] * yv[i][e];
   ss = wave_sum(ss);
   if (lane == 0) ssq[wid] = ss;
   __syncthreads();
-  if (!early && t0 < ntask) load_tasks(t0);
   const float rs = rsqrtf((ssq[0] + ssq[1] + ssq[2] + ssq[3]) / (float)a.d + a.eps);
   const WT* g2 = static_cast<const WT*>(a.ffn_norm);
 #pragma unroll
@@ -292,22 +310,23 @@ moe_gateup_decode(MoeDecodeArgs a) {
 
   if (blockIdx.x == 0) {
     // publish the routing (one token: perm lists its k entries by expert)
-    if (threadIdx.x < a.k) {
-      const int j = threadIdx.x;
-      a.sel[j] = sel[j];
-      a.wsel[j] = wsel[j];
-      if (a.topk_idx) a.topk_idx[j] = sel[j];
-      if (a.topk_w) a.topk_w[j] = wsel[j];
+    if (wid == 0 && lane < a.k) {
+      const int sj = sel[lane];
+      const float wj = wsel[lane];
+      a.sel[lane] = sj;
+      a.wsel[lane] = wj;
+      if (a.topk_idx) a.topk_idx[lane] = sj;
+      if (a.topk_w) a.topk_w[lane] = wj;
       if (a.perm) {
         int r = 0;
-        for (int i = 0; i < a.k; ++i) r += sel[i] < sel[j];
-        a.perm[r] = j;
+        for (int q = 0; q < a.k; ++q) r += sel[q] < sj;
+        a.perm[r] = lane;
       }
     }
     if (a.count || a.offset) {
       for (int e = threadIdx.x; e <= a.E; e += blockDim.x) {
         int c = 0, o = 0;
-        for (int i = 0; i < a.k; ++i) { c += sel[i] == e; o += sel[i] < e; }
+        for (int q = 0; q < a.k; ++q) { c += sel[q] == e; o += sel[q] < e; }
         if (a.count && e < a.E) a.count[e] = c;
         if (a.offset) a.offset[e] = o;
       }

@@ -66,10 +66,22 @@ template <> struct Chunk8<float> {
 };
 
 // ----------------------------------------------------------- reductions
+// Wave-wide reductions on the DPP lane network (row_shr 1/2/4/8 inside each
+// 16-lane row, then row_bcast 15/31 across rows; the total ends in lane 63
+// and is read back as a wave-uniform value).  No LDS round trips: about a
+// third of the latency of the same butterfly through ds_bpermute, which is
+// what every GEMV row result and the router's top-k wait on.
+#define DS4G_DPP_F(old, v, ctrl, rm, bc)                                                   \
+  __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), ctrl, \
+                                             rm, 0xF, bc))
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += DS4G_DPP_F(0.f, v, 0x111, 0xF, true);    // row_shr:1, zero fill
+  v += DS4G_DPP_F(0.f, v, 0x112, 0xF, true);    // row_shr:2
+  v += DS4G_DPP_F(0.f, v, 0x114, 0xF, true);    // row_shr:4
+  v += DS4G_DPP_F(0.f, v, 0x118, 0xF, true);    // row_shr:8 -> lane 15 of each row
+  v += DS4G_DPP_F(0.f, v, 0x142, 0xA, false);   // row_bcast:15 into rows 1, 3
+  v += DS4G_DPP_F(0.f, v, 0x143, 0xC, false);   // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -77,18 +89,34 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, DS4G_DPP_F(-INFINITY, v, 0x111, 0xF, false));
+  v = fmaxf(v, DS4G_DPP_F(-INFINITY, v, 0x112, 0xF, false));
+  v = fmaxf(v, DS4G_DPP_F(-INFINITY, v, 0x114, 0xF, false));
+  v = fmaxf(v, DS4G_DPP_F(-INFINITY, v, 0x118, 0xF, false));
+  v = fmaxf(v, DS4G_DPP_F(-INFINITY, v, 0x142, 0xA, false));
+  v = fmaxf(v, DS4G_DPP_F(-INFINITY, v, 0x143, 0xC, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
-// (value, index) max with the lower index winning ties
+__device__ __forceinline__ int wave_min(int v) {
+#define DS4G_DPP_MIN(ctrl, rm) v = min(v, __builtin_amdgcn_update_dpp(0x7fffffff, v, ctrl, rm, 0xF, false))
+  DS4G_DPP_MIN(0x111, 0xF); DS4G_DPP_MIN(0x112, 0xF); DS4G_DPP_MIN(0x114, 0xF);
+  DS4G_DPP_MIN(0x118, 0xF); DS4G_DPP_MIN(0x142, 0xA); DS4G_DPP_MIN(0x143, 0xC);
+#undef DS4G_DPP_MIN
+  return __builtin_amdgcn_readlane(v, 63);
+}
+// (value, index) max with the lower index winning ties; every lane gets it
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o, kWave);
-    int oi = __shfl_xor(i, o, kWave);
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+#define DS4G_DPP_ARG(ctrl, rm)                                                   \
+  {                                                                              \
+    const float ov = DS4G_DPP_F(-INFINITY, v, ctrl, rm, false);                  \
+    const int oi = __builtin_amdgcn_update_dpp(0x7fffffff, i, ctrl, rm, 0xF, false); \
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }                       \
   }
+  DS4G_DPP_ARG(0x111, 0xF) DS4G_DPP_ARG(0x112, 0xF) DS4G_DPP_ARG(0x114, 0xF)
+  DS4G_DPP_ARG(0x118, 0xF) DS4G_DPP_ARG(0x142, 0xA) DS4G_DPP_ARG(0x143, 0xC)
+#undef DS4G_DPP_ARG
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
 // Block-wide sum (blockDim.x a multiple of 64, <= 1024); every thread gets it.
