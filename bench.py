@@ -37,6 +37,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+
+# HBM bytes of one decode step as read by the hardware counters (rocprofv3
+# --pmc FETCH_SIZE, then WRITE_SIZE, summed over the step's 7 kernels, mean of
+# 8 steps; FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0, the factors that make a
+# 1 GiB device copy read 1 GiB and write 1 GiB).  Valid only for the decode
+# sources it was measured on: any change to them reports traffic as null.
+DECODE_TRAFFIC_BYTES = 273839203
+DECODE_TRAFFIC_SOURCES = ("api.hip", "attn.hip", "decode.hip", "dev.h", "kernels.h")
+DECODE_TRAFFIC_SHA1 = "9919c55c83ea46f03f62cb418ffb3ce97bcb5e83"
+
+
+def decode_traffic():
+    import hashlib
+    h = hashlib.sha1()
+    for f in DECODE_TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "moe_dsv4_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return DECODE_TRAFFIC_BYTES if h.hexdigest() == DECODE_TRAFFIC_SHA1 else None
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
 
@@ -210,6 +228,9 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch decode eagerly")
     ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer workloads")
     ap.add_argument("--stack-decode-steps", type=int, default=256)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 1 GiB on the device 5 times (calibrates the HBM byte "
+                         "counters FETCH_SIZE / WRITE_SIZE against a known size) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -222,6 +243,16 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = 1 << 28                                    # 2^28 fp32 = 1 GiB
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                          "copies": 5}))
+        return 0
     wl = synth.WORKLOADS["layer_decode"]
     s = wl.layer
     cfg = ds4g.make_cfg(s)
@@ -368,7 +399,7 @@ def main() -> int:
                    "global_batch": 1, "seq_len": 1, "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": "ds4g_layer_decode (whole layer step)",
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
                      "algorithmic_bytes": dec_bytes},
         "prefill": {"workload": "same layer, layer-major prefill of 2048 tokens",
                     "tok_s": round(T_pre / (ms_prefill * 1e-3), 1),
