@@ -13,18 +13,26 @@ namespace {
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// The prefill router GEMM splits K = hidden into up to this many parts.
-constexpr int kRouterSplit = 8;
-inline int router_split(int hidden) {
+// The prefill router GEMM splits K into up to this many parts (partial sums
+// added in split order by the top-k kernel).  fp32 weights: K = hidden on the
+// vector ALUs; bf16 weights: K = 3 * hidden (the three-term bf16 split of y)
+// on the matrix cores.
+constexpr int kRouterSplit = 24;
+inline int router_split(int hidden, bool mfma) {
+  if (mfma) {
+    // 3 * (hidden / 1024) slices of equal length, each a multiple of 64
+    const int s = (hidden % 1024 == 0 && hidden / 1024 <= 8) ? 3 * (hidden / 1024) : 3;
+    return s;
+  }
   int s = hidden / 512;
   if (s < 1) s = 1;
-  if (s > kRouterSplit) s = kRouterSplit;
+  if (s > 8) s = 8;
   while (hidden % (16 * s)) --s;
   return s;
 }
 
 struct Layout {
-  size_t xn, c, qkv, q, kc, vc, o, yf, yb, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
+  size_t xn, c, qkv, q, kc, vc, o, yf, ys, wr3, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
       count, offset, tiles, ntiles, z, zs, part, total;
 };
 
@@ -45,7 +53,8 @@ Layout layout(const ds4g_layer_cfg& c, int T) {
   L.vc = take((size_t)T * dh * 2);
   L.o = take((size_t)T * qd * 4);
   L.yf = take((size_t)T * d * 4);
-  L.yb = take((size_t)T * d * 2);
+  L.ys = take((size_t)T * 3 * d * 2);
+  L.wr3 = take(E * 3 * d * 2);
   L.logits = take((size_t)T * E * 4);
   L.lpart = take((size_t)T * E * 4 * kRouterSplit);
   L.tidx = take((size_t)T * k * 4);
@@ -136,10 +145,10 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   // x_norm = RMSNorm(h) * g1
   if (bf)
     rc |= launch_rmsnorm_rows<uint16_t>(x, T, d, (const uint16_t*)w.attn_norm, c.rms_eps, nullptr,
-                                        at<uint16_t>(ws, L.xn), st);
+                                        at<uint16_t>(ws, L.xn), nullptr, st);
   else
     rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.attn_norm, c.rms_eps,
-                                     at<float>(ws, L.xn), nullptr, st);
+                                     at<float>(ws, L.xn), nullptr, nullptr, st);
 
   auto gemm = [&](const void* A, int lda, const void* B, int M, int N, int K, int epi, void* C,
                   int ldc) {
@@ -163,23 +172,31 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   // h2 = h + W_o o   (in place in x)
   gemm(at<void>(ws, L.o), qd, w.wo, T, d, qd, EPI_RESID, x, d);
 
-  // y = RMSNorm(h2) * g2 (fp32 for the router, bf16 for the expert GEMMs)
+  // y = RMSNorm(h2) * g2: fp32, and (bf16 weights) its three-term bf16 split,
+  // whose first term is bf16(y), the expert GEMMs' input
   if (bf)
     rc |= launch_rmsnorm_rows<uint16_t>(x, T, d, (const uint16_t*)w.ffn_norm, c.rms_eps,
-                                        at<float>(ws, L.yf), at<uint16_t>(ws, L.yb), st);
+                                        at<float>(ws, L.yf), nullptr, at<uint16_t>(ws, L.ys), st);
   else
     rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.ffn_norm, c.rms_eps,
-                                     at<float>(ws, L.yf), nullptr, st);
+                                     at<float>(ws, L.yf), nullptr, nullptr, st);
 
-  // router logits in fp32 (they decide integer expert choices): split-K
-  // partial sums, added in split order by the top-k kernel
-  const int rsplit = router_split(d);
+  // router logits at fp32 quality (they decide integer expert choices):
+  // bf16 weights: y1|y2|y3 against [W_r|W_r|W_r] on the matrix cores; fp32
+  // weights: fp32 y on the vector ALUs.  Split-K partial sums, added in split
+  // order by the top-k kernel.
+  const int rsplit = router_split(d, bf);
   {
     GemmArgs g{};
-    g.A = at<void>(ws, L.yf); g.lda = d; g.B = w.router; g.M = T; g.N = E; g.K = d;
-    g.epi = EPI_F32; g.C = at<void>(ws, L.lpart); g.ldc = E;
+    g.M = T; g.N = E; g.epi = EPI_F32; g.C = at<void>(ws, L.lpart); g.ldc = E;
     g.ksplit = rsplit; g.part_stride = (long)T * E;
-    rc |= launch_gemm(g, false, bf ? 1 : 0, st);
+    if (bf) {
+      rc |= launch_repeat3((const uint16_t*)w.router, E, d, at<uint16_t>(ws, L.wr3), st);
+      g.A = at<void>(ws, L.ys); g.lda = 3 * d; g.B = at<void>(ws, L.wr3); g.K = 3 * d;
+    } else {
+      g.A = at<void>(ws, L.yf); g.lda = d; g.B = w.router; g.K = d;
+    }
+    rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
   // tile height of the grouped expert GEMMs: follow the mean rows per expert
   const int mean_rows = (T * k + E - 1) / E;
@@ -197,11 +214,12 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   rc |= launch_route(ra, st);
   const int max_tiles = E + (T * k + tile_m - 1) / tile_m;
 
-  const void* yA = bf ? at<void>(ws, L.yb) : at<void>(ws, L.yf);
+  const void* yA = bf ? at<void>(ws, L.ys) : at<void>(ws, L.yf);
+  const int ylda = bf ? 3 * d : d;
   // routed gate/up + SwiGLU over the permuted rows
   {
     GemmArgs g{};
-    g.A = yA; g.lda = d; g.gather = ra.gather; g.B = w.gate; g.B2 = w.up;
+    g.A = yA; g.lda = ylda; g.gather = ra.gather; g.B = w.gate; g.B2 = w.up;
     g.b_stride = (long)I * d; g.N = I; g.K = d; g.tiles = ra.tiles; g.ntiles = ra.ntiles;
     g.row_off = ra.offset; g.max_tiles = max_tiles; g.rows_hint = tile_m;
     g.epi = bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32; g.C = at<void>(ws, L.z); g.ldc = I;
@@ -210,7 +228,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   // shared gate/up + SwiGLU over every token
   {
     GemmArgs g{};
-    g.A = yA; g.lda = d; g.B = w.sh_gate; g.B2 = w.sh_up; g.M = T; g.N = Is; g.K = d;
+    g.A = yA; g.lda = ylda; g.B = w.sh_gate; g.B2 = w.sh_up; g.M = T; g.N = Is; g.K = d;
     g.epi = bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32; g.C = at<void>(ws, L.zs); g.ldc = Is;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
@@ -335,7 +353,7 @@ int ds4g_layer_prefill(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
   if ((long)T * cfg->top_k >= (1 << 24) || T > (1 << 20)) return DS4G_ERR_UNSUPPORTED;
   if (cfg->wdtype == DS4G_BF16) {
     // the MFMA GEMMs address their bf16 operands with 32-bit byte offsets
-    const double widest = std::max({(double)cfg->hidden, (double)cfg->n_heads * cfg->head_dim,
+    const double widest = std::max({3.0 * cfg->hidden, (double)cfg->n_heads * cfg->head_dim,
                                     (double)cfg->qkv_rank, (double)cfg->shared_inter,
                                     (double)cfg->top_k * cfg->ffn_inter});
     if ((double)T * widest * 2.0 >= 4294967296.0) return DS4G_ERR_UNSUPPORTED;

@@ -320,12 +320,17 @@ gemm_dma_kernel(GemmArgs g) {
     }
   }
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(&smem[0][0]);
+  // split-K: slice z of ksplit covers k in [z*K/ksplit, (z+1)*K/ksplit) and
+  // writes its partial sums (EPI_F32 only) to C + z * part_stride
+  const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
+  const int kbase = (int)blockIdx.z * (g.K / nsplit);
+  const int nk = g.K / nsplit / BK;
   auto issue = [&](int kt, int st) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const uint32_t dst = lds0 + (uint32_t)(st * ROWS * 128 + (wid * NDMA + j) * 1024);
       const i32x4_t rs = which[j] == 0 ? rsA : (which[j] == 1 ? rsB : rsB2);
-      dma16(rs, __builtin_amdgcn_readfirstlane(dst), voff[j] + (uint32_t)(kt * BK * 2));
+      dma16(rs, __builtin_amdgcn_readfirstlane(dst), voff[j] + (uint32_t)((kbase + kt * BK) * 2));
     }
   };
 
@@ -337,7 +342,6 @@ gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = g.K / BK;
   const int lr = lane & 31, lg = lane >> 5;
   auto compute = [&](int st) {
     const u32x4_t* As = &smem[st][0];
@@ -371,7 +375,9 @@ gemm_dma_kernel(GemmArgs g) {
     compute(kt % S);
   }
 
-  mfma_epilogue<EPI, FM, FN>(g, acc, ti.row0 + wm * TM, ti.row1,
+  GemmArgs ge = g;
+  if (nsplit > 1) ge.C = static_cast<float*>(g.C) + (long)blockIdx.z * g.part_stride;
+  mfma_epilogue<EPI, FM, FN>(ge, acc, ti.row0 + wm * TM, ti.row1,
                              ncol0 + wn * (DUAL ? TN / 2 : TN), lane);
 }
 
@@ -380,7 +386,8 @@ int launch_dma_cfg(const GemmArgs& g, hipStream_t st) {
   const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
   const int bn_out = dual ? BN / 2 : BN;
   const int mt = g.tiles ? g.max_tiles : (g.M + BM - 1) / BM;
-  const dim3 grid((g.N + bn_out - 1) / bn_out, mt), block(64 * WM * WN);
+  const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
+  const dim3 grid((g.N + bn_out - 1) / bn_out, mt, nsplit), block(64 * WM * WN);
   switch (g.epi) {
     case EPI_F32:
       hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_F32>), grid, block, 0, st, g);
@@ -403,7 +410,9 @@ int launch_dma_cfg(const GemmArgs& g, hipStream_t st) {
 int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
   const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
   if (mfma) {
-    if (g.K % 64) return -1;
+    const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
+    if (g.K % (64 * nsplit)) return -1;
+    if (nsplit > 1 && (g.epi != EPI_F32 || g.tiles)) return -1;
     // byte offsets of the direct loads are 32-bit
     if ((double)g.N * g.K * 2 >= 4294967296.0) return -1;
     if (g.tiles) {   // the tile list was built for exactly rows_hint rows per tile
@@ -412,10 +421,10 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
       return -1;
     }
     const long nout = dual ? g.N * 2L : g.N;           // B rows per output row
-    const long big_blocks = ((g.M + 255) / 256) * ((nout + 255) / 256);
+    const long big_blocks = ((g.M + 255) / 256) * ((nout + 255) / 256) * nsplit;
     if (big_blocks >= 512) return launch_dma_cfg<256, 256, 2, 4, 2>(g, st);
     if (g.M <= 64) return launch_dma_cfg<64, 256, 1, 4, 3>(g, st);
-    const long blocks = ((g.M + 127) / 128) * ((nout + 127) / 128);
+    const long blocks = ((g.M + 127) / 128) * ((nout + 127) / 128) * nsplit;
     // one block per CU either way: spend the LDS on a deeper pipeline
     if (blocks <= 256) return launch_dma_cfg<128, 128, 2, 2, 3>(g, st);
     return launch_dma_cfg<128, 128, 2, 2, 2>(g, st);

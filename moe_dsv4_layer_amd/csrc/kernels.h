@@ -94,7 +94,8 @@ int launch_moe_decode(const MoeDecodeArgs& a, float* x, int64_t* pos_inc, hipStr
 // ---------------------------------------------------------------- prefill misc
 template <typename WT>
 int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps,
-                        float* out_f32, uint16_t* out_bf16, hipStream_t st);
+                        float* out_f32, uint16_t* out_bf16, uint16_t* out_split3, hipStream_t st);
+int launch_repeat3(const uint16_t* w, int E, int d, uint16_t* out, hipStream_t st);
 
 struct RouteArgs {
   const float* logits;  // nsplit partial sums [nsplit][T][E], added in order

@@ -13,10 +13,15 @@
 namespace ds4g {
 
 // ------------------------------------------------------------ RMSNorm rows
+// y = RMSNorm(x[t]) * gamma per row; outputs (each optional): fp32 of, bf16
+// ob, and os3 = the exact three-term bf16 split [y1 | y2 | y3] (row stride
+// 3d): y1 = bf16(y), y2 = bf16(y - y1), y3 = bf16(y - y1 - y2).  Products of
+// the terms with bf16 weights are exact in fp32 and y - y1 - y2 - y3 is below
+// 2^-27 |y|, so a bf16 MFMA GEMM over the split gives fp32-quality results.
 template <typename WT>
 __global__ void __launch_bounds__(256)
 rmsnorm_rows_kernel(const float* __restrict__ x, int d, const WT* __restrict__ gamma, float eps,
-                    float* __restrict__ of, uint16_t* __restrict__ ob) {
+                    float* __restrict__ of, uint16_t* __restrict__ ob, uint16_t* __restrict__ os3) {
   __shared__ float red[16];
   const long t = blockIdx.x;
   const float* row = x + t * d;
@@ -32,27 +37,59 @@ rmsnorm_rows_kernel(const float* __restrict__ x, int d, const WT* __restrict__ g
     float y[4] = {v.x * rs * ldw(gamma, i), v.y * rs * ldw(gamma, i + 1),
                   v.z * rs * ldw(gamma, i + 2), v.w * rs * ldw(gamma, i + 3)};
     if (of) *reinterpret_cast<float4*>(of + t * d + i) = make_float4(y[0], y[1], y[2], y[3]);
-    if (ob) {
+    uint16_t b1[4], b2[4], b3[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      b1[e] = f32_to_bf16(y[e]);
+      const float r1 = y[e] - bf16_to_f32(b1[e]);
+      b2[e] = f32_to_bf16(r1);
+      b3[e] = f32_to_bf16(r1 - bf16_to_f32(b2[e]));
+    }
+    auto pack = [](const uint16_t* b) {
       uint2 p;
-      p.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-      p.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
-      *reinterpret_cast<uint2*>(ob + t * d + i) = p;
+      p.x = (uint32_t)b[0] | ((uint32_t)b[1] << 16);
+      p.y = (uint32_t)b[2] | ((uint32_t)b[3] << 16);
+      return p;
+    };
+    if (ob) *reinterpret_cast<uint2*>(ob + t * d + i) = pack(b1);
+    if (os3) {
+      uint16_t* o = os3 + t * 3 * d + i;
+      *reinterpret_cast<uint2*>(o) = pack(b1);
+      *reinterpret_cast<uint2*>(o + d) = pack(b2);
+      *reinterpret_cast<uint2*>(o + 2 * d) = pack(b3);
     }
   }
 }
 
 template <typename WT>
 int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps, float* of,
-                        uint16_t* ob, hipStream_t st) {
+                        uint16_t* ob, uint16_t* os3, hipStream_t st) {
   if (d % 4) return -1;
   hipLaunchKernelGGL((rmsnorm_rows_kernel<WT>), dim3(T), dim3(256), 0, st, x, d, gamma, eps, of,
-                     ob);
+                     ob, os3);
   return 0;
 }
 template int launch_rmsnorm_rows<uint16_t>(const float*, int, int, const uint16_t*, float,
-                                           float*, uint16_t*, hipStream_t);
+                                           float*, uint16_t*, uint16_t*, hipStream_t);
 template int launch_rmsnorm_rows<float>(const float*, int, int, const float*, float, float*,
-                                        uint16_t*, hipStream_t);
+                                        uint16_t*, uint16_t*, hipStream_t);
+
+// [W | W | W]: each row of the [E, d] bf16 router weight repeated three times
+// ([E, 3d]), the B operand of the router GEMM over the three-term split of y.
+__global__ void __launch_bounds__(256)
+repeat3_kernel(const uint16_t* __restrict__ w, int d, uint16_t* __restrict__ out) {
+  const long e = blockIdx.x;
+  for (int i = threadIdx.x * 8; i < d; i += 256 * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(w + e * d + i);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) *reinterpret_cast<uint4*>(out + e * 3 * d + p * d + i) = v;
+  }
+}
+int launch_repeat3(const uint16_t* w, int E, int d, uint16_t* out, hipStream_t st) {
+  if (d % 8) return -1;
+  hipLaunchKernelGGL(repeat3_kernel, dim3(E), dim3(256), 0, st, w, d, out);
+  return 0;
+}
 
 // ------------------------------------------------------------ top-k per token
 // One wave per token: k rounds of a wave arg-max (lower index wins ties) over
