@@ -359,19 +359,26 @@ int launch_attention_decode(const AttnArgs& a, hipStream_t st) {
 // Prefill attention on the matrix cores (bf16 q, K, V; fp32 accumulate).
 //
 // A block takes the tokens of one 16-position-aligned span of absolute
-// positions [A, A + 16) and 16 heads.  MQA makes every head of a token look
-// at the same keys, so a 16-row MFMA tile is one token's 16 heads and its
+// positions [A, A + 16) and every head.  MQA makes every head of a token look
+// at the same keys, so a 16-row MFMA tile is 16 heads of one token and its
 // window mask is one key range: token tl (0..15) of the span sees block key
-// rows [tl, tl + W - 1] (block key row j is position A - W + 1 + j).
+// rows [tl, tl + W - 1] (block key row j is position A - W + 1 + j).  The
+// tile's arithmetic does not depend on how tokens and heads are spread over
+// blocks and waves.
 // Aligning spans to absolute positions (not to the batch start) gives every
 // token the same key-to-lane placement and reduction order whatever batch it
 // arrives in, so a prefill resumed from a ring snapshot reproduces the
-// uninterrupted prefill bit for bit.  The
-// block stages its <= 16 + W - 1 keys (bf16, XOR-swizzled rows) and the
-// values transposed (so 8 consecutive keys of one dim are 16 contiguous
-// bytes) in LDS.  Each wave handles 4 tokens one at a time:
+// uninterrupted prefill bit for bit.  The block stages its <= 16 + W - 1 keys
+// once for all heads (bf16, XOR-swizzled rows) and the values transposed (so
+// 8 consecutive keys of one dim are 16 contiguous bytes; consecutive lanes
+// write consecutive keys) in LDS.  For long batches a block covers every head
+// (waves split head groups of 16 and the span's tokens), so the keys are
+// staged once per span; for short
+// batches a block covers 16 heads and its waves split the tokens.  8 waves per
+// block, two per SIMD, so one wave's LDS reads overlap the other's MFMAs.
+// Either way one (token, 16 heads) tile is computed as:
 //   S = Q K^T      9 key tiles x dh/32 steps of v_mfma_f32_16x16x32_bf16
-//   mask, row max / sum across the 16 lanes that hold a row
+//   mask, row max / sum across the 16 lanes that hold a row (DPP)
 //   P (bf16)       through LDS into the A-operand layout
 //   O = P V        dh/16 output tiles x 5 key steps; O /= row sum
 // Keys before the batch come from the ring (slot pos % W); the batch's own
@@ -380,145 +387,156 @@ typedef __attribute__((__vector_size__(8 * sizeof(short)))) short attn_bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float attn_f32x4;
 
 template <int DH>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                   const uint16_t* __restrict__ vc, const uint16_t* __restrict__ ring_k,
                   const uint16_t* __restrict__ ring_v, const int64_t* __restrict__ pos, int T,
-                  int H, int W, uint16_t* __restrict__ o) {
+                  int H, int W, int split_heads, uint16_t* __restrict__ o) {
   constexpr int BQ = 16, NKT = 9, NKS = 5, NKP = 168;   // key tiles, PV key steps, padded row
   constexpr int CPR = DH / 8;                           // 16-B chunks per K row
   __shared__ __align__(16) uint16_t Ks[144 * DH];       // [key][dh], chunk-swizzled
   __shared__ __align__(16) uint16_t Vt[DH * NKP];       // [dh][key]
-  __shared__ __align__(16) uint16_t Ps[4][16 * NKP];    // per wave [head][key]
+  __shared__ __align__(16) uint16_t Ps[8][16 * NKP];    // per wave [head][key]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int h0 = blockIdx.y * 16;
   const long pos0 = *pos;
   const long P0 = (pos0 / BQ) * BQ + (long)blockIdx.x * BQ;   // span start A
   const long t0 = P0 - pos0;                            // batch row of span position 0 (may be < 0)
   if (t0 >= T) return;
   const long kbase = P0 - W + 1;                        // position of block key row 0
   const int nkeys = BQ + W - 1;                         // <= 143
-  // ---- stage K (swizzled) and V (transposed); rows outside the sequence are 0
-  for (int idx = tid; idx < 144 * CPR; idx += 256) {
-    const int j = idx / CPR, c = idx - j * CPR;
+  auto key_src = [&](int j, bool val) -> const uint16_t* {
     const long kp = kbase + j;
-    uint4 kk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (j < nkeys && kp >= 0 && kp < pos0 + T) {
-      const uint16_t *ksrc, *vsrc;
-      if (kp < pos0) {
-        const long slot = kp % W;
-        ksrc = ring_k + slot * DH;
-        vsrc = ring_v + slot * DH;
-      } else {
-        ksrc = kc + (kp - pos0) * DH;
-        vsrc = vc + (kp - pos0) * DH;
-      }
-      kk = *reinterpret_cast<const uint4*>(ksrc + c * 8);
-      vv = *reinterpret_cast<const uint4*>(vsrc + c * 8);
-    }
+    if (j >= nkeys || kp < 0 || kp >= pos0 + T) return nullptr;   // outside the sequence: 0
+    if (kp < pos0) return (val ? ring_v : ring_k) + (kp % W) * DH;
+    return (val ? vc : kc) + (kp - pos0) * DH;
+  };
+  // ---- stage K: lanes of a row write its chunks (swizzled, conflict-free)
+  for (int idx = tid; idx < 144 * CPR; idx += 512) {
+    const int j = idx / CPR, c = idx - j * CPR;
+    const uint16_t* src = key_src(j, false);
+    const uint4 kk = src ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(Ks + j * DH + ((c ^ (j & 7)) * 8)) = kk;
+  }
+  // ---- stage V transposed: consecutive lanes take consecutive keys of one
+  // 8-dim chunk, so each 2-byte store row is contiguous across the wave
+  for (int idx = tid; idx < NKP * CPR; idx += 512) {
+    const int c = idx / NKP, j = idx - c * NKP;
+    const uint16_t* src = j < 144 ? key_src(j, true) : nullptr;
+    const uint4 vv = src ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0, 0, 0, 0);
     const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) Vt[(c * 8 + e) * NKP + j] = ve[e];
-  }
-  for (int idx = tid; idx < DH * (NKP - 144); idx += 256) {
-    const int d = idx / (NKP - 144), j = 144 + idx % (NKP - 144);
-    Vt[d * NKP + j] = 0;
   }
   __syncthreads();
   const int lr = lane & 15, lg = lane >> 4;
   const float scale = rsqrtf((float)DH);
   uint16_t* P = Ps[wid];
-  for (int tt = 0; tt < 4; ++tt) {
-    const int tl = wid + 4 * tt;             // token of this wave's tile
-    const long tb = t0 + tl;                 // its batch row
-    if (tb >= T) break;
-    if (tb < 0) continue;                    // position before the batch
-    const int t = (int)tb;
-    const long pt = P0 + tl;
-    // ---- S = Q K^T for the token's 16 heads
+  // 8 waves.  split_heads: the block has every head group; wave w takes groups
+  // w%4, w%4 + 4, ... and tokens w/4, w/4 + 2, ...; otherwise the block has
+  // head group blockIdx.y and wave w takes tokens w, w + 8 (short batches:
+  // more blocks)
+  const int ngroups = (H + 15) / 16;
+  const int hg_lo = split_heads ? (wid & 3) : blockIdx.y, hg_step = split_heads ? 4 : ngroups;
+  const int tl_lo = split_heads ? (wid >> 2) : wid, tl_step = split_heads ? 2 : 8;
+  auto load_q = [&](int tl, int h0, attn_bf16x8 (&dst)[DH / 32]) {
+    const int t = (int)(t0 + tl), h = h0 + lr;
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (h < H) v = *reinterpret_cast<const uint4*>(q + ((long)t * H + h) * DH + ks * 32 + lg * 8);
+      dst[ks] = *reinterpret_cast<const attn_bf16x8*>(&v);
+    }
+  };
+  for (int hg = hg_lo; hg < ngroups; hg += hg_step) {
+    const int h0 = hg * 16;
+    int tl = tl_lo;
+    while (tl < BQ && t0 + tl < 0) tl += tl_step;   // positions before the batch
+    if (tl >= BQ || t0 + tl >= T) continue;
     attn_bf16x8 qa[DH / 32];
-    {
-      const int h = h0 + lr;
+    load_q(tl, h0, qa);
+    for (;;) {
+      // the next token's q goes out before this token's math
+      const int tn = tl + tl_step;
+      const bool more = tn < BQ && t0 + tn < T;
+      attn_bf16x8 qn[DH / 32];
+      if (more) load_q(tn, h0, qn);
+      const int t = (int)(t0 + tl);
+      const long pt = P0 + tl;
+      // ---- S = Q K^T for the token's 16 heads
+      attn_f32x4 sacc[NKT];
 #pragma unroll
-      for (int ks = 0; ks < DH / 32; ++ks) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (h < H) v = *reinterpret_cast<const uint4*>(q + ((long)t * H + h) * DH + ks * 32 + lg * 8);
-        qa[ks] = *reinterpret_cast<const attn_bf16x8*>(&v);
+      for (int kt = 0; kt < NKT; ++kt) {
+        sacc[kt] = attn_f32x4{0.f, 0.f, 0.f, 0.f};
+        const int j = kt * 16 + lr;
+#pragma unroll
+        for (int ks = 0; ks < DH / 32; ++ks) {
+          const int c = ks * 4 + lg;
+          const uint4 v = *reinterpret_cast<const uint4*>(Ks + j * DH + ((c ^ (j & 7)) * 8));
+          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              qa[ks], *reinterpret_cast<const attn_bf16x8*>(&v), sacc[kt], 0, 0, 0);
+        }
       }
-    }
-    attn_f32x4 sacc[NKT];
+      // ---- mask + softmax; lane holds key kt*16+lr of heads 4*lg+r
+      float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      sacc[kt] = attn_f32x4{0.f, 0.f, 0.f, 0.f};
-      const int j = kt * 16 + lr;
+      for (int kt = 0; kt < NKT; ++kt) {
+        const int j = kt * 16 + lr;
+        const long kp = kbase + j;
+        const bool ok = j >= tl && j <= tl + W - 1 && kp >= 0 && kp <= pt;
 #pragma unroll
-      for (int ks = 0; ks < DH / 32; ++ks) {
-        const int c = ks * 4 + lg;
-        const uint4 v = *reinterpret_cast<const uint4*>(Ks + j * DH + ((c ^ (j & 7)) * 8));
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            qa[ks], *reinterpret_cast<const attn_bf16x8*>(&v), sacc[kt], 0, 0, 0);
+        for (int r = 0; r < 4; ++r) {
+          const float v = ok ? sacc[kt][r] * scale : -INFINITY;
+          sacc[kt][r] = v;
+          mx[r] = fmaxf(mx[r], v);
+        }
       }
-    }
-    // ---- mask + softmax; lane holds key kt*16+lr of heads 4*lg+r
-    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      const int j = kt * 16 + lr;
-      const long kp = kbase + j;
-      const bool ok = j >= tl && j <= tl + W - 1 && kp >= 0 && kp <= pt;
+      for (int r = 0; r < 4; ++r) mx[r] = row16_max(mx[r]);
+      float sm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = expf(sacc[kt][r] - mx[r]);     // exp(-inf) = 0 for masked keys
+          sm[r] += e;
+          P[(4 * lg + r) * NKP + kt * 16 + lr] = f32_to_bf16(e);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = ok ? sacc[kt][r] * scale : -INFINITY;
-        sacc[kt][r] = v;
-        mx[r] = fmaxf(mx[r], v);
+        P[(4 * lg + r) * NKP + 144 + lr] = 0;         // keys 144..159: padding
+        sm[r] = row16_sum(sm[r]);
       }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], off, 64));
-    float sm[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = expf(sacc[kt][r] - mx[r]);     // exp(-inf) = 0 for masked keys
-        sm[r] += e;
-        P[(4 * lg + r) * NKP + kt * 16 + lr] = f32_to_bf16(e);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      P[(4 * lg + r) * NKP + 144 + lr] = 0;         // keys 144..159: padding
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) sm[r] += __shfl_xor(sm[r], off, 64);
-    }
-    wave_lds_sync();
-    // ---- O = P V
-    attn_bf16x8 pa[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(P + lr * NKP + ks * 32 + lg * 8);
-      pa[ks] = *reinterpret_cast<const attn_bf16x8*>(&v);
-    }
-#pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt) {
-      attn_f32x4 oacc = attn_f32x4{0.f, 0.f, 0.f, 0.f};
-      const int d = dt * 16 + lr;
+      wave_lds_sync();
+      // ---- O = P V
+      attn_bf16x8 pa[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 v = *reinterpret_cast<const uint4*>(Vt + d * NKP + ks * 32 + lg * 8);
-        oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            pa[ks], *reinterpret_cast<const attn_bf16x8*>(&v), oacc, 0, 0, 0);
+        const uint4 v = *reinterpret_cast<const uint4*>(P + lr * NKP + ks * 32 + lg * 8);
+        pa[ks] = *reinterpret_cast<const attn_bf16x8*>(&v);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = h0 + 4 * lg + r;
-        if (h < H) o[((long)t * H + h) * DH + d] = f32_to_bf16(oacc[r] / sm[r]);
+      for (int dt = 0; dt < DH / 16; ++dt) {
+        attn_f32x4 oacc = attn_f32x4{0.f, 0.f, 0.f, 0.f};
+        const int d = dt * 16 + lr;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const uint4 v = *reinterpret_cast<const uint4*>(Vt + d * NKP + ks * 32 + lg * 8);
+          oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              pa[ks], *reinterpret_cast<const attn_bf16x8*>(&v), oacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = h0 + 4 * lg + r;
+          if (h < H) o[((long)t * H + h) * DH + d] = f32_to_bf16(oacc[r] / sm[r]);
+        }
       }
+      wave_lds_sync();
+      if (!more) break;
+#pragma unroll
+      for (int ks = 0; ks < DH / 32; ++ks) qa[ks] = qn[ks];
+      tl = tn;
     }
-    wave_lds_sync();
   }
 }
 
@@ -528,13 +546,18 @@ int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st) {
                      a.dh, a.rd, a.base, a.pos, (uint16_t*)a.q, a.kc, a.vc);
   // spans are aligned to absolute positions: one extra span covers the
   // unknown (device-side) offset of the first position within its span
-  const dim3 grid((a.T + 15) / 16 + 1, (a.H + 15) / 16);
+  // every head per block once there are spans enough to fill the chip
+  const int nspans = (a.T + 15) / 16 + 1;
+  const int split_heads = nspans >= 512 ? 1 : 0;
+  const dim3 grid(nspans, split_heads ? 1 : (a.H + 15) / 16);
   if (a.dh == 128)
-    hipLaunchKernelGGL((attn_prefill_mfma<128>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
-                       a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
+    hipLaunchKernelGGL((attn_prefill_mfma<128>), grid, dim3(512), 0, st, (const uint16_t*)a.q,
+                       a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, split_heads,
+                       (uint16_t*)a.o);
   else if (a.dh == 64)
-    hipLaunchKernelGGL((attn_prefill_mfma<64>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
-                       a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
+    hipLaunchKernelGGL((attn_prefill_mfma<64>), grid, dim3(512), 0, st, (const uint16_t*)a.q,
+                       a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, split_heads,
+                       (uint16_t*)a.o);
   else
     return -1;
   ring_commit(a, st);

@@ -119,6 +119,24 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   i = __builtin_amdgcn_readlane(i, 63);
 }
 
+// All-reduce inside each 16-lane row (every lane of the row gets the row's
+// result): quad_perm swaps for lane distance 1 and 2, then row rotations by
+// 4 and 8.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, DS4G_DPP_F(v, v, 0xB1, 0xF, false));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, DS4G_DPP_F(v, v, 0x4E, 0xF, false));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, DS4G_DPP_F(v, v, 0x124, 0xF, false));   // row_ror:4
+  v = fmaxf(v, DS4G_DPP_F(v, v, 0x128, 0xF, false));   // row_ror:8
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += DS4G_DPP_F(v, v, 0xB1, 0xF, false);
+  v += DS4G_DPP_F(v, v, 0x4E, 0xF, false);
+  v += DS4G_DPP_F(v, v, 0x124, 0xF, false);
+  v += DS4G_DPP_F(v, v, 0x128, 0xF, false);
+  return v;
+}
+
 // Block-wide sum (blockDim.x a multiple of 64, <= 1024); every thread gets it.
 __device__ __forceinline__ float block_sum(float v, float* red /*[16]*/) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
