@@ -359,183 +359,176 @@ int launch_attention_decode(const AttnArgs& a, hipStream_t st) {
 // Prefill attention on the matrix cores (bf16 q, K, V; fp32 accumulate).
 //
 // A block takes the tokens of one 16-position-aligned span of absolute
-// positions [A, A + 16) and every head.  MQA makes every head of a token look
-// at the same keys, so a 16-row MFMA tile is 16 heads of one token and its
-// window mask is one key range: token tl (0..15) of the span sees block key
-// rows [tl, tl + W - 1] (block key row j is position A - W + 1 + j).  The
-// tile's arithmetic does not depend on how tokens and heads are spread over
-// blocks and waves.
+// positions [A, A + 16) and 32 heads.  Block key row j is position
+// A - W + 1 + j, so token tl (0..15) of the span sees rows [tl, tl + W - 1].
+// The block stages its key rows once (bf16, XOR-swizzled rows) and the values
+// transposed (8 consecutive keys of one dim are 16 contiguous bytes) in LDS.
 // Aligning spans to absolute positions (not to the batch start) gives every
 // token the same key-to-lane placement and reduction order whatever batch it
 // arrives in, so a prefill resumed from a ring snapshot reproduces the
-// uninterrupted prefill bit for bit.  The block stages its <= 16 + W - 1 keys
-// once for all heads (bf16, XOR-swizzled rows) and the values transposed (so
-// 8 consecutive keys of one dim are 16 contiguous bytes; consecutive lanes
-// write consecutive keys) in LDS.  For long batches a block covers every head
-// (waves split head groups of 16 and the span's tokens), so the keys are
-// staged once per span; for short
-// batches a block covers 16 heads and its waves split the tokens.  8 waves per
-// block, two per SIMD, so one wave's LDS reads overlap the other's MFMAs.
-// Either way one (token, 16 heads) tile is computed as:
-//   S = Q K^T      9 key tiles x dh/32 steps of v_mfma_f32_16x16x32_bf16
-//   mask, row max / sum across the 16 lanes that hold a row (DPP)
-//   P (bf16)       through LDS into the A-operand layout
-//   O = P V        dh/16 output tiles x 5 key steps; O /= row sum
+// uninterrupted prefill bit for bit.
+//
+// The unit of work is a 32-column tile: two consecutive tokens x 16 heads
+// (MQA: every head of a token sees the same keys).  It is computed
+// transposed, keys on the rows, so that the scores never leave registers:
+//   S^T = K Q^T   5 key tiles of 32 rows starting at the pair's window start
+//                 rounded down to 8, x dh/16 steps of v_mfma_f32_32x32x16_bf16
+//   mask, column max / sum: within the lane, then with lane ^ 32
+//   O^T = V^T P^T dh/32 output tiles x 10 key steps; the B operand P^T is
+//                 the S^T accumulator rounded to bf16 in place
+// The accumulator of a 32x32 MFMA gives lane l the column l % 32 and rows
+// 8g + 4(l / 32) + i (g, i < 4); the B operand wants 8 consecutive keys
+// 8(l / 32) .. + 7 of a 16-key step.  Feeding K row pi(r) to A-operand row r,
+// pi(8g + 4h + i) = 16(g / 2) + 8h + 4(g % 2) + i, makes the accumulator rows
+// of g = 2s, 2s + 1 exactly the keys of step s, so P^T needs no shuffle.
 // Keys before the batch come from the ring (slot pos % W); the batch's own
 // keys from kc/vc (already rotated and rounded to bf16).
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short attn_bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float attn_f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float attn_f32x16;
+
+// K rows are 16-B chunk-swizzled so that the 8 rows {x..x+3, x+8..x+11}
+// (x % 4 == 0) that 8 consecutive lanes read hit 8 different bank groups
+__device__ __forceinline__ int attn_kswz(int j) { return (j & 3) | (((j >> 3) & 1) << 2); }
 
 template <int DH>
 __global__ void __launch_bounds__(512)
 attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                   const uint16_t* __restrict__ vc, const uint16_t* __restrict__ ring_k,
                   const uint16_t* __restrict__ ring_v, const int64_t* __restrict__ pos, int T,
-                  int H, int W, int split_heads, uint16_t* __restrict__ o) {
-  constexpr int BQ = 16, NKT = 9, NKS = 5, NKP = 168;   // key tiles, PV key steps, padded row
-  constexpr int CPR = DH / 8;                           // 16-B chunks per K row
-  __shared__ __align__(16) uint16_t Ks[144 * DH];       // [key][dh], chunk-swizzled
-  __shared__ __align__(16) uint16_t Vt[DH * NKP];       // [dh][key]
-  __shared__ __align__(16) uint16_t Ps[8][16 * NKP];    // per wave [head][key]
+                  int H, int W, uint16_t* __restrict__ o) {
+  constexpr int BQ = 16;
+  constexpr int NKR = 168;        // staged key rows: window start (<= 8) + 5 x 32
+  constexpr int CPR = DH / 8;     // 16-B chunks per row
+  constexpr int KSTEP = DH / 16;  // S^T contraction steps
+  constexpr int DTILE = DH / 32;  // O^T row tiles
+  __shared__ __align__(16) uint16_t Ks[NKR * DH];   // [key][dh], chunk-swizzled
+  __shared__ __align__(16) uint16_t Vt[DH * NKR];   // [dh][key]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const long pos0 = *pos;
   const long P0 = (pos0 / BQ) * BQ + (long)blockIdx.x * BQ;   // span start A
-  const long t0 = P0 - pos0;                            // batch row of span position 0 (may be < 0)
+  const long t0 = P0 - pos0;              // batch row of span position 0 (may be < 0)
   if (t0 >= T) return;
-  const long kbase = P0 - W + 1;                        // position of block key row 0
-  const int nkeys = BQ + W - 1;                         // <= 143
+  const long kbase = P0 - W + 1;          // position of block key row 0
+  const int nkeys = BQ + W - 1;           // <= 143
   auto key_src = [&](int j, bool val) -> const uint16_t* {
     const long kp = kbase + j;
     if (j >= nkeys || kp < 0 || kp >= pos0 + T) return nullptr;   // outside the sequence: 0
     if (kp < pos0) return (val ? ring_v : ring_k) + (kp % W) * DH;
     return (val ? vc : kc) + (kp - pos0) * DH;
   };
-  // ---- stage K: lanes of a row write its chunks (swizzled, conflict-free)
-  for (int idx = tid; idx < 144 * CPR; idx += 512) {
+  for (int idx = tid; idx < NKR * CPR; idx += 512) {
     const int j = idx / CPR, c = idx - j * CPR;
     const uint16_t* src = key_src(j, false);
     const uint4 kk = src ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(Ks + j * DH + ((c ^ (j & 7)) * 8)) = kk;
+    *reinterpret_cast<uint4*>(Ks + j * DH + ((c ^ attn_kswz(j)) * 8)) = kk;
   }
-  // ---- stage V transposed: consecutive lanes take consecutive keys of one
-  // 8-dim chunk, so each 2-byte store row is contiguous across the wave
-  for (int idx = tid; idx < NKP * CPR; idx += 512) {
-    const int c = idx / NKP, j = idx - c * NKP;
-    const uint16_t* src = j < 144 ? key_src(j, true) : nullptr;
+  // consecutive lanes take consecutive keys of one 8-dim chunk, so each 2-byte
+  // store row is contiguous across the wave
+  for (int idx = tid; idx < NKR * CPR; idx += 512) {
+    const int c = idx / NKR, j = idx - c * NKR;
+    const uint16_t* src = key_src(j, true);
     const uint4 vv = src ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0, 0, 0, 0);
     const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) Vt[(c * 8 + e) * NKP + j] = ve[e];
+    for (int e = 0; e < 8; ++e) Vt[(c * 8 + e) * NKR + j] = ve[e];
   }
   __syncthreads();
-  const int lr = lane & 15, lg = lane >> 4;
-  const float scale = rsqrtf((float)DH);
-  uint16_t* P = Ps[wid];
-  // 8 waves.  split_heads: the block has every head group; wave w takes groups
-  // w%4, w%4 + 4, ... and tokens w/4, w/4 + 2, ...; otherwise the block has
-  // head group blockIdx.y and wave w takes tokens w, w + 8 (short batches:
-  // more blocks)
-  const int ngroups = (H + 15) / 16;
-  const int hg_lo = split_heads ? (wid & 3) : blockIdx.y, hg_step = split_heads ? 4 : ngroups;
-  const int tl_lo = split_heads ? (wid >> 2) : wid, tl_step = split_heads ? 2 : 8;
-  auto load_q = [&](int tl, int h0, attn_bf16x8 (&dst)[DH / 32]) {
-    const int t = (int)(t0 + tl), h = h0 + lr;
+  const int lr = lane & 31, hf = lane >> 5;
+  // exp(x * scale) = exp2(x * scale * log2(e))
+  const float sl2 = rsqrtf((float)DH) * 1.4426950408889634f;
+  const int pr = 16 * ((lr >> 3) >> 1) + 8 * ((lr >> 2) & 1) + 4 * ((lr >> 3) & 1) + (lr & 3);
+  // wave w: head group 2 * blockIdx.y + w % 2, token pairs w / 2 and w / 2 + 4
+  const int head = (2 * blockIdx.y + (wid & 1)) * 16 + (lr & 15);
+  if ((2 * blockIdx.y + (wid & 1)) * 16 >= H) return;
+  for (int p = wid >> 1; p < BQ / 2; p += 4) {
+    const int tl = 2 * p;
+    if (t0 + tl + 1 < 0 || t0 + tl >= T) continue;   // both tokens outside the batch
+    const int tc = tl + ((lr >> 4) & 1);             // this lane's column token
+    const long t = t0 + tc;
+    const bool col_ok = t >= 0 && t < T && head < H;
+    const int j0 = tl & ~7;
+    attn_bf16x8 qf[KSTEP];
 #pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks) {
+    for (int ks = 0; ks < KSTEP; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (h < H) v = *reinterpret_cast<const uint4*>(q + ((long)t * H + h) * DH + ks * 32 + lg * 8);
-      dst[ks] = *reinterpret_cast<const attn_bf16x8*>(&v);
+      if (col_ok) v = *reinterpret_cast<const uint4*>(q + (t * H + head) * DH + ks * 16 + hf * 8);
+      qf[ks] = *reinterpret_cast<const attn_bf16x8*>(&v);
     }
-  };
-  for (int hg = hg_lo; hg < ngroups; hg += hg_step) {
-    const int h0 = hg * 16;
-    int tl = tl_lo;
-    while (tl < BQ && t0 + tl < 0) tl += tl_step;   // positions before the batch
-    if (tl >= BQ || t0 + tl >= T) continue;
-    attn_bf16x8 qa[DH / 32];
-    load_q(tl, h0, qa);
-    for (;;) {
-      // the next token's q goes out before this token's math
-      const int tn = tl + tl_step;
-      const bool more = tn < BQ && t0 + tn < T;
-      attn_bf16x8 qn[DH / 32];
-      if (more) load_q(tn, h0, qn);
-      const int t = (int)(t0 + tl);
-      const long pt = P0 + tl;
-      // ---- S = Q K^T for the token's 16 heads
-      attn_f32x4 sacc[NKT];
+    // ---- S^T = K Q^T
+    attn_f32x16 sacc[5];
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        sacc[kt] = attn_f32x4{0.f, 0.f, 0.f, 0.f};
-        const int j = kt * 16 + lr;
+    for (int m = 0; m < 5; ++m) {
+      sacc[m] = attn_f32x16{};
+      const int j = j0 + 32 * m + pr;
+      const uint16_t* krow = Ks + j * DH;
+      const int sw = attn_kswz(j);
 #pragma unroll
-        for (int ks = 0; ks < DH / 32; ++ks) {
-          const int c = ks * 4 + lg;
-          const uint4 v = *reinterpret_cast<const uint4*>(Ks + j * DH + ((c ^ (j & 7)) * 8));
-          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              qa[ks], *reinterpret_cast<const attn_bf16x8*>(&v), sacc[kt], 0, 0, 0);
+      for (int ks = 0; ks < KSTEP; ++ks) {
+        const uint4 v = *reinterpret_cast<const uint4*>(krow + (((2 * ks + hf) ^ sw) * 8));
+        sacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const attn_bf16x8*>(&v), qf[ks], sacc[m], 0, 0, 0);
+      }
+    }
+    // ---- mask to the window [tc, tc + W - 1] and the sequence start, then
+    // column max; accumulator (m, g, i) is key j0 + 32m + 16(g/2) + 8hf + 4(g%2) + i
+    const int lo = max(tc, (int)max(-kbase, 0L)), hi = tc + W - 1;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + 32 * m + 16 * (g >> 1) + 8 * hf + 4 * (g & 1) + i;
+          const float v = (j >= lo && j <= hi) ? sacc[m][4 * g + i] : -INFINITY;
+          sacc[m][4 * g + i] = v;
+          mx = fmaxf(mx, v);
         }
-      }
-      // ---- mask + softmax; lane holds key kt*16+lr of heads 4*lg+r
-      float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mo = -mx * sl2;
+    float sm = 0.f;
+    attn_bf16x8 pf[5][2];
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        const int j = kt * 16 + lr;
-        const long kp = kbase + j;
-        const bool ok = j >= tl && j <= tl + W - 1 && kp >= 0 && kp <= pt;
+    for (int m = 0; m < 5; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = ok ? sacc[kt][r] * scale : -INFINITY;
-          sacc[kt][r] = v;
-          mx[r] = fmaxf(mx[r], v);
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[m][4 * g + i], sl2, mo));   // masked: 0
+          sm += e;
+          pf[m][g >> 1][4 * (g & 1) + i] = (short)f32_to_bf16(e);
         }
-      }
+    sm += __shfl_xor(sm, 32, kWave);
+    // ---- O^T = V^T P^T
+    attn_f32x16 oacc[DTILE];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx[r] = row16_max(mx[r]);
-      float sm[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DTILE; ++dt) {
+      oacc[dt] = attn_f32x16{};
+      const uint16_t* vrow = Vt + (dt * 32 + lr) * NKR + j0 + 8 * hf;
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
+      for (int m = 0; m < 5; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = expf(sacc[kt][r] - mx[r]);     // exp(-inf) = 0 for masked keys
-          sm[r] += e;
-          P[(4 * lg + r) * NKP + kt * 16 + lr] = f32_to_bf16(e);
+        for (int s = 0; s < 2; ++s) {
+          const uint4 v = *reinterpret_cast<const uint4*>(vrow + 32 * m + 16 * s);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *reinterpret_cast<const attn_bf16x8*>(&v), pf[m][s], oacc[dt], 0, 0, 0);
         }
-      }
+    }
+    // lane holds dims dt*32 + 8g + 4hf + (0..3) of its column
+    if (col_ok) {
+      const float inv = 1.f / sm;
+      uint16_t* orow = o + (t * H + head) * DH + 4 * hf;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        P[(4 * lg + r) * NKP + 144 + lr] = 0;         // keys 144..159: padding
-        sm[r] = row16_sum(sm[r]);
-      }
-      wave_lds_sync();
-      // ---- O = P V
-      attn_bf16x8 pa[NKS];
+      for (int dt = 0; dt < DTILE; ++dt)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const uint4 v = *reinterpret_cast<const uint4*>(P + lr * NKP + ks * 32 + lg * 8);
-        pa[ks] = *reinterpret_cast<const attn_bf16x8*>(&v);
-      }
-#pragma unroll
-      for (int dt = 0; dt < DH / 16; ++dt) {
-        attn_f32x4 oacc = attn_f32x4{0.f, 0.f, 0.f, 0.f};
-        const int d = dt * 16 + lr;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const uint4 v = *reinterpret_cast<const uint4*>(Vt + d * NKP + ks * 32 + lg * 8);
-          oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              pa[ks], *reinterpret_cast<const attn_bf16x8*>(&v), oacc, 0, 0, 0);
+        for (int g = 0; g < 4; ++g) {
+          uint2 w;
+          w.x = (uint32_t)f32_to_bf16(oacc[dt][4 * g] * inv) |
+                ((uint32_t)f32_to_bf16(oacc[dt][4 * g + 1] * inv) << 16);
+          w.y = (uint32_t)f32_to_bf16(oacc[dt][4 * g + 2] * inv) |
+                ((uint32_t)f32_to_bf16(oacc[dt][4 * g + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g) = w;
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = h0 + 4 * lg + r;
-          if (h < H) o[((long)t * H + h) * DH + d] = f32_to_bf16(oacc[r] / sm[r]);
-        }
-      }
-      wave_lds_sync();
-      if (!more) break;
-#pragma unroll
-      for (int ks = 0; ks < DH / 32; ++ks) qa[ks] = qn[ks];
-      tl = tn;
     }
   }
 }
@@ -546,18 +539,13 @@ int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st) {
                      a.dh, a.rd, a.base, a.pos, (uint16_t*)a.q, a.kc, a.vc);
   // spans are aligned to absolute positions: one extra span covers the
   // unknown (device-side) offset of the first position within its span
-  // every head per block once there are spans enough to fill the chip
-  const int nspans = (a.T + 15) / 16 + 1;
-  const int split_heads = nspans >= 512 ? 1 : 0;
-  const dim3 grid(nspans, split_heads ? 1 : (a.H + 15) / 16);
+  const dim3 grid((a.T + 15) / 16 + 1, (a.H + 31) / 32);
   if (a.dh == 128)
     hipLaunchKernelGGL((attn_prefill_mfma<128>), grid, dim3(512), 0, st, (const uint16_t*)a.q,
-                       a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, split_heads,
-                       (uint16_t*)a.o);
+                       a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
   else if (a.dh == 64)
     hipLaunchKernelGGL((attn_prefill_mfma<64>), grid, dim3(512), 0, st, (const uint16_t*)a.q,
-                       a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, split_heads,
-                       (uint16_t*)a.o);
+                       a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
   else
     return -1;
   ring_commit(a, st);
