@@ -200,7 +200,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   }
   // tile height of the grouped expert GEMMs: follow the mean rows per expert
   const int mean_rows = (T * k + E - 1) / E;
-  const int tile_m = (!bf || mean_rows <= 64) ? 64 : 128;
+  const int tile_m = (!bf || mean_rows <= 64) ? 64 : mean_rows < 160 ? 128 : 256;
   RouteArgs ra{};
   ra.logits = at<float>(ws, L.lpart); ra.nsplit = rsplit;
   ra.logits_sum = at<float>(ws, L.logits); ra.T = T; ra.E = E; ra.k = k;
@@ -223,6 +223,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.b_stride = (long)I * d; g.N = I; g.K = d; g.tiles = ra.tiles; g.ntiles = ra.ntiles;
     g.row_off = ra.offset; g.max_tiles = max_tiles; g.rows_hint = tile_m;
     g.epi = bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32; g.C = at<void>(ws, L.z); g.ldc = I;
+    g.xcd_remap = 1;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
   // shared gate/up + SwiGLU over every token

@@ -371,10 +371,11 @@ int launch_attention_decode(const AttnArgs& a, hipStream_t st) {
 // The unit of work is a 32-column tile: two consecutive tokens x 16 heads
 // (MQA: every head of a token sees the same keys).  It is computed
 // transposed, keys on the rows, so that the scores never leave registers:
-//   S^T = K Q^T   5 key tiles of 32 rows starting at the pair's window start
-//                 rounded down to 8, x dh/16 steps of v_mfma_f32_32x32x16_bf16
+//   S^T = K Q^T   key tiles of 32 rows from the pair's window start rounded
+//                 down to 8 (4.5 tiles: the pair needs at most 136 rows), x
+//                 dh/16 steps of v_mfma_f32_32x32x16_bf16
 //   mask, column max / sum: within the lane, then with lane ^ 32
-//   O^T = V^T P^T dh/32 output tiles x 10 key steps; the B operand P^T is
+//   O^T = V^T P^T dh/32 output tiles x 9 key steps of 16; the B operand P^T is
 //                 the S^T accumulator rounded to bf16 in place
 // The accumulator of a 32x32 MFMA gives lane l the column l % 32 and rows
 // 8g + 4(l / 32) + i (g, i < 4); the B operand wants 8 consecutive keys
@@ -383,6 +384,8 @@ int launch_attention_decode(const AttnArgs& a, hipStream_t st) {
 // of g = 2s, 2s + 1 exactly the keys of step s, so P^T needs no shuffle.
 // Keys before the batch come from the ring (slot pos % W); the batch's own
 // keys from kc/vc (already rotated and rounded to bf16).
+// 4 waves and 74 KB of LDS per block: two blocks per CU, so one block's
+// staging overlaps the other's arithmetic.
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short attn_bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float attn_f32x16;
 
@@ -391,18 +394,19 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float attn_f32x16;
 __device__ __forceinline__ int attn_kswz(int j) { return (j & 3) | (((j >> 3) & 1) << 2); }
 
 template <int DH>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(256, 2)
 attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                   const uint16_t* __restrict__ vc, const uint16_t* __restrict__ ring_k,
                   const uint16_t* __restrict__ ring_v, const int64_t* __restrict__ pos, int T,
                   int H, int W, uint16_t* __restrict__ o) {
   constexpr int BQ = 16;
-  constexpr int NKR = 168;        // staged key rows: window start (<= 8) + 5 x 32
+  constexpr int NK = 144;         // K rows: every key of the span (16 + W - 1 <= 143)
+  constexpr int NV = 152;         // V keys: window start (<= 8) + 9 steps of 16
   constexpr int CPR = DH / 8;     // 16-B chunks per row
   constexpr int KSTEP = DH / 16;  // S^T contraction steps
   constexpr int DTILE = DH / 32;  // O^T row tiles
-  __shared__ __align__(16) uint16_t Ks[NKR * DH];   // [key][dh], chunk-swizzled
-  __shared__ __align__(16) uint16_t Vt[DH * NKR];   // [dh][key]
+  __shared__ __align__(16) uint16_t Ks[NK * DH];    // [key][dh], chunk-swizzled
+  __shared__ __align__(16) uint16_t Vt[DH * NV];    // [dh][key]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const long pos0 = *pos;
   const long P0 = (pos0 / BQ) * BQ + (long)blockIdx.x * BQ;   // span start A
@@ -416,50 +420,86 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     if (kp < pos0) return (val ? ring_v : ring_k) + (kp % W) * DH;
     return (val ? vc : kc) + (kp - pos0) * DH;
   };
-  for (int idx = tid; idx < NKR * CPR; idx += 512) {
-    const int j = idx / CPR, c = idx - j * CPR;
-    const uint16_t* src = key_src(j, false);
-    const uint4 kk = src ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(Ks + j * DH + ((c ^ attn_kswz(j)) * 8)) = kk;
-  }
-  // consecutive lanes take consecutive keys of one 8-dim chunk, so each 2-byte
-  // store row is contiguous across the wave
-  for (int idx = tid; idx < NKR * CPR; idx += 512) {
-    const int c = idx / NKR, j = idx - c * NKR;
-    const uint16_t* src = key_src(j, true);
-    const uint4 vv = src ? *reinterpret_cast<const uint4*>(src + c * 8) : make_uint4(0, 0, 0, 0);
-    const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv);
+  const int lr = lane & 31, hf = lane >> 5;
+  // wave w: head group 2 * blockIdx.y + w % 2, token pairs w / 2, w / 2 + 2, ...
+  const int hg = 2 * blockIdx.y + (wid & 1);
+  const int head = hg * 16 + (lr & 15);
+  // Q^T B operand of pair p: column lr is token 2p + lr/16, head lr % 16 of
+  // the group; zero outside the batch (branch-free: such lanes load row 0)
+  auto load_q = [&](int p, attn_bf16x8 (&dst)[DH / 16]) {
+    const long t = t0 + 2 * p + ((lr >> 4) & 1);
+    const bool ok = p < BQ / 2 && t >= 0 && t < T && head < H;
+    const uint16_t* src = ok ? q + (t * H + head) * DH + hf * 8 : q;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) Vt[(c * 8 + e) * NKR + j] = ve[e];
+    for (int ks = 0; ks < DH / 16; ++ks) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + (ok ? ks * 16 : 0));
+      dst[ks] = __builtin_bit_cast(attn_bf16x8, ok ? v : u32x4_t{0, 0, 0, 0});
+    }
+  };
+  // the first pair's q goes out ahead of the staging loads
+  attn_bf16x8 qf[DH / 16];
+  load_q(wid >> 1, qf);
+  // every load of a thread goes out before its first LDS store (one wait, not
+  // one round trip per chunk)
+  constexpr int KIT = (NK * CPR + 255) / 256, VIT = (NV * CPR + 255) / 256;
+  u32x4_t kbuf[KIT], vbuf[VIT];
+  // branch-free: rows outside the sequence load row 0 of the batch and are
+  // zeroed after the load
+  const u32x4_t zero = {0, 0, 0, 0};
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int idx = tid + 256 * it, j = idx / CPR, c = idx - j * CPR;
+    const uint16_t* src = idx < NK * CPR ? key_src(j, false) : nullptr;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>((src ? src : kc) + c * 8);
+    kbuf[it] = src ? v : zero;
+  }
+  // V: consecutive lanes take consecutive keys of one 8-dim chunk, so each
+  // 2-byte store row is contiguous across the wave
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int idx = tid + 256 * it, c = idx / NV, j = idx - c * NV;
+    const uint16_t* src = idx < NV * CPR ? key_src(j, true) : nullptr;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>((src ? src : vc) + (idx < NV * CPR ? c * 8 : 0));
+    vbuf[it] = src ? v : zero;
+  }
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int idx = tid + 256 * it, j = idx / CPR, c = idx - j * CPR;
+    if (idx < NK * CPR)
+      *reinterpret_cast<u32x4_t*>(Ks + j * DH + ((c ^ attn_kswz(j)) * 8)) = kbuf[it];
+  }
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int idx = tid + 256 * it, c = idx / NV, j = idx - c * NV;
+    if (idx < NV * CPR) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        Vt[(c * 8 + e) * NV + j] = (uint16_t)(vbuf[it][e >> 1] >> (16 * (e & 1)));
+    }
   }
   __syncthreads();
-  const int lr = lane & 31, hf = lane >> 5;
   // exp(x * scale) = exp2(x * scale * log2(e))
   const float sl2 = rsqrtf((float)DH) * 1.4426950408889634f;
   const int pr = 16 * ((lr >> 3) >> 1) + 8 * ((lr >> 2) & 1) + 4 * ((lr >> 3) & 1) + (lr & 3);
-  // wave w: head group 2 * blockIdx.y + w % 2, token pairs w / 2 and w / 2 + 4
-  const int head = (2 * blockIdx.y + (wid & 1)) * 16 + (lr & 15);
-  if ((2 * blockIdx.y + (wid & 1)) * 16 >= H) return;
-  for (int p = wid >> 1; p < BQ / 2; p += 4) {
+  if (hg * 16 >= H) return;
+  const long kmin = kbase < 0 ? -kbase : 0;       // first key row inside the sequence
+  for (int p = wid >> 1; p < BQ / 2; p += 2) {
+    // the next pair's q goes out before this pair's math
+    attn_bf16x8 qn[KSTEP];
+    load_q(p + 2, qn);
     const int tl = 2 * p;
-    if (t0 + tl + 1 < 0 || t0 + tl >= T) continue;   // both tokens outside the batch
     const int tc = tl + ((lr >> 4) & 1);             // this lane's column token
     const long t = t0 + tc;
     const bool col_ok = t >= 0 && t < T && head < H;
     const int j0 = tl & ~7;
-    attn_bf16x8 qf[KSTEP];
-#pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (col_ok) v = *reinterpret_cast<const uint4*>(q + (t * H + head) * DH + ks * 16 + hf * 8);
-      qf[ks] = *reinterpret_cast<const attn_bf16x8*>(&v);
-    }
-    // ---- S^T = K Q^T
+    if (t0 + tl + 1 >= 0 && t0 + tl < T) {           // a token of the pair is in the batch
+    // ---- S^T = K Q^T; tile 4 keeps only its first 16 rows (g < 2), its
+    // other rows are clamped to the last staged row and never used
     attn_f32x16 sacc[5];
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
       sacc[m] = attn_f32x16{};
-      const int j = j0 + 32 * m + pr;
+      const int j = min(j0 + 32 * m + pr, NK - 1);
       const uint16_t* krow = Ks + j * DH;
       const int sw = attn_kswz(j);
 #pragma unroll
@@ -469,50 +509,64 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             *reinterpret_cast<const attn_bf16x8*>(&v), qf[ks], sacc[m], 0, 0, 0);
       }
     }
-    // ---- mask to the window [tc, tc + W - 1] and the sequence start, then
-    // column max; accumulator (m, g, i) is key j0 + 32m + 16(g/2) + 8hf + 4(g%2) + i
-    const int lo = max(tc, (int)max(-kbase, 0L)), hi = tc + W - 1;
+    // ---- mask to the window [tc, tc + W - 1] and the sequence start where a
+    // tile crosses either edge for either token (wave-uniform test); then the
+    // column max.  Accumulator (m, g, i) is key j0 + 32m + 16(g/2) + 8hf + 4(g%2) + i
+    const int lo = max(tc, (int)kmin), hi = tc + W - 1;
+    const int lo_pair = max(tl + 1, (int)kmin), hi_pair = tl + W - 1;
     float mx = -INFINITY;
 #pragma unroll
-    for (int m = 0; m < 5; ++m)
+    for (int m = 0; m < 5; ++m) {
+      const int ng = m < 4 ? 4 : 2;
+      const int jt = j0 + 32 * m;
+      if (jt >= lo_pair && jt + 16 * (ng / 2) - 1 <= hi_pair) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < ng; ++g)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j0 + 32 * m + 16 * (g >> 1) + 8 * hf + 4 * (g & 1) + i;
-          const float v = (j >= lo && j <= hi) ? sacc[m][4 * g + i] : -INFINITY;
-          sacc[m][4 * g + i] = v;
-          mx = fmaxf(mx, v);
-        }
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[m][4 * g + i]);
+      } else {
+#pragma unroll
+        for (int g = 0; g < ng; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = jt + 16 * (g >> 1) + 8 * hf + 4 * (g & 1) + i;
+            const float v = (j >= lo && j <= hi) ? sacc[m][4 * g + i] : -INFINITY;
+            sacc[m][4 * g + i] = v;
+            mx = fmaxf(mx, v);
+          }
+      }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float mo = -mx * sl2;
     float sm = 0.f;
-    attn_bf16x8 pf[5][2];
+    attn_bf16x8 pf[9];
 #pragma unroll
     for (int m = 0; m < 5; ++m)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int s = 0; s < (m < 4 ? 2 : 1); ++s) {
+        float e[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[m][4 * g + i], sl2, mo));   // masked: 0
-          sm += e;
-          pf[m][g >> 1][4 * (g & 1) + i] = (short)f32_to_bf16(e);
+        for (int k = 0; k < 8; ++k) {
+          e[k] = __builtin_amdgcn_exp2f(fmaf(sacc[m][8 * s + k], sl2, mo));   // masked: 0
+          sm += e[k];
         }
+        const u32x4_t pk = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
+                            pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
+        pf[2 * m + s] = __builtin_bit_cast(attn_bf16x8, pk);
+      }
     sm += __shfl_xor(sm, 32, kWave);
     // ---- O^T = V^T P^T
     attn_f32x16 oacc[DTILE];
 #pragma unroll
     for (int dt = 0; dt < DTILE; ++dt) {
       oacc[dt] = attn_f32x16{};
-      const uint16_t* vrow = Vt + (dt * 32 + lr) * NKR + j0 + 8 * hf;
+      const uint16_t* vrow = Vt + (dt * 32 + lr) * NV + j0 + 8 * hf;
 #pragma unroll
-      for (int m = 0; m < 5; ++m)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint4 v = *reinterpret_cast<const uint4*>(vrow + 32 * m + 16 * s);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              *reinterpret_cast<const attn_bf16x8*>(&v), pf[m][s], oacc[dt], 0, 0, 0);
-        }
+      for (int st = 0; st < 9; ++st) {
+        const uint4 v = *reinterpret_cast<const uint4*>(vrow + 16 * st);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const attn_bf16x8*>(&v), pf[st], oacc[dt], 0, 0, 0);
+      }
     }
     // lane holds dims dt*32 + 8g + 4hf + (0..3) of its column
     if (col_ok) {
@@ -523,13 +577,14 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint2 w;
-          w.x = (uint32_t)f32_to_bf16(oacc[dt][4 * g] * inv) |
-                ((uint32_t)f32_to_bf16(oacc[dt][4 * g + 1] * inv) << 16);
-          w.y = (uint32_t)f32_to_bf16(oacc[dt][4 * g + 2] * inv) |
-                ((uint32_t)f32_to_bf16(oacc[dt][4 * g + 3] * inv) << 16);
+          w.x = pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv);
+          w.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
           *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g) = w;
         }
     }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks) qf[ks] = qn[ks];
   }
 }
 
@@ -541,10 +596,10 @@ int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   // unknown (device-side) offset of the first position within its span
   const dim3 grid((a.T + 15) / 16 + 1, (a.H + 31) / 32);
   if (a.dh == 128)
-    hipLaunchKernelGGL((attn_prefill_mfma<128>), grid, dim3(512), 0, st, (const uint16_t*)a.q,
+    hipLaunchKernelGGL((attn_prefill_mfma<128>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
                        a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
   else if (a.dh == 64)
-    hipLaunchKernelGGL((attn_prefill_mfma<64>), grid, dim3(512), 0, st, (const uint16_t*)a.q,
+    hipLaunchKernelGGL((attn_prefill_mfma<64>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
                        a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
   else
     return -1;

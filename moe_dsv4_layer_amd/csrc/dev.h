@@ -21,6 +21,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ float bf16_round(float f) {
   return bf16_to_f32(f32_to_bf16(f));
 }
+// two values rounded to nearest even in one v_cvt_pk_bf16_f32 (a in the low
+// half); the same result as f32_to_bf16 on each for finite inputs
+typedef float ds4g_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 ds4g_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(ds4g_f32x2{a, b}, ds4g_bf16x2));
+}
 
 // Load a stored scalar of either weight type as float.
 __device__ __forceinline__ float ldw(const uint16_t* p, long i) { return bf16_to_f32(p[i]); }

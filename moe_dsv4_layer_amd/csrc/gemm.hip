@@ -259,6 +259,23 @@ __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "me
 // for the fragment reads (32 rows x 2 chunks per instruction)
 __device__ __forceinline__ int swz1(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
+// Workgroups go to the 8 XCDs round-robin (linear id % 8), each XCD with its
+// own L2.  Renumbering the nb tiles that have work so that XCD k runs a
+// contiguous run of them (N tile fastest) keeps each expert's weight panels
+// and gathered rows on one XCD, fetched from HBM once rather than by several
+// XCDs.  A bijection of [0, nb) for any nb; the grid's blocks past nb (a
+// grouped launch sizes its grid for the worst case) have no tile.
+__device__ __forceinline__ bool xcd_tile(int nb, int& bx, int& by) {
+  const int gx = gridDim.x;
+  const int L = blockIdx.y * gx + blockIdx.x;
+  if (L >= nb) return false;
+  const int c = nb >> 3, r = nb & 7, k = L & 7, i = L >> 3;
+  const int lt = k * c + min(k, r) + i;
+  bx = lt % gx;
+  by = lt / gx;
+  return true;
+}
+
 template <int BM, int BN, int WM, int WN, int S, int EPI>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_dma_kernel(GemmArgs g) {
@@ -273,11 +290,15 @@ gemm_dma_kernel(GemmArgs g) {
   static_assert(S >= 2 && (S - 2) * NDMA <= 63, "vmcnt range");
   __shared__ u32x4_t smem[S][ROWS * 8];
   TileInfo ti;
-  if (!tile_info(g, blockIdx.y, BM, ti)) return;
+  int bx = blockIdx.x, by = blockIdx.y;
+  if (g.xcd_remap && gridDim.z == 1 &&
+      !xcd_tile(gridDim.x * (g.tiles ? min(*g.ntiles, (int)gridDim.y) : (int)gridDim.y), bx, by))
+    return;
+  if (!tile_info(g, by, BM, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / WN, wn = wid % WN;
-  const int ncol0 = blockIdx.x * (DUAL ? BN / 2 : BN);
+  const int ncol0 = bx * (DUAL ? BN / 2 : BN);
   const uint16_t* Bp = static_cast<const uint16_t*>(g.B) + ti.boff;
   const uint16_t* B2p = DUAL ? static_cast<const uint16_t*>(g.B2) + ti.boff : nullptr;
   const i32x4_t rsA = buffer_rsrc(g.A), rsB = buffer_rsrc(Bp);
@@ -418,6 +439,7 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
     if (g.tiles) {   // the tile list was built for exactly rows_hint rows per tile
       if (g.rows_hint == 64) return launch_dma_cfg<64, 256, 1, 4, 3>(g, st);
       if (g.rows_hint == 128) return launch_dma_cfg<128, 256, 2, 4, 3>(g, st);
+      if (g.rows_hint == 256) return launch_dma_cfg<256, 256, 2, 4, 2>(g, st);
       return -1;
     }
     const long nout = dual ? g.N * 2L : g.N;           // B rows per output row

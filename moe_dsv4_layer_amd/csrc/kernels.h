@@ -33,6 +33,7 @@ struct GemmArgs {
   // SIMT split-K: blockIdx.z of ksplit writes its partial sum to C + z * part_stride
   int ksplit;
   long part_stride;
+  int xcd_remap;        // MFMA: renumber tiles so each XCD runs a contiguous run
 };
 int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st);
 
