@@ -233,12 +233,14 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.epi = bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32; g.C = at<void>(ws, L.zs); g.ldc = Is;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
-  // routed down projections -> part (permuted rows, fp32)
+  // routed down projections -> part (permuted rows; bf16 on the MFMA path,
+  // fp32 on the fp32-weight path), combined in fp32 below
   {
     GemmArgs g{};
     g.A = at<void>(ws, L.z); g.lda = I; g.B = w.down; g.b_stride = (long)d * I; g.N = d;
     g.K = I; g.tiles = ra.tiles; g.ntiles = ra.ntiles; g.row_off = ra.offset;
-    g.max_tiles = max_tiles; g.rows_hint = tile_m; g.epi = EPI_F32; g.C = at<void>(ws, L.part);
+    g.max_tiles = max_tiles; g.rows_hint = tile_m; g.epi = bf ? EPI_BF16 : EPI_F32;
+    g.C = at<void>(ws, L.part);
     g.ldc = d;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
@@ -249,7 +251,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.epi = EPI_RESID; g.C = x; g.ldc = d;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
-  rc |= launch_moe_combine(x, at<float>(ws, L.part), ra.pos_of, ra.topk_w, T, d, k, st);
+  rc |= launch_moe_combine(x, at<void>(ws, L.part), bf ? 1 : 0, ra.pos_of, ra.topk_w, T, d, k, st);
   if (routing) {
     copy_out(routing->topk_idx, ra.topk_idx, (size_t)T * k * 4, st);
     copy_out(routing->topk_w, ra.topk_w, (size_t)T * k * 4, st);

@@ -43,15 +43,20 @@ namespace ds4g {
 __device__ __forceinline__ void route_wave(const float (&lg)[8], int E, int k, int* sel,
                                            float* wsel) {
   const int lane = threadIdx.x & 63;
+  // a NaN score ranks below every number; a chosen expert becomes NaN, which
+  // neither > nor == selects again.  k < E leaves a candidate every round.
   float v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (lane + 64 * i < E) ? lg[i] : -INFINITY;
+  for (int i = 0; i < 8; ++i) {
+    const float x = lg[i];
+    v[i] = (lane + 64 * i < E) ? (x == x ? x : -INFINITY) : __builtin_nanf("");
+  }
   auto best = [&](float& bv, int& bi) {
-    bv = v[0];
-    bi = lane;
+    bv = -INFINITY;
+    bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 1; i < 8; ++i)
-      if (v[i] > bv) { bv = v[i]; bi = lane + 64 * i; }
+    for (int i = 0; i < 8; ++i)
+      if (v[i] > bv || (v[i] == bv && lane + 64 * i < bi)) { bv = v[i]; bi = lane + 64 * i; }
   };
   float bv;
   int bi;
@@ -64,12 +69,12 @@ __device__ __forceinline__ void route_wave(const float (&lg)[8], int E, int k, i
 #pragma unroll 1
   for (int r = 0; r < k; ++r) {
     const float top = (r == 0) ? m : wave_max(bv);
-    const int idx = wave_min(bv == top ? bi : 0x7fffffff);
+    const int idx = min(wave_min(bv == top ? bi : 0x7fffffff), E - 1);
     if (lane == 0) { sel[r] = idx; wsel[r] = expf(top - m) / s; }
     if (lane == (idx & 63)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (lane + 64 * i == idx) v[i] = -INFINITY;
+        if (lane + 64 * i == idx) v[i] = __builtin_nanf("");
       best(bv, bi);
     }
   }

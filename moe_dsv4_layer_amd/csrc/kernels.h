@@ -118,9 +118,10 @@ struct RouteArgs {
   int* out_count; int* out_offset;
 };
 int launch_route(const RouteArgs& r, hipStream_t st);
-// x[t] += sum_j w[t,j] part[pos_of[t*k+j]] (fixed j order)
-int launch_moe_combine(float* x, const float* part, const int* pos_of, const float* w, int T,
-                       int d, int k, hipStream_t st);
+// x[t] += sum_j w[t,j] part[pos_of[t*k+j]] (fixed j order); part is fp32, or bf16
+// when part_bf16 (the bf16 path rounds each routed expert output to bf16)
+int launch_moe_combine(float* x, const void* part, int part_bf16, const int* pos_of,
+                       const float* w, int T, int d, int k, hipStream_t st);
 
 // ---------------------------------------------------------------- sampler
 struct SampleArgs {

@@ -112,6 +112,7 @@ topk_kernel(const float* __restrict__ logits, int nsplit, float* __restrict__ ls
       a = 0.f;
       for (int z = 0; z < nsplit; ++z) a += logits[((long)z * T + t) * E + e];
       lsum[(long)t * E + e] = a;
+      if (a != a) a = -INFINITY;   // a NaN score ranks below every number
     }
     v[i] = a;
     m = fmaxf(m, v[i]);
@@ -131,13 +132,16 @@ topk_kernel(const float* __restrict__ logits, int nsplit, float* __restrict__ ls
       if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
     }
     wave_argmax(bv, bi);
+    // k < E leaves a candidate every round, so bi < E; the clamp keeps an
+    // index that addresses expert weights inside [0, E) whatever the scores
     if (lane == 0) {
-      idx[(long)t * k + r] = bi;
+      idx[(long)t * k + r] = min(max(bi, 0), E - 1);
       wts[(long)t * k + r] = expf(bv - m) / sum;
     }
+    // a chosen expert becomes NaN: neither > nor == picks it again
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (lane + 64 * i == bi) v[i] = -INFINITY;
+      if (lane + 64 * i == bi) v[i] = __builtin_nanf("");
   }
 }
 
@@ -263,8 +267,17 @@ int launch_route(const RouteArgs& r, hipStream_t st) {
 // x[t] += sum_j w[t, j] * part[pos_of[t*k + j]], j = 0..k-1 in order, where
 // x already holds h2 + shared-expert output.  One block per token: the k
 // expert-output rows are read whole (contiguous), 4 floats per thread.
+// 4 consecutive expert-output values as fp32 (fp32 or bf16 storage)
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
+
+template <typename PT>
 __global__ void __launch_bounds__(256)
-moe_combine_kernel(float* __restrict__ x, const float* __restrict__ part,
+moe_combine_kernel(float* __restrict__ x, const PT* __restrict__ part,
                    const int* __restrict__ pos_of, const float* __restrict__ w, int d, int k) {
   const int t = blockIdx.x;
   __shared__ int rows[8];
@@ -277,17 +290,22 @@ moe_combine_kernel(float* __restrict__ x, const float* __restrict__ part,
   for (int c = threadIdx.x * 4; c < d; c += 1024) {
     float4 a = *reinterpret_cast<const float4*>(x + (long)t * d + c);
     for (int j = 0; j < k; ++j) {
-      const float4 p = *reinterpret_cast<const float4*>(part + (long)rows[j] * d + c);
+      const float4 p = load4(part + (long)rows[j] * d + c);
       a.x += ws[j] * p.x; a.y += ws[j] * p.y; a.z += ws[j] * p.z; a.w += ws[j] * p.w;
     }
     *reinterpret_cast<float4*>(x + (long)t * d + c) = a;
   }
 }
 
-int launch_moe_combine(float* x, const float* part, const int* pos_of, const float* w, int T,
-                       int d, int k, hipStream_t st) {
+int launch_moe_combine(float* x, const void* part, int part_bf16, const int* pos_of,
+                       const float* w, int T, int d, int k, hipStream_t st) {
   if (d % 4 || k > 8) return -1;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, st, x, part, pos_of, w, d, k);
+  if (part_bf16)
+    hipLaunchKernelGGL(moe_combine_kernel<uint16_t>, dim3(T), dim3(256), 0, st, x,
+                       static_cast<const uint16_t*>(part), pos_of, w, d, k);
+  else
+    hipLaunchKernelGGL(moe_combine_kernel<float>, dim3(T), dim3(256), 0, st, x,
+                       static_cast<const float*>(part), pos_of, w, d, k);
   return 0;
 }
 
