@@ -109,7 +109,7 @@ samp_max_kernel(const float* __restrict__ logits, int V, SampWs w) {
   __shared__ float bv[4];
   __shared__ int bi[4];
   float m = -INFINITY;
-  int mi = 0x7fffffff;
+  int mi = blockIdx.x * SEG;   // a segment of NaN / -inf logits still names a token
   for (int i = blockIdx.x * SEG + threadIdx.x; i < min(V, (blockIdx.x + 1) * SEG); i += 256) {
     const float l = logits[i];
     if (l > m) { m = l; mi = i; }
@@ -157,7 +157,8 @@ samp_q_kernel(const float* __restrict__ logits, int V, float temperature, SampWs
   const float M = Ms;
   if (blockIdx.x == 0 && threadIdx.x == 0) w.st->M = M;
   for (int i = blockIdx.x * SEG + threadIdx.x; i < min(V, (blockIdx.x + 1) * SEG); i += 256) {
-    const float q = expf((logits[i] - M) / temperature);
+    float q = expf((logits[i] - M) / temperature);
+    q = (q == q) ? fminf(q, 1.f) : 0.f;   // a NaN logit weighs nothing; keys stay < NB1
     w.q[i] = q;
     const uint32_t key = __float_as_uint(q) >> 16;
     atomicAdd(&w.h1[key], (unsigned long long)fx(q));
