@@ -33,7 +33,7 @@ inline int router_split(int hidden, bool mfma) {
 
 struct Layout {
   size_t xn, c, qkv, q, kc, vc, o, yf, ys, wr3, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
-      count, offset, tiles, ntiles, z, zs, part, total;
+      count, offset, tiles, ntiles, z, zs, part, psh, total;
 };
 
 // Byte offsets of every workspace buffer for T tokens.  fp32-sized slots are
@@ -70,6 +70,7 @@ Layout layout(const ds4g_layer_cfg& c, int T) {
   L.z = take(((size_t)T * k * I + I + Is) * 4);
   L.zs = take((size_t)T * Is * 4);
   L.part = take((size_t)T * k * d * 4);
+  L.psh = take(d * 4);
   L.total = o;
   return L;
 }
@@ -299,19 +300,15 @@ int decode_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ri
     g.W = w.wo; g.N = d; g.K = qd; g.x = at<float>(ws, L.o); g.out = x; g.accumulate = 1;
     rc |= launch_gemv<WT>(g, st);
   }
-  // router logits on y = RMSNorm(h2) g2
-  {
-    GemvArgs g{};
-    g.W = w.router; g.N = E; g.K = d; g.x = x; g.gamma = w.ffn_norm; g.eps = c.rms_eps;
-    g.out = logits;
-    rc |= launch_gemv<WT>(g, st);
-  }
+  // router logits and the shared expert on y = RMSNorm(h2) g2, routed
+  // experts, combine + residual
   MoeDecodeArgs m{};
-  m.h2 = x; m.ffn_norm = w.ffn_norm; m.eps = c.rms_eps; m.logits = logits; m.E = E;
+  m.h2 = x; m.ffn_norm = w.ffn_norm; m.eps = c.rms_eps; m.router = w.router;
+  m.logits_out = logits; m.logits = logits; m.E = E;
   m.k = c.top_k; m.d = d; m.I = c.ffn_inter; m.Is = c.shared_inter; m.gate = w.gate;
   m.up = w.up; m.down = w.down; m.sh_gate = w.sh_gate; m.sh_up = w.sh_up;
-  m.sh_down = w.sh_down; m.z = at<float>(ws, L.z); m.sel = at<int>(ws, L.tidx);
-  m.wsel = at<float>(ws, L.tw);
+  m.sh_down = w.sh_down; m.z = at<float>(ws, L.z); m.part_sh = at<float>(ws, L.psh);
+  m.sel = at<int>(ws, L.tidx); m.wsel = at<float>(ws, L.tw);
   if (routing) {
     m.topk_idx = routing->topk_idx; m.topk_w = routing->topk_w;
     m.count = routing->expert_count; m.offset = routing->expert_offset;

@@ -22,10 +22,19 @@
 #define DS4G_GATEUP_RB 4
 #endif
 #ifndef DS4G_GATEUP_GRID_MAX
-#define DS4G_GATEUP_GRID_MAX 1024
+#define DS4G_GATEUP_GRID_MAX 896
 #endif
 #ifndef DS4G_DOWN_RB
 #define DS4G_DOWN_RB 8
+#endif
+#ifndef DS4G_ROUTER_SHARED_RB
+#define DS4G_ROUTER_SHARED_RB 2
+#endif
+#ifndef DS4G_SHDOWN_GRID_MAX
+#define DS4G_SHDOWN_GRID_MAX 128
+#endif
+#ifndef DS4G_SHDOWN_RB
+#define DS4G_SHDOWN_RB 8
 #endif
 
 namespace ds4g {
@@ -230,120 +239,276 @@ template int launch_gemv<uint16_t>(const GemvArgs&, hipStream_t);
 template int launch_gemv<float>(const GemvArgs&, hipStream_t);
 
 // ---------------------------------------------------------------------------
-// MoE gate/up for one token: for each chosen expert slot s (k routed + the
-// shared expert) and inner row i:  z[s, i] = silu(G y) * (U y) with
-// y = RMSNorm(h2) * g2.  Blocks (4 waves splitting K = hidden) stride over
-// RB (gate, up) row pairs, shared-expert rows first.  Every wave routes for
-// itself from the logits in its registers (no block barrier before its
-// routed loads); block 0 publishes the routing for the down kernel and the
-// caller.
+// MoE decode for one token, three kernels:
+//   router_shared_decode  logits = W_r y and the shared expert's
+//                         z_sh = silu(G_sh y) * (U_sh y), y = RMSNorm(h2) * g2
+//   moe_gateup_decode     every wave picks the top-k from the logits; routed
+//                         z_s = silu(G_s y) * (U_s y); its first blocks do the
+//                         shared expert's down rows part_sh = D_sh z_sh, whose
+//                         loads need no routing and fill HBM while the routed
+//                         blocks route
+//   moe_down_decode       x = h2 + sum_s w_s D_s z_s + part_sh
+// The shared expert needs only y, so it runs beside the router (itself a
+// small read); the routed kernels carry only the routed weights.
+
+// y = RMSNorm(h2) * g2 over the K slice of wave w (chunks [w*CPL*64,
+// (w+1)*CPL*64)); h2 is read by every block (L2-resident).
+template <typename WT, int CPL>
+struct NormSlice {
+  float v[CPL][8];
+  __device__ __forceinline__ void load(const float* h2, int nchunk) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = (wid * CPL + i) * 64 + lane;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = (c < nchunk) ? h2[c * 8 + e] : 0.f;
+    }
+  }
+  // block-wide (4 waves): every thread must call it
+  __device__ __forceinline__ void normalize(const void* gamma, float eps, int d, float* ssq) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nchunk = d >> 3;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
+    ss = wave_sum(ss);
+    if (lane == 0) ssq[wid] = ss;
+    __syncthreads();
+    const float rs = rsqrtf((ssq[0] + ssq[1] + ssq[2] + ssq[3]) / (float)d + eps);
+    const WT* g = static_cast<const WT*>(gamma);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = (wid * CPL + i) * 64 + lane;
+      if (c < nchunk) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = v[i][e] * rs * ldw(g, c * 8 + e);
+      }
+    }
+  }
+};
+
+// Router logits and the shared expert's gate/up.  Task groups: the first
+// ceil(E/RB) are RB router rows each (one weight row -> one logit), the rest
+// RB shared (gate, up) row pairs each.  Blocks (4 waves splitting K = hidden)
+// stride over groups; the next group's loads go out before the reductions.
 template <typename WT, int CPL, int RB>
+__global__ void __launch_bounds__(256)
+router_shared_decode(MoeDecodeArgs a) {
+  __shared__ float ssq[4];
+  __shared__ float red[4][RB][2];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nchunk = a.d >> 3;
+  const int ngr = (a.E + RB - 1) / RB, ng = ngr + (a.Is + RB - 1) / RB;
+  Chunk8<WT> cg[RB][CPL], cu[RB][CPL];
+  auto load_group = [&](int g) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const WT *G, *U = nullptr;
+      if (g < ngr) {
+        const int e = g * RB + r;
+        if (e >= a.E) continue;
+        G = static_cast<const WT*>(a.router) + (long)e * a.d;
+      } else {
+        const int t = (g - ngr) * RB + r;
+        if (t >= a.Is) continue;
+        G = static_cast<const WT*>(a.sh_gate) + (long)t * a.d;
+        U = static_cast<const WT*>(a.sh_up) + (long)t * a.d;
+      }
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = (wid * CPL + i) * 64 + lane;
+        if (c < nchunk) {
+          cg[r][i].load(G + c * 8);
+          if (U) cu[r][i].load(U + c * 8);
+        }
+      }
+    }
+  };
+  int g = blockIdx.x;
+  if (g < ng) load_group(g);
+  NormSlice<WT, CPL> y;
+  y.load(a.h2, nchunk);
+  y.normalize(a.ffn_norm, a.eps, a.d, ssq);
+  if (blockIdx.x == 0 && a.router_in) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = (wid * CPL + i) * 64 + lane;
+      if (c < nchunk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a.router_in[c * 8 + e] = y.v[i][e];
+    }
+  }
+  for (; g < ng; g += gridDim.x) {
+    const bool router = g < ngr;
+    float ag[RB], au[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      ag[r] = 0.f; au[r] = 0.f;
+      const bool live = router ? g * RB + r < a.E : (g - ngr) * RB + r < a.Is;
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int c = (wid * CPL + i) * 64 + lane;
+          if (c < nchunk) {
+            float f[8];
+            cg[r][i].widen(f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ag[r] += f[e] * y.v[i][e];
+            if (!router) {
+              cu[r][i].widen(f);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) au[r] += f[e] * y.v[i][e];
+            }
+          }
+        }
+      }
+    }
+    if (g + (int)gridDim.x < ng) load_group(g + gridDim.x);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      ag[r] = wave_sum(ag[r]);
+      if (!router) au[r] = wave_sum(au[r]);
+    }
+    __syncthreads();
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) { red[wid][r][0] = ag[r]; red[wid][r][1] = au[r]; }
+    }
+    __syncthreads();
+    if (wid == 0 && lane < RB) {
+      float gs = 0.f, us = 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) { gs += red[p][lane][0]; us += red[p][lane][1]; }
+      if (router) {
+        const int e = g * RB + lane;
+        if (e < a.E) a.logits_out[e] = gs;
+      } else {
+        const int t = (g - ngr) * RB + lane;
+        if (t < a.Is) a.z[a.k * a.I + t] = silu(gs) * us;   // z layout: routed slots, then shared
+      }
+    }
+  }
+}
+
+// Shared expert's down rows: part_sh[n] = D_sh[n, :] . z_sh, RBS whole rows
+// (K = Is <= 512 * CPL2) per wave, every wave of blocks [0, nblk).
+template <typename WT, int CPL2, int RBS>
+__device__ void shared_down_rows(const MoeDecodeArgs& a, int blk, int nblk) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int Ks = a.Is;
+  const WT* D = static_cast<const WT*>(a.sh_down);
+  const float* zz = a.z + a.k * a.I;
+  for (int n0 = (blk * 4 + wid) * RBS; n0 < a.d; n0 += nblk * 4 * RBS) {
+    Chunk8<WT> ch[RBS][CPL2];
+#pragma unroll
+    for (int r = 0; r < RBS; ++r)
+#pragma unroll
+      for (int i = 0; i < CPL2; ++i) {
+        const int c = i * 64 + lane;
+        if (n0 + r < a.d && c * 8 < Ks) ch[r][i].load(D + (long)(n0 + r) * Ks + c * 8);
+      }
+    float zv[CPL2][8];
+#pragma unroll
+    for (int i = 0; i < CPL2; ++i) {
+      const int c = i * 64 + lane;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zv[i][e] = (c * 8 < Ks) ? zz[c * 8 + e] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < RBS; ++r) {
+      float p = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL2; ++i) {
+        const int c = i * 64 + lane;
+        if (n0 + r < a.d && c * 8 < Ks) {
+          float f[8];
+          ch[r][i].widen(f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p += f[e] * zv[i][e];
+        }
+      }
+      p = wave_sum(p);
+      if (lane == 0 && n0 + r < a.d) a.part_sh[n0 + r] = p;
+    }
+  }
+}
+
+// Routed gate/up: blocks [0, a.nsd) are shared-down blocks; the rest stride
+// over RB routed (gate, up) row pairs.  Every wave routes for itself from the
+// logits in its registers (no block barrier before its routed loads); the
+// first routed block publishes the routing for the down kernel and the caller.
+template <typename WT, int CPL, int RB, int CPL2>
 __global__ void __launch_bounds__(256)
 moe_gateup_decode(MoeDecodeArgs a) {
   __shared__ float ssq[4];
   __shared__ float red[4][RB][2];
   __shared__ int wsel_idx[4][8];
   __shared__ float wsel_w[4][8];
+  if ((int)blockIdx.x < a.nsd) {
+    shared_down_rows<WT, CPL2, DS4G_SHDOWN_RB>(a, blockIdx.x, a.nsd);
+    return;
+  }
+  const int bid = blockIdx.x - a.nsd, nblk = gridDim.x - a.nsd;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nchunk = a.d >> 3;
-  const int ntask = a.k * a.I + a.Is;
+  const int ntask = a.k * a.I;
 
   // The reads every block needs (router logits, h2) go out first, ahead of
   // any weight traffic: the routed rows cannot be loaded before they return.
   float lg[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) lg[i] = a.logits[min(lane + 64 * i, a.E - 1)];
-  float yv[CPL][8];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = (wid * CPL + i) * 64 + lane;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) yv[i][e] = (c < nchunk) ? a.h2[c * 8 + e] : 0.f;
-  }
+  NormSlice<WT, CPL> y;
+  y.load(a.h2, nchunk);
   const int* sel = wsel_idx[wid];     // this wave's routing (its own LDS slots)
   const float* wsel = wsel_w[wid];
 
   Chunk8<WT> cg[RB][CPL], cu[RB][CPL];
-  // task t < Is: shared row t; else routed slot s = (t - Is) / I, row i
+  // task t: routed slot s = t / I, row i
   auto load_tasks = [&](int t0) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const int t = t0 + r;
       if (t >= ntask) continue;
-      const WT *G, *U;
-      if (t < a.Is) {
-        const long base = (long)t * a.d;
-        G = static_cast<const WT*>(a.sh_gate) + base;
-        U = static_cast<const WT*>(a.sh_up) + base;
-      } else {
-        const int u = t - a.Is, s = u / a.I, i = u - s * a.I;
-        const long base = ((long)sel[s] * a.I + i) * a.d;
-        G = static_cast<const WT*>(a.gate) + base;
-        U = static_cast<const WT*>(a.up) + base;
-      }
+      const int s = t / a.I, i = t - s * a.I;
+      const long base = ((long)sel[s] * a.I + i) * a.d;
+      const WT* G = static_cast<const WT*>(a.gate) + base;
+      const WT* U = static_cast<const WT*>(a.up) + base;
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = (wid * CPL + i) * 64 + lane;
-        if (c < nchunk) { cg[r][i].load(G + c * 8); cu[r][i].load(U + c * 8); }
+      for (int ii = 0; ii < CPL; ++ii) {
+        const int c = (wid * CPL + ii) * 64 + lane;
+        if (c < nchunk) { cg[r][ii].load(G + c * 8); cu[r][ii].load(U + c * 8); }
       }
     }
   };
-  int t0 = blockIdx.x * RB;
-  const int stride = gridDim.x * RB;
+  int t0 = bid * RB;
+  const int stride = nblk * RB;
   route_wave(lg, a.E, a.k, wsel_idx[wid], wsel_w[wid]);   // every wave routes for itself
   if (t0 < ntask) load_tasks(t0);
+  y.normalize(a.ffn_norm, a.eps, a.d, ssq);
 
-  // y = RMSNorm(h2) * g2 (wave w holds chunks [w*CPL*64, (w+1)*CPL*64))
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += yv[i][e] * yv[i][e];
-  ss = wave_sum(ss);
-  if (lane == 0) ssq[wid] = ss;
-  __syncthreads();
-  const float rs = rsqrtf((ssq[0] + ssq[1] + ssq[2] + ssq[3]) / (float)a.d + a.eps);
-  const WT* g2 = static_cast<const WT*>(a.ffn_norm);
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = (wid * CPL + i) * 64 + lane;
-    if (c < nchunk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) yv[i][e] = yv[i][e] * rs * ldw(g2, c * 8 + e);
+  if (bid == 0 && wid == 0 && lane < a.k) {
+    // publish the routing (one token: perm lists its k entries by expert)
+    const int sj = sel[lane];
+    const float wj = wsel[lane];
+    a.sel[lane] = sj;
+    a.wsel[lane] = wj;
+    if (a.topk_idx) a.topk_idx[lane] = sj;
+    if (a.topk_w) a.topk_w[lane] = wj;
+    if (a.perm) {
+      int r = 0;
+      for (int q = 0; q < a.k; ++q) r += sel[q] < sj;
+      a.perm[r] = lane;
     }
   }
-
-  if (blockIdx.x == 0) {
-    // publish the routing (one token: perm lists its k entries by expert)
-    if (wid == 0 && lane < a.k) {
-      const int sj = sel[lane];
-      const float wj = wsel[lane];
-      a.sel[lane] = sj;
-      a.wsel[lane] = wj;
-      if (a.topk_idx) a.topk_idx[lane] = sj;
-      if (a.topk_w) a.topk_w[lane] = wj;
-      if (a.perm) {
-        int r = 0;
-        for (int q = 0; q < a.k; ++q) r += sel[q] < sj;
-        a.perm[r] = lane;
-      }
-    }
-    if (a.count || a.offset) {
-      for (int e = threadIdx.x; e <= a.E; e += blockDim.x) {
-        int c = 0, o = 0;
-        for (int q = 0; q < a.k; ++q) { c += sel[q] == e; o += sel[q] < e; }
-        if (a.count && e < a.E) a.count[e] = c;
-        if (a.offset) a.offset[e] = o;
-      }
-    }
-    if (a.router_in) {
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = (wid * CPL + i) * 64 + lane;
-        if (c < nchunk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a.router_in[c * 8 + e] = yv[i][e];
-      }
+  if (bid == 0 && (a.count || a.offset)) {
+    for (int e = threadIdx.x; e <= a.E; e += blockDim.x) {
+      int c = 0, o = 0;
+      for (int q = 0; q < a.k; ++q) { c += sel[q] == e; o += sel[q] < e; }
+      if (a.count && e < a.E) a.count[e] = c;
+      if (a.offset) a.offset[e] = o;
     }
   }
 
@@ -357,11 +522,11 @@ moe_gateup_decode(MoeDecodeArgs a) {
         for (int i = 0; i < CPL; ++i) {
           const int c = (wid * CPL + i) * 64 + lane;
           if (c < nchunk) {
-            float f[8], g[8];
+            float f[8], gg[8];
             cg[r][i].widen(f);
-            cu[r][i].widen(g);
+            cu[r][i].widen(gg);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { ag[r] += f[e] * yv[i][e]; au[r] += g[e] * yv[i][e]; }
+            for (int e = 0; e < 8; ++e) { ag[r] += f[e] * y.v[i][e]; au[r] += gg[e] * y.v[i][e]; }
           }
         }
       }
@@ -376,21 +541,18 @@ moe_gateup_decode(MoeDecodeArgs a) {
     }
     __syncthreads();
     if (wid == 0 && lane < RB && t0 + lane < ntask) {
-      float g = 0.f, u = 0.f;
+      float gs = 0.f, us = 0.f;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) { g += red[p][lane][0]; u += red[p][lane][1]; }
-      // z layout: routed slots 0..k-1 (I each), then the shared expert
-      const int t = t0 + lane;
-      const int zi = (t < a.Is) ? a.k * a.I + t : t - a.Is;
-      a.z[zi] = silu(g) * u;
+      for (int p = 0; p < 4; ++p) { gs += red[p][lane][0]; us += red[p][lane][1]; }
+      a.z[t0 + lane] = silu(gs) * us;
     }
   }
 }
 
 // MoE down + combine + residual for one token:
-//   x[n] = h2[n] + sum_s w_s (D_{e_s} z_s)[n] + (D_sh z_sh)[n]
-// A block is 8 waves and owns RB output rows; wave w handles slots w and
-// w + 8, so the weight rows of every slot are in flight together.  The sum
+//   x[n] = h2[n] + sum_s w_s (D_{e_s} z_s)[n] + part_sh[n]
+// A block is 8 waves and owns RB output rows; wave w handles routed slot w
+// (k <= 8), so the weight rows of every slot are in flight together.  The sum
 // runs in slot order, then the shared expert, then the residual.  Block 0
 // advances the ring position (the attention kernel has read it already).
 template <typename WT, int CPL, int RB>
@@ -398,16 +560,16 @@ __global__ void __launch_bounds__(512)
 moe_down_decode(MoeDecodeArgs a, float* x, int64_t* pos_inc) {
   __shared__ int sel[8];
   __shared__ float wsel[8];
-  __shared__ float part[9][RB];
+  __shared__ float part[8][RB];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (threadIdx.x < a.k) { sel[threadIdx.x] = a.sel[threadIdx.x]; wsel[threadIdx.x] = a.wsel[threadIdx.x]; }
   if (pos_inc && blockIdx.x == 0 && threadIdx.x == 0) *pos_inc += 1;
   __syncthreads();
   const int n0 = blockIdx.x * RB;
-  for (int s = wid; s <= a.k; s += 8) {
-    const int Ks = (s < a.k) ? a.I : a.Is;
-    const WT* D = (s < a.k) ? static_cast<const WT*>(a.down) + (long)sel[s] * a.d * a.I
-                            : static_cast<const WT*>(a.sh_down);
+  const int Ks = a.I;
+  if (wid < a.k) {
+    const int s = wid;
+    const WT* D = static_cast<const WT*>(a.down) + (long)sel[s] * a.d * a.I;
     Chunk8<WT> ch[RB][CPL];
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -445,42 +607,51 @@ moe_down_decode(MoeDecodeArgs a, float* x, int64_t* pos_inc) {
   if (wid == 0 && lane < RB && n0 + lane < a.d) {
     float v = 0.f;
     for (int s = 0; s < a.k; ++s) v += wsel[s] * part[s][lane];
-    v += part[a.k][lane];
+    v += a.part_sh[n0 + lane];
     x[n0 + lane] = a.h2[n0 + lane] + v;
   }
 }
 
 template <typename WT>
-int launch_moe_decode(const MoeDecodeArgs& a, float* x, int64_t* pos_inc, hipStream_t st) {
-  if (a.k > 8) return -1;
-  // gate/up: K = d split over 4 waves; blocks stride over task groups
-  const int nchunk = a.d / 8;
-  const int ntask = a.k * a.I + a.Is;
-  const int cpl = (nchunk + 255) / 256;
-  constexpr int RB = DS4G_GATEUP_RB;
-  int grid = (ntask + RB - 1) / RB;
-  if (grid > DS4G_GATEUP_GRID_MAX) grid = DS4G_GATEUP_GRID_MAX;
-  if (cpl <= 1)
-    hipLaunchKernelGGL((moe_gateup_decode<WT, 1, RB>), dim3(grid), dim3(256), 0, st, a);
-  else if (cpl <= 2)
-    hipLaunchKernelGGL((moe_gateup_decode<WT, 2, RB>), dim3(grid), dim3(256), 0, st, a);
-  else if (cpl <= 4)
-    hipLaunchKernelGGL((moe_gateup_decode<WT, 4, RB>), dim3(grid), dim3(256), 0, st, a);
-  else
-    return -1;
-  // down: K = I (or Is) per slot, whole rows per wave
-  const int kmax = a.I > a.Is ? a.I : a.Is;
-  const int cpl2 = (kmax / 8 + 63) / 64;
-  constexpr int RB2 = DS4G_DOWN_RB;
-  const int grid2 = (a.d + RB2 - 1) / RB2;
-  if (cpl2 <= 1)
-    hipLaunchKernelGGL((moe_down_decode<WT, 1, RB2>), dim3(grid2), dim3(512), 0, st, a, x, pos_inc);
-  else if (cpl2 <= 2)
-    hipLaunchKernelGGL((moe_down_decode<WT, 2, RB2>), dim3(grid2), dim3(512), 0, st, a, x, pos_inc);
-  else if (cpl2 <= 4)
-    hipLaunchKernelGGL((moe_down_decode<WT, 4, RB2>), dim3(grid2), dim3(512), 0, st, a, x, pos_inc);
-  else
-    return -1;
+int launch_moe_decode(const MoeDecodeArgs& a0, float* x, int64_t* pos_inc, hipStream_t st) {
+  if (a0.k > 8 || a0.E > 512 || a0.d % 8 || a0.I % 8 || a0.Is % 8) return -1;
+  const int nchunk = a0.d / 8;
+  const int cpl = (nchunk + 255) / 256;      // K = d over 4 waves
+  const int cpls = (a0.Is / 8 + 63) / 64;    // K = Is per wave (shared down)
+  const int cpld = (a0.I / 8 + 63) / 64;     // K = I per wave (routed down)
+  if (cpl > 4 || cpls > 4 || cpld > 4) return -1;
+  MoeDecodeArgs a = a0;
+  // router logits + shared gate/up
+  {
+    constexpr int RB = DS4G_ROUTER_SHARED_RB;
+    const int ng = (a.E + RB - 1) / RB + (a.Is + RB - 1) / RB;
+#define DS4G_RS(C) hipLaunchKernelGGL((router_shared_decode<WT, C, RB>), dim3(ng), dim3(256), 0, st, a)
+    if (cpl == 1) DS4G_RS(1); else if (cpl == 2) DS4G_RS(2); else DS4G_RS(4);
+#undef DS4G_RS
+  }
+  // shared down rows + routed gate/up
+  {
+    constexpr int RB = DS4G_GATEUP_RB;
+    a.nsd = (a.d + 4 * DS4G_SHDOWN_RB - 1) / (4 * DS4G_SHDOWN_RB);   // 4 waves x RB rows
+    if (a.nsd > DS4G_SHDOWN_GRID_MAX) a.nsd = DS4G_SHDOWN_GRID_MAX;
+    const int ntask = a.k * a.I;
+    int grid = (ntask + RB - 1) / RB;
+    if (grid > DS4G_GATEUP_GRID_MAX) grid = DS4G_GATEUP_GRID_MAX;
+    grid += a.nsd;
+#define DS4G_GU(C, C2) hipLaunchKernelGGL((moe_gateup_decode<WT, C, RB, C2>), dim3(grid), dim3(256), 0, st, a)
+#define DS4G_GU2(C) { if (cpls == 1) DS4G_GU(C, 1); else if (cpls == 2) DS4G_GU(C, 2); else DS4G_GU(C, 4); }
+    if (cpl == 1) DS4G_GU2(1) else if (cpl == 2) DS4G_GU2(2) else DS4G_GU2(4)
+#undef DS4G_GU2
+#undef DS4G_GU
+  }
+  // routed down + combine + residual
+  {
+    constexpr int RB2 = DS4G_DOWN_RB;
+    const int grid2 = (a.d + RB2 - 1) / RB2;
+#define DS4G_DN(C) hipLaunchKernelGGL((moe_down_decode<WT, C, RB2>), dim3(grid2), dim3(512), 0, st, a, x, pos_inc)
+    if (cpld == 1) DS4G_DN(1); else if (cpld == 2) DS4G_DN(2); else DS4G_DN(4);
+#undef DS4G_DN
+  }
   return 0;
 }
 template int launch_moe_decode<uint16_t>(const MoeDecodeArgs&, float*, int64_t*, hipStream_t);
