@@ -20,10 +20,10 @@ brute force on tiny inputs, or published test values.
 from .layer import (widen, rmsnorm, silu, rope, Ring, attend, topk_desc,
                     routing_permutation, layer_forward, lm_head, embed,
                     stack_prefill, router_margin)
-from .sampler import sample, argmax, nucleus
+from .sampler import sample, argmax, nucleus, min_p_mask
 from .rng import SplitMix64
 
 __all__ = ["widen", "rmsnorm", "silu", "rope", "Ring", "attend", "topk_desc",
            "routing_permutation", "layer_forward", "lm_head", "embed",
-           "stack_prefill", "router_margin", "sample", "argmax", "nucleus",
+           "stack_prefill", "router_margin", "sample", "argmax", "nucleus", "min_p_mask",
            "SplitMix64"]

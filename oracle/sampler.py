@@ -18,7 +18,12 @@ Readings where the page is silent:
     token is kept, top_p >= 1 keeps everything;
   * the roulette walks the vocabulary in index order and skips tokens the
     top-p step dropped; if rounding leaves r > 0 after the last kept token,
-    that last kept token is returned.
+    that last kept token is returned;
+  * min-p (named with top-p in the page's function index, not defined
+    there): the usual filter, a token stays when its probability is at least
+    min(min_p, 1) times the largest one (so the most probable tokens always
+    stay); with top-p a token is kept when both keep it (both keep a prefix
+    of the descending order, so the shorter prefix); min_p <= 0 disables it.
 """
 from __future__ import annotations
 
@@ -44,18 +49,28 @@ def nucleus(q: np.ndarray, top_p: float) -> np.ndarray:
     return keep
 
 
-def sample(logits, temperature: float, top_p: float, u: float) -> dict:
+def min_p_mask(q: np.ndarray, min_p: float) -> np.ndarray:
+    """Boolean mask of the tokens min-p keeps: q >= min(min_p, 1) * max q."""
+    if min_p <= 0.0:
+        return np.ones(q.shape[0], dtype=bool)
+    return q >= min(min_p, 1.0) * np.max(q)
+
+
+def sample(logits, temperature: float, top_p: float, u: float, min_p: float = 0.0) -> dict:
     """Sample one token id.  u in [0, 1) is the generator's draw.
 
-    Returns dict(token, n_kept, kept_sum, r, gap) where gap is the smallest
-    distance, relative to kept_sum, between r and a running-sum boundary of
-    the roulette; a test uses it to spot draws that sit on a boundary.
+    Returns dict(token, n_kept, kept_sum, r, gap, min_p_gap) where gap is
+    the smallest distance, relative to kept_sum, between r and a running-sum
+    boundary of the roulette, and min_p_gap the smallest relative distance of
+    a weight from the min-p threshold (inf without min-p); a test uses them
+    to spot draws that sit on a boundary.
     """
     l = np.asarray(logits, dtype=np.float64)
     if temperature <= 0.0:
-        return dict(token=argmax(l), n_kept=1, kept_sum=1.0, r=0.0, gap=np.inf)
+        return dict(token=argmax(l), n_kept=1, kept_sum=1.0, r=0.0, gap=np.inf,
+                    min_p_gap=np.inf)
     q = np.exp((l - np.max(l)) / temperature)
-    keep = nucleus(q, top_p)
+    keep = nucleus(q, top_p) & min_p_mask(q, min_p)
     kept_idx = np.nonzero(keep)[0]                 # index order
     running = np.cumsum(q[kept_idx])
     S = running[-1]
@@ -63,5 +78,9 @@ def sample(logits, temperature: float, top_p: float, u: float) -> dict:
     pos = int(np.searchsorted(running, r, side="left"))   # first running >= r
     tok = int(kept_idx[min(pos, kept_idx.size - 1)])
     gap = float(np.min(np.abs(running - r)) / S)
+    mgap = np.inf
+    if min_p > 0.0:
+        thr = min(min_p, 1.0) * np.max(q)
+        mgap = float(np.min(np.abs(q - thr)) / thr)
     return dict(token=tok, n_kept=int(kept_idx.size), kept_sum=float(S),
-                r=float(r), gap=gap)
+                r=float(r), gap=gap, min_p_gap=mgap)

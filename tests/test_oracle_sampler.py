@@ -118,3 +118,60 @@ def test_low_temperature_and_tiny_top_p_are_argmax():
 def test_underflow_keeps_one_token():
     l = np.array([0.0, -1e4, -2e4])
     assert sample(l, 0.5, 0.95, 0.99)["token"] == 0
+
+
+# ---- min-p (a reading: keep q >= min(min_p, 1) * max q, intersected with top-p)
+
+def test_min_p_closed_form():
+    # weights 8, 4, 2, 1 (max 8); min_p 0.3 keeps weights >= 2.4: {8, 4}
+    q = np.array([8.0, 4.0, 2.0, 1.0])
+    assert oracle.min_p_mask(q, 0.3).tolist() == [True, True, False, False]
+    assert oracle.min_p_mask(q, 0.25).tolist() == [True, True, True, False]   # 2 >= 2 exactly
+    assert oracle.min_p_mask(q, 0.0).all()
+    l = np.log(q)
+    # kept {0, 1}, sum 12, walked in index order: boundary at 8/12
+    assert sample(l, 1.0, 1.0, 0.66, min_p=0.3)["token"] == 0
+    assert sample(l, 1.0, 1.0, 0.67, min_p=0.3)["token"] == 1
+    # top-p 0.5 (8/15 >= 0.5 after the first) is the shorter prefix here
+    assert sample(l, 1.0, 0.5, 0.99, min_p=0.3)["token"] == 0
+    assert sample(l, 1.0, 0.5, 0.99, min_p=0.3)["n_kept"] == 1
+
+
+def test_min_p_zero_is_top_p_alone():
+    r = np.random.default_rng(11)
+    l = r.normal(size=500) * 2
+    for u in r.random(40):
+        a = sample(l, 0.8, 0.9, u)
+        b = sample(l, 0.8, 0.9, u, min_p=0.0)
+        assert a["token"] == b["token"] and a["n_kept"] == b["n_kept"]
+
+
+def test_min_p_one_is_argmax():
+    # min_p >= 1 keeps only the largest weight(s): a unique maximum is argmax
+    r = np.random.default_rng(12)
+    for _ in range(10):
+        l = r.normal(size=200)
+        for u in (0.0, 0.3, 0.999):
+            assert sample(l, 1.3, 1.0, u, min_p=1.0)["token"] == argmax(l)
+            assert sample(l, 1.3, 1.0, u, min_p=2.5)["token"] == argmax(l)
+
+
+def test_min_p_brute_force_against_page_loop():
+    # kept set by definition, token by the page's own loop over it
+    r = np.random.default_rng(13)
+    for trial in range(20):
+        l = r.normal(size=40) * 3
+        T, p, mp = 0.9, float(r.uniform(0.3, 1.0)), float(r.uniform(0.01, 0.5))
+        q = np.exp((l - l.max()) / T)
+        # top-p kept set, brute force: a token is kept when the mass strictly
+        # ahead of it in the (q desc, index asc) order is below p * total
+        ahead = np.array([q[(q > q[i]) | ((q == q[i]) & (np.arange(40) < i))].sum()
+                          for i in range(40)])
+        kept = (ahead < p * q.sum()) | (p >= 1.0)
+        kept &= q >= mp * q.max()
+        for u in r.random(10):
+            got = sample(l, T, p, u, min_p=mp)
+            if got["gap"] < 1e-12 or got["min_p_gap"] < 1e-12:
+                continue
+            assert got["n_kept"] == int(kept.sum())
+            assert got["token"] == _page_roulette(q.tolist(), kept.tolist(), u)
