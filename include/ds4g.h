@@ -166,6 +166,35 @@ int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype,
                        const void *embed_table, float *x_next,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* Sampling parameters of ds4g_lmhead_sample_ex.
+ *   temperature, top_p: as for ds4g_lmhead_sample.
+ *   min_p: the min-p filter that the page's function index names together
+ *     with top-p (sample_top_p_min_p; 阶段四 4.3 and the index table): a
+ *     token stays only if q_i >= min(min_p, 1) * max q; with top-p a token is
+ *     kept when both keep it.  min_p <= 0 disables it.
+ *   temperature_dev: NULL, or a device float read by every call in place of
+ *     `temperature` (<= 0 or NaN: argmax, rng untouched).  It is the per-token
+ *     temperature override of the page's tool-call mode (阶段六 温度覆盖:
+ *     structural tokens at temperature 0): a captured decode graph switches
+ *     between sampling and argmax by writing that float, with no re-capture.
+ *     rng_state must then be non-NULL. */
+typedef struct {
+  float temperature, top_p, min_p;
+  const float *temperature_dev;
+} ds4g_sample_params;
+
+/* ds4g_lmhead_sample with min-p and the device temperature override;
+ * ds4g_lmhead_sample is this call with min_p = 0 and temperature_dev = NULL.
+ * params: host pointer, read during the call.  Other arguments, results and
+ * errors as for ds4g_lmhead_sample; DS4G_ERR_INVALID_ARG also for a NaN
+ * min_p or a NULL params. */
+int ds4g_lmhead_sample_ex(int32_t hidden, int32_t vocab, int32_t wdtype,
+                          const void *final_norm, float rms_eps, const void *w_lm,
+                          const float *x, const ds4g_sample_params *params,
+                          uint64_t *rng_state, float *logits, int32_t *token,
+                          const void *embed_table, float *x_next,
+                          void *ws, size_t ws_bytes, void *stream);
+
 /* Token embedding (阶段四 4.1): x[t] = widen(table[ids[t]]) for t < T.
  *   table: device [vocab, hidden] in wdtype; ids: device int32 [T];
  *   x: device fp32 [T, hidden] out.  An id outside [0, vocab) yields a row

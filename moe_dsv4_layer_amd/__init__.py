@@ -19,7 +19,7 @@ F32, BF16 = 0, 1
 
 # ds4g.h declares these functions; the ABI test checks the header agrees.
 EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_prefill", "ds4g_layer_decode",
-           "ds4g_lmhead_sample", "ds4g_embed", "ds4g_status_string")
+           "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_status_string")
 
 
 class LayerCfg(ctypes.Structure):
@@ -38,6 +38,11 @@ WEIGHT_NAMES = ("attn_norm", "qkv_a", "qkv_b", "wo", "ffn_norm", "router", "gate
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+
+
+class SampleParams(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("min_p", ctypes.c_float), ("temperature_dev", ctypes.c_void_p)]
 
 
 class KvRing(ctypes.Structure):
@@ -94,6 +99,10 @@ def _load() -> ctypes.CDLL:
     lib.ds4g_lmhead_sample.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
                                        ctypes.c_float, P, P, ctypes.c_float, ctypes.c_float, P,
                                        P, P, P, P, P, ctypes.c_size_t, P]
+    lib.ds4g_lmhead_sample_ex.restype = ctypes.c_int
+    lib.ds4g_lmhead_sample_ex.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
+                                          ctypes.c_float, P, P, ctypes.POINTER(SampleParams), P,
+                                          P, P, P, P, P, ctypes.c_size_t, P]
     lib.ds4g_embed.restype = ctypes.c_int
     lib.ds4g_embed.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
                                ctypes.c_int32, P, P]
@@ -185,6 +194,21 @@ def lmhead_sample(hidden: int, vocab: int, wdtype: int, final_norm, rms_eps: flo
                                 _ptr(embed_table), _ptr(x_next),
                                 ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "ds4g_lmhead_sample")
+
+
+def lmhead_sample_ex(hidden: int, vocab: int, wdtype: int, final_norm, rms_eps: float, w_lm, x,
+                     temperature: float, top_p: float, min_p: float, rng_state, logits, token,
+                     ws, stream=None, temperature_dev=None, embed_table=None,
+                     x_next=None) -> None:
+    """ds4g_lmhead_sample_ex: min-p, and an optional device temperature
+    (float32 tensor of one element) read by the call in place of temperature."""
+    p = SampleParams(temperature, top_p, min_p, _ptr(temperature_dev))
+    rc = lib.ds4g_lmhead_sample_ex(hidden, vocab, wdtype, _ptr(final_norm), rms_eps,
+                                   w_lm.data_ptr(), x.data_ptr(), ctypes.byref(p),
+                                   _ptr(rng_state), logits.data_ptr(), token.data_ptr(),
+                                   _ptr(embed_table), _ptr(x_next),
+                                   ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "ds4g_lmhead_sample_ex")
 
 
 def embed(vocab: int, hidden: int, wdtype: int, table, ids, x, stream=None) -> None:

@@ -378,18 +378,20 @@ int ds4g_layer_decode(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, ds
   return decode_impl<float>(*cfg, *w, *ring, x, routing, ws, (hipStream_t)stream);
 }
 
-int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype, const void* final_norm,
-                       float rms_eps, const void* w_lm, const float* x, float temperature,
-                       float top_p, uint64_t* rng_state, float* logits, int32_t* token,
-                       const void* embed_table, float* x_next, void* ws, size_t ws_bytes,
-                       void* stream) {
+int ds4g_lmhead_sample_ex(int32_t hidden, int32_t vocab, int32_t wdtype, const void* final_norm,
+                          float rms_eps, const void* w_lm, const float* x,
+                          const ds4g_sample_params* params, uint64_t* rng_state, float* logits,
+                          int32_t* token, const void* embed_table, float* x_next, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!params) return DS4G_ERR_INVALID_ARG;
+  const float temperature = params->temperature, top_p = params->top_p, min_p = params->min_p;
   if (hidden <= 0 || vocab <= 0 || !w_lm || !x || !logits || !token || !ws)
     return DS4G_ERR_INVALID_ARG;
   if ((embed_table == nullptr) != (x_next == nullptr)) return DS4G_ERR_INVALID_ARG;
   if (wdtype != DS4G_F32 && wdtype != DS4G_BF16) return DS4G_ERR_INVALID_ARG;
-  if (!(rms_eps >= 0.f) || temperature != temperature || top_p != top_p)
+  if (!(rms_eps >= 0.f) || temperature != temperature || top_p != top_p || min_p != min_p)
     return DS4G_ERR_INVALID_ARG;
-  if (temperature > 0.f && !rng_state) return DS4G_ERR_INVALID_ARG;
+  if ((temperature > 0.f || params->temperature_dev) && !rng_state) return DS4G_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
   if (hidden % 8 || hidden > 16384 || vocab > (1 << 18)) return DS4G_ERR_UNSUPPORTED;
   if (ws_bytes < sample_ws_bytes(vocab)) return DS4G_ERR_WORKSPACE;
@@ -404,11 +406,22 @@ int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype, const void
   }
   SampleArgs sa{};
   sa.logits = logits; sa.V = vocab; sa.temperature = temperature; sa.top_p = top_p;
+  sa.min_p = min_p; sa.temperature_dev = params->temperature_dev;
   sa.rng = rng_state; sa.token = token; sa.ws = ws;
   rc |= launch_sample(sa, st);
   if (embed_table)
     rc |= launch_embed(embed_table, wdtype == DS4G_BF16, token, 1, vocab, hidden, x_next, st);
   return hip_status(rc);
+}
+
+int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype, const void* final_norm,
+                       float rms_eps, const void* w_lm, const float* x, float temperature,
+                       float top_p, uint64_t* rng_state, float* logits, int32_t* token,
+                       const void* embed_table, float* x_next, void* ws, size_t ws_bytes,
+                       void* stream) {
+  ds4g_sample_params p{temperature, top_p, 0.f, nullptr};
+  return ds4g_lmhead_sample_ex(hidden, vocab, wdtype, final_norm, rms_eps, w_lm, x, &p, rng_state,
+                               logits, token, embed_table, x_next, ws, ws_bytes, stream);
 }
 
 int ds4g_embed(int32_t vocab, int32_t hidden, int32_t wdtype, const void* table,

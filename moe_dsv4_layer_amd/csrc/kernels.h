@@ -133,7 +133,8 @@ int launch_moe_combine(float* x, const void* part, int part_bf16, const int* pos
 struct SampleArgs {
   const float* logits;
   int V;
-  float temperature, top_p;
+  float temperature, top_p, min_p;
+  const float* temperature_dev;   // optional device temperature (overrides temperature)
   uint64_t* rng;
   int* token;
   void* ws;             // sampler workspace

@@ -34,7 +34,7 @@ struct SampState {
   uint32_t vstar;       // bits of the cut weight q*
   int m;                // equal-to-q* entries kept (in index order)
   unsigned long long above; // mass strictly above q*
-  double r;             // roulette point
+  double u;             // the uniform draw; r = u * (kept mass) is formed in S7
   int all;              // top_p >= 1: keep everything
 };
 
@@ -127,9 +127,18 @@ samp_max_kernel(const float* __restrict__ logits, int V, SampWs w) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < NB2; i += nb * 256) { w.h2[i] = 0; w.c2[i] = 0; }
 }
 
+// The temperature of a call: a host value, or one read from device memory
+// each time (tdev), so that a captured graph can switch between sampling and
+// argmax without being captured again.
+__device__ __forceinline__ bool sampling(float temperature, const float* tdev) {
+  const float t = tdev ? *tdev : temperature;
+  return t > 0.f;
+}
+
 // argmax over the segment results (temperature <= 0)
 __global__ void __launch_bounds__(64)
-samp_argmax_kernel(int nb, SampWs w, int* token) {
+samp_argmax_kernel(int nb, SampWs w, int* token, float temperature, const float* tdev) {
+  if (sampling(temperature, tdev)) return;
   float m = -INFINITY;
   int mi = 0x7fffffff;
   for (int b = threadIdx.x; b < nb; b += 64) {
@@ -149,7 +158,10 @@ __device__ __forceinline__ float global_max(const SampWs& w, int nb) {
 
 // S2: q = exp((l - M) / T); level-1 histogram of fixed-point mass.
 __global__ void __launch_bounds__(256)
-samp_q_kernel(const float* __restrict__ logits, int V, float temperature, SampWs w) {
+samp_q_kernel(const float* __restrict__ logits, int V, float temperature, const float* tdev,
+              SampWs w) {
+  if (!sampling(temperature, tdev)) return;
+  if (tdev) temperature = *tdev;
   __shared__ float Ms;
   const int nb = gridDim.x;
   if (threadIdx.x == 0) Ms = global_max(w, nb);
@@ -168,7 +180,8 @@ samp_q_kernel(const float* __restrict__ logits, int V, float temperature, SampWs
 // S3 (one block of 1024): total mass, target, and the level-1 bucket where the
 // descending cumulative mass reaches the target.
 __global__ void __launch_bounds__(1024)
-samp_level1_kernel(float top_p, SampWs w) {
+samp_level1_kernel(float top_p, SampWs w, float temperature, const float* tdev) {
+  if (!sampling(temperature, tdev)) return;
   __shared__ unsigned long long red[16];
   constexpr int PER = NB1 / 1024;
   // position i in descending bucket order: bucket NB1-1-i
@@ -206,8 +219,8 @@ samp_level1_kernel(float top_p, SampWs w) {
 
 // S4: level-2 histogram inside bucket b1.
 __global__ void __launch_bounds__(256)
-samp_hist2_kernel(int V, SampWs w) {
-  if (w.st->all) return;
+samp_hist2_kernel(int V, SampWs w, float temperature, const float* tdev) {
+  if (!sampling(temperature, tdev) || w.st->all) return;
   const uint32_t b1 = w.st->b1;
   for (int i = blockIdx.x * SEG + threadIdx.x; i < min(V, (blockIdx.x + 1) * SEG); i += 256) {
     const float q = w.q[i];
@@ -226,10 +239,23 @@ __device__ __forceinline__ uint64_t splitmix64_next(uint64_t* s) {
   return z ^ (z >> 31);
 }
 
+// min-p: every weight below min(min_p, 1) is dropped (the largest weight
+// is exactly 1).  When that threshold lies above the top-p cut q*, it becomes
+// the cut and every entry equal to it is kept; otherwise top-p decides.
+__device__ __forceinline__ void apply_min_p(SampState* st, float min_p) {
+  if (!(min_p > 0.f)) return;
+  const float thr = fminf(min_p, 1.f);
+  if (thr > __uint_as_float(st->vstar)) {
+    st->vstar = __float_as_uint(thr);
+    st->m = 0x7fffffff;
+  }
+}
+
 // S5 (one block of 1024): exact cut weight q*, how many equal-to-q* entries
-// are kept, kept mass, and the roulette point r = u * kept mass.
+// are kept (top-p, then min-p), and the generator draw u.
 __global__ void __launch_bounds__(1024)
-samp_level2_kernel(SampWs w, uint64_t* rng) {
+samp_level2_kernel(SampWs w, uint64_t* rng, float min_p, float temperature, const float* tdev) {
+  if (!sampling(temperature, tdev)) return;
   __shared__ unsigned long long red[16];
   SampState* st = w.st;
   if (st->all) {
@@ -237,9 +263,9 @@ samp_level2_kernel(SampWs w, uint64_t* rng) {
       st->vstar = 0u;
       st->m = 0x7fffffff;   // every entry equal to q* = 0 is kept too
       st->above = st->total;
+      apply_min_p(st, min_p);
       const uint64_t z = splitmix64_next(rng);
-      const double u = (double)(z >> 40) * (1.0 / 16777216.0);
-      st->r = u * (double)st->total;
+      st->u = (double)(z >> 40) * (1.0 / 16777216.0);
     }
     return;
   }
@@ -266,10 +292,9 @@ samp_level2_kernel(SampWs w, uint64_t* rng) {
       st->vstar = vbits;
       st->m = (int)mm;
       st->above = run;
-      const unsigned long long kept = run + (unsigned long long)mm * qf;
+      apply_min_p(st, min_p);
       const uint64_t z = splitmix64_next(rng);
-      const double u = (double)(z >> 40) * (1.0 / 16777216.0);
-      st->r = u * (double)kept;
+      st->u = (double)(z >> 40) * (1.0 / 16777216.0);
     }
     run = nxt;
   }
@@ -278,7 +303,8 @@ samp_level2_kernel(SampWs w, uint64_t* rng) {
 // S6: per segment, mass strictly above q*, how many such entries, and how
 // many entries equal q*.
 __global__ void __launch_bounds__(256)
-samp_segsum_kernel(int V, SampWs w) {
+samp_segsum_kernel(int V, SampWs w, float temperature, const float* tdev) {
+  if (!sampling(temperature, tdev)) return;
   __shared__ unsigned long long ss[4];
   __shared__ int sn[4], st_[4];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -305,19 +331,20 @@ samp_segsum_kernel(int V, SampWs w) {
   }
 }
 
-// S7 (one block of 1024): find the segment, then the entry, where the running
-// kept mass (vocabulary order) first reaches r.
+// S7 (one block of 1024): the kept mass K (exact, per segment in fixed point),
+// r = u * K, then the segment and the entry where the running kept mass
+// (vocabulary order) first reaches r.
 __global__ void __launch_bounds__(1024)
-samp_pick_kernel(int V, int nb, SampWs w, int* token) {
+samp_pick_kernel(int V, int nb, SampWs w, int* token, float temperature, const float* tdev) {
+  if (!sampling(temperature, tdev)) return;
   __shared__ unsigned long long red[16];
   __shared__ int tie_base_s, seg_s;
-  __shared__ unsigned long long cum_before_s;
+  __shared__ unsigned long long cum_before_s, kept_s;
   __shared__ int wtie[16];
   const SampState& st = *w.st;
   const float qs = __uint_as_float(st.vstar);
   const unsigned long long qf = fx(qs);
   const int m = st.m;
-  const double r = st.r;
   // level A: segments (nb <= 1024), one per thread
   const int b = threadIdx.x;
   int tie = (b < nb) ? w.seg_tie[b] : 0;
@@ -345,7 +372,9 @@ samp_pick_kernel(int V, int nb, SampWs w, int* token) {
   const int segn = (b < nb) ? w.seg_gtn[b] + (int)kt : 0;
   const unsigned long long cinc = block_incl_scan_u64(segk, red);
   if (b == 0) seg_s = nb - 1;
+  if (b == nb - 1) kept_s = cinc;
   __syncthreads();
+  const double r = st.u * (double)kept_s;
   // first segment with kept entries whose inclusive cumulative mass >= r
   const bool hit = (b < nb) && segn > 0 && (double)cinc >= r;
   // smallest such b: reduce with atomicMin in LDS
@@ -399,17 +428,19 @@ int launch_sample(const SampleArgs& s, hipStream_t st) {
   const int nb = (s.V + SEG - 1) / SEG;
   if (nb > 1024 || s.V > (1 << 18)) return -1;
   SampWs w = carve(s.ws, s.V);
+  const float T = s.temperature;
+  const float* td = s.temperature_dev;
   hipLaunchKernelGGL(samp_max_kernel, dim3(nb), dim3(256), 0, st, s.logits, s.V, w);
-  if (!(s.temperature > 0.f)) {
-    hipLaunchKernelGGL(samp_argmax_kernel, dim3(1), dim3(64), 0, st, nb, w, s.token);
-    return 0;
-  }
-  hipLaunchKernelGGL(samp_q_kernel, dim3(nb), dim3(256), 0, st, s.logits, s.V, s.temperature, w);
-  hipLaunchKernelGGL(samp_level1_kernel, dim3(1), dim3(1024), 0, st, s.top_p, w);
-  hipLaunchKernelGGL(samp_hist2_kernel, dim3(nb), dim3(256), 0, st, s.V, w);
-  hipLaunchKernelGGL(samp_level2_kernel, dim3(1), dim3(1024), 0, st, w, s.rng);
-  hipLaunchKernelGGL(samp_segsum_kernel, dim3(nb), dim3(256), 0, st, s.V, w);
-  hipLaunchKernelGGL(samp_pick_kernel, dim3(1), dim3(1024), 0, st, s.V, nb, w, s.token);
+  // a host temperature picks the path here; a device one, inside every kernel
+  if (td || !(T > 0.f))
+    hipLaunchKernelGGL(samp_argmax_kernel, dim3(1), dim3(64), 0, st, nb, w, s.token, T, td);
+  if (!td && !(T > 0.f)) return 0;
+  hipLaunchKernelGGL(samp_q_kernel, dim3(nb), dim3(256), 0, st, s.logits, s.V, T, td, w);
+  hipLaunchKernelGGL(samp_level1_kernel, dim3(1), dim3(1024), 0, st, s.top_p, w, T, td);
+  hipLaunchKernelGGL(samp_hist2_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
+  hipLaunchKernelGGL(samp_level2_kernel, dim3(1), dim3(1024), 0, st, w, s.rng, s.min_p, T, td);
+  hipLaunchKernelGGL(samp_segsum_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
+  hipLaunchKernelGGL(samp_pick_kernel, dim3(1), dim3(1024), 0, st, s.V, nb, w, s.token, T, td);
   return 0;
 }
 

@@ -129,3 +129,20 @@ def test_decode_and_sample_reject_before_launch():
     assert E(10, 64, ds4g.BF16, 0x1000, 0x1000, 0, 0x1000, None) == ds4g.ERR_INVALID_ARG
     assert E(10, 60, ds4g.BF16, 0x1000, 0x1000, 4, 0x1000, None) == ds4g.ERR_UNSUPPORTED
     assert E(10, 64, 3, 0x1000, 0x1000, 4, 0x1000, None) == ds4g.ERR_INVALID_ARG
+
+
+def test_sample_ex_rejects_before_launch():
+    L = ds4g.lib
+    ns = ds4g.workspace_bytes(None, 0, 129280)
+
+    def call(params, rng=0x1000):
+        return L.ds4g_lmhead_sample_ex(4096, 129280, ds4g.BF16, 0x1000, 1e-6, 0x1000, 0x1000,
+                                       ctypes.byref(params) if params is not None else None,
+                                       rng, 0x1000, 0x1000, None, None, 0x1000, ns, None)
+    P = ds4g.SampleParams
+    assert call(None) == ds4g.ERR_INVALID_ARG                            # no params
+    assert call(P(0.7, 0.95, float("nan"), None)) == ds4g.ERR_INVALID_ARG
+    assert call(P(0.7, 0.95, 0.05, None), rng=None) == ds4g.ERR_INVALID_ARG
+    # a device temperature may ask for sampling at run time: the generator is required
+    assert call(P(0.0, 0.95, 0.0, 0x1000), rng=None) == ds4g.ERR_INVALID_ARG
+    assert call(P(0.7, float("nan"), 0.0, None)) == ds4g.ERR_INVALID_ARG

@@ -101,3 +101,95 @@ def test_sampler_small_vocab_grid():
         u = oracle.SplitMix64(st_in).next_f32()
         ref = oracle.sample(logits, 0.8, 0.9, u)
         assert tok == ref["token"] or ref["gap"] < 1e-5, (i, tok, ref)
+
+
+def _run_ex(hw, shape, vocab, x, temperature, top_p, min_p, state, ws, tdev=None):
+    logits = torch.empty(vocab, dtype=torch.float32, device="cuda")
+    token = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    rng = torch.tensor([np.array(state, dtype=np.uint64).view(np.int64).item()],
+                       dtype=torch.int64, device="cuda")
+    wd = ds4g.BF16 if shape.wdtype == synth.BF16 else ds4g.F32
+    ds4g.lmhead_sample_ex(shape.hidden, vocab, wd, hw["final_norm"], shape.rms_eps,
+                          hw["lm_head"], x, temperature, top_p, min_p, rng, logits, token, ws,
+                          temperature_dev=tdev)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy(), int(token.item()), int(rng.cpu().numpy().view(np.uint64)[0])
+
+
+@pytest.mark.parametrize("temperature,top_p,min_p", [(0.7, 0.95, 0.05), (1.0, 1.0, 0.1),
+                                                     (1.2, 0.9, 0.3), (0.7, 0.95, 0.0)])
+def test_sampler_min_p_teacher_forced(temperature, top_p, min_p):
+    shape, hw, ws = _setup(4096, 129280, synth.BF16, 80)
+    state = synth.rng_seed(1004) ^ 0x5555
+    agree = amb = 0
+    for i in range(20):
+        x = synth.hidden(1, 4096, 80, stream=i, device="cuda").reshape(-1) * 2.0
+        st_in = state
+        logits, tok, state = _run_ex(hw, shape, 129280, x, temperature, top_p, min_p, st_in, ws)
+        g = oracle.SplitMix64(st_in)
+        u = g.next_f32()
+        assert _u64(state) == g.state, "generator must advance by exactly one draw"
+        ref = oracle.sample(logits, temperature, top_p, u, min_p=min_p)
+        if tok == ref["token"]:
+            agree += 1
+            continue
+        assert ref["gap"] < 1e-5 or ref["min_p_gap"] < 1e-5, (i, tok, ref)
+        amb += 1
+    log(f"sampler T={temperature} p={top_p} min_p={min_p}: {agree} equal, {amb} on a boundary")
+    assert agree >= 18
+
+
+def test_sampler_device_temperature_override():
+    # the temperature read from device memory: 0 -> argmax with the generator
+    # untouched; > 0 -> the same token and draw as the host temperature
+    shape, hw, ws = _setup(512, 5000, synth.BF16, 81)
+    tdev = torch.zeros(1, dtype=torch.float32, device="cuda")
+    for i in range(6):
+        x = synth.hidden(1, 512, 81, stream=i, device="cuda").reshape(-1) * 3.0
+        state = 1000 + i
+        tdev.fill_(0.0)
+        logits, tok, st2 = _run_ex(hw, shape, 5000, x, 0.9, 0.95, 0.0, state, ws, tdev=tdev)
+        assert tok == oracle.argmax(logits) and st2 == state
+        tdev.fill_(0.9)
+        _, tok_d, st_d = _run_ex(hw, shape, 5000, x, 123.0, 0.95, 0.02, state, ws, tdev=tdev)
+        _, tok_h, st_h = _run_ex(hw, shape, 5000, x, 0.9, 0.95, 0.02, state, ws)
+        assert (tok_d, st_d) == (tok_h, st_h)
+        g = oracle.SplitMix64(state)
+        g.next_u64()
+        assert st_d == g.state                      # exactly one draw
+
+
+def test_sampler_device_temperature_in_a_graph():
+    # one captured call, replayed with the device temperature switched between
+    # argmax and sampling; every replay is checked against an eager call
+    shape, hw, ws = _setup(512, 5000, synth.BF16, 82)
+    x = synth.hidden(1, 512, 82, device="cuda").reshape(-1) * 3.0
+    tdev = torch.full((1,), 0.8, dtype=torch.float32, device="cuda")
+    logits = torch.empty(5000, dtype=torch.float32, device="cuda")
+    token = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    rng = torch.tensor([777], dtype=torch.int64, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ds4g.lmhead_sample_ex(512, 5000, ds4g.BF16, hw["final_norm"], shape.rms_eps, hw["lm_head"],
+                              x, 0.0, 0.95, 0.05, rng, logits, token, ws, stream=s,
+                              temperature_dev=tdev)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ds4g.lmhead_sample_ex(512, 5000, ds4g.BF16, hw["final_norm"], shape.rms_eps, hw["lm_head"],
+                              x, 0.0, 0.95, 0.05, rng, logits, token, ws, stream=s,
+                              temperature_dev=tdev)
+    torch.cuda.synchronize()
+    for i, t in enumerate([0.8, 0.0, 1.1, 0.0, 0.8]):
+        tdev.fill_(t)
+        state = 4242 + i
+        rng.copy_(torch.tensor([state], dtype=torch.int64))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_tok, got_state = int(token.item()), int(rng.cpu().numpy().view(np.uint64)[0])
+        lg, tok_e, st_e = _run_ex(hw, shape, 5000, x, t, 0.95, 0.05, state, ws)
+        assert (got_tok, got_state) == (tok_e, st_e), (i, t)
+        if t == 0.0:
+            assert got_state == state and got_tok == oracle.argmax(lg)
