@@ -355,6 +355,31 @@ def main() -> int:
     pre_tflops = layer_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
     pre_dense_tflops = dense_gemm_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
 
+    # ------------------------------------------------------------ batched decode
+    # one token of each of B sequences per call (rings at position 128; the
+    # projections, router and experts run over the B rows, weights read once)
+    batch = {}
+    for B in (8, 32, 128):
+        rkb = torch.zeros((B, s.window, s.head_dim), dtype=torch.bfloat16, device=dev)
+        rvb = torch.zeros_like(rkb)
+        posb = torch.full((B,), s.window, dtype=torch.int64, device=dev)
+        ringb = ds4g.make_ring(rkb, rvb, posb)
+        xb0 = synth.hidden(B, s.hidden, 7000 + B, device=dev)
+        xb = xb0.clone()
+        for i in range(2):
+            xb.copy_(xb0)
+            ds4g.layer_decode_batch(cfg, layers[i % nl]["cw"], ringb, xb, B, ws, stream=stream)
+        torch.cuda.synchronize()
+        nb_steps = 8
+        e0.record(stream)
+        for i in range(nb_steps):
+            ds4g.layer_decode_batch(cfg, layers[i % nl]["cw"], ringb, xb, B, ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_b = e0.elapsed_time(e1) / nb_steps
+        batch[str(B)] = {"ms_per_step": round(ms_b, 4), "tok_s": round(B / (ms_b * 1e-3), 1)}
+        del rkb, rvb, posb, xb, xb0
+
     # ------------------------------------------------------------ lm_head + sampler
     V = 129280
     hw = synth.head_weights(s, V, 1004, device=dev)
@@ -409,6 +434,9 @@ def main() -> int:
                     "weight_bytes": prefill_weight_bytes(s),
                     "hbm_frac_weights": round(prefill_weight_bytes(s) / (ms_prefill * 1e-3)
                                               / 1e9 / HBM_PEAK_GBS, 4)},
+        "decode_batch": {"workload": "same layer, one decode token of each of B sequences per "
+                                     "call (ds4g_layer_decode_batch), weight sets rotated",
+                         "by_B": batch},
         "lmhead_sample": {"workload": "RMSNorm + lm_head 129280x4096 bf16 + T=0.7 top-p 0.95",
                           "us": round(us_lm, 2),
                           "hbm_frac": round(lm_bytes / (us_lm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},

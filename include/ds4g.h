@@ -142,6 +142,27 @@ int ds4g_layer_decode(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
                       ds4g_kv_ring *ring, float *x, ds4g_routing *routing,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* Batched decode: one token of each of B >= 1 independent sequences through
+ * the layer (the throughput form of 阶段四 4.2's single-token step; the
+ * pages' server decodes one sequence at a time).  Sequence b is at position
+ * rings->pos[b] and owns ring b.
+ *   rings: k, v device [B, window, head_dim] in the ring's dtype (ring b at
+ *          offset b * window * head_dim), pos device int64 [B]; ring b gets the
+ *          token's key/value at slot pos[b] % window and pos[b] += 1.
+ *   x:     device fp32 [B, hidden], row b the layer input of sequence b;
+ *          overwritten with the layer output.
+ *   routing: optional outputs as for ds4g_layer_prefill with T = B (row b =
+ *          sequence b).
+ *   ws:    at least ds4g_workspace_bytes(cfg, B, 0) bytes, 256-byte aligned.
+ * The projections, router and experts run as in ds4g_layer_prefill over the
+ * B rows (weights read once for all of them); each row's attention sees only
+ * its own ring.  Returns DS4G_OK or a negative ds4g_status (B > 65535:
+ * DS4G_ERR_UNSUPPORTED). */
+int ds4g_layer_decode_batch(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
+                            ds4g_kv_ring *rings, float *x, int32_t B,
+                            ds4g_routing *routing, void *ws, size_t ws_bytes,
+                            void *stream);
+
 /* lm_head + sampler for one token (阶段四 4.3 采样).
  *   final_norm: device [hidden] gain in wdtype, or NULL to skip the norm.
  *   w_lm:   device [vocab, hidden] in wdtype.

@@ -19,6 +19,7 @@ F32, BF16 = 0, 1
 
 # ds4g.h declares these functions; the ABI test checks the header agrees.
 EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_prefill", "ds4g_layer_decode",
+           "ds4g_layer_decode_batch",
            "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_status_string")
 
 
@@ -95,6 +96,10 @@ def _load() -> ctypes.CDLL:
     lib.ds4g_layer_decode.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
                                       ctypes.POINTER(KvRing), P, ctypes.POINTER(Routing), P,
                                       ctypes.c_size_t, P]
+    lib.ds4g_layer_decode_batch.restype = ctypes.c_int
+    lib.ds4g_layer_decode_batch.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
+                                            ctypes.POINTER(KvRing), P, ctypes.c_int32,
+                                            ctypes.POINTER(Routing), P, ctypes.c_size_t, P]
     lib.ds4g_lmhead_sample.restype = ctypes.c_int
     lib.ds4g_lmhead_sample.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
                                        ctypes.c_float, P, P, ctypes.c_float, ctypes.c_float, P,
@@ -183,6 +188,17 @@ def layer_decode(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x, ws,
                                ctypes.byref(routing) if routing is not None else None,
                                ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "ds4g_layer_decode")
+
+
+def layer_decode_batch(cfg: LayerCfg, w: LayerWeights, rings: KvRing, x, B: int, ws,
+                       routing: Optional[Routing] = None, stream=None) -> None:
+    """One decode token of each of B sequences; rings: k, v [B, W, dh], pos [B]."""
+    rc = lib.ds4g_layer_decode_batch(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(rings),
+                                     x.data_ptr(), B,
+                                     ctypes.byref(routing) if routing is not None else None,
+                                     ws.data_ptr(), ws.numel() * ws.element_size(),
+                                     _stream(stream))
+    _check(rc, "ds4g_layer_decode_batch")
 
 
 def lmhead_sample(hidden: int, vocab: int, wdtype: int, final_norm, rms_eps: float, w_lm, x,

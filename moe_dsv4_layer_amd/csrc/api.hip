@@ -133,8 +133,12 @@ void copy_out(void* dst, const void* src, size_t bytes, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------ prefill
+// Layer-major prefill of T tokens of one sequence, or (batch) one decode
+// token of each of T independent sequences: the same GEMMs, router and
+// experts over T rows; only the attention stage differs.
 int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring& ring,
-                 float* x, int T, ds4g_routing* routing, void* ws, hipStream_t st) {
+                 float* x, int T, ds4g_routing* routing, void* ws, hipStream_t st,
+                 bool batch = false) {
   const Layout L = layout(c, T);
   const bool bf = c.wdtype == DS4G_BF16;
   const int d = c.hidden, r = c.qkv_rank, H = c.n_heads, dh = c.head_dim, qd = H * dh,
@@ -168,7 +172,10 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   aa.kc = at<uint16_t>(ws, L.kc); aa.vc = at<uint16_t>(ws, L.vc);
   aa.ring_k = (uint16_t*)ring.k; aa.ring_v = (uint16_t*)ring.v;
   aa.o = at<void>(ws, L.o); aa.o_bf16 = bf ? 1 : 0; aa.heads_per_block = H < 64 ? H : 64;
-  rc |= bf ? launch_attention_prefill_mfma(aa, st) : launch_attention(aa, st);
+  if (batch)   // RoPE at each sequence's position, its own ring, *pos[b] += 1
+    rc |= launch_attention_decode_batch(aa, T, st);
+  else
+    rc |= bf ? launch_attention_prefill_mfma(aa, st) : launch_attention(aa, st);
 
   // h2 = h + W_o o   (in place in x)
   gemm(at<void>(ws, L.o), qd, w.wo, T, d, qd, EPI_RESID, x, d);
@@ -361,6 +368,21 @@ int ds4g_layer_prefill(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
   if (ws_bytes < layout(*cfg, T).total) return DS4G_ERR_WORKSPACE;
   clear_stale_error();
   return prefill_impl(*cfg, *w, *ring, x, T, routing, ws, (hipStream_t)stream);
+}
+
+int ds4g_layer_decode_batch(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
+                            ds4g_kv_ring* rings, float* x, int32_t B, ds4g_routing* routing,
+                            void* ws, size_t ws_bytes, void* stream) {
+  int s = check_cfg(cfg);
+  if (s != DS4G_OK) return s;
+  if ((s = check_weights(w)) != DS4G_OK) return s;
+  if ((s = check_ring(rings)) != DS4G_OK) return s;
+  if (!x || !ws || B <= 0) return DS4G_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
+  if (B > 65535) return DS4G_ERR_UNSUPPORTED;
+  if (ws_bytes < layout(*cfg, B).total) return DS4G_ERR_WORKSPACE;
+  clear_stale_error();
+  return prefill_impl(*cfg, *w, *rings, x, B, routing, ws, (hipStream_t)stream, true);
 }
 
 int ds4g_layer_decode(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, ds4g_kv_ring* ring,

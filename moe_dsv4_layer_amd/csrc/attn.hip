@@ -210,12 +210,22 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
 //           key groups meet in LDS.
 // Slot p % W holds position p - W, outside the window, so block 0 may
 // overwrite it while the other blocks read.  *pos is advanced by a later
-// kernel.
-template <int DH>
+// kernel.  Batched decode: blockIdx.y is the sequence b, with its own qkv row
+// (stride qkv_stride), ring (b * W * DH), position pos[b] and o row (H * DH);
+// o is fp32 or bf16 (OT).
+template <int DH, typename OT>
 __global__ void __launch_bounds__(256)
-attn_decode_kernel(const float* __restrict__ qkv, int H, int W, int rd, float base,
-                   const int64_t* __restrict__ pos, uint16_t* __restrict__ ring_k,
-                   uint16_t* __restrict__ ring_v, float* __restrict__ o) {
+attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W, int rd,
+                   float base, const int64_t* __restrict__ pos, uint16_t* __restrict__ ring_k,
+                   uint16_t* __restrict__ ring_v, OT* __restrict__ o) {
+  {
+    const int b = blockIdx.y;
+    qkv += b * qkv_stride;
+    pos += b;
+    ring_k += (long)b * W * DH;
+    ring_v += (long)b * W * DH;
+    o += (long)b * H * DH;
+  }
   constexpr int KC = DH / 16;            // 16-byte K chunks per thread (half a row)
   constexpr int DG = DH / 8;             // p.v dim groups of 8
   constexpr int KG = 256 / DG;           // p.v key groups
@@ -338,20 +348,46 @@ attn_decode_kernel(const float* __restrict__ qkv, int H, int W, int rd, float ba
     float v = 0.f;
 #pragma unroll
     for (int g = 0; g < KG; ++g) v += red[g][tid];
-    o[(long)h * DH + tid] = v * inv;
+    if constexpr (sizeof(OT) == 2) o[(long)h * DH + tid] = f32_to_bf16(v * inv);
+    else o[(long)h * DH + tid] = v * inv;
   }
 }
 
 int launch_attention_decode(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(a.H);
   if (a.dh == 128)
-    hipLaunchKernelGGL((attn_decode_kernel<128>), grid, dim3(256), 0, st, a.qkv, a.H, a.W, a.rd,
-                       a.base, a.pos, a.ring_k, a.ring_v, (float*)a.o);
+    hipLaunchKernelGGL((attn_decode_kernel<128, float>), grid, dim3(256), 0, st, a.qkv, 0L, a.H,
+                       a.W, a.rd, a.base, a.pos, a.ring_k, a.ring_v, (float*)a.o);
   else if (a.dh == 64)
-    hipLaunchKernelGGL((attn_decode_kernel<64>), grid, dim3(256), 0, st, a.qkv, a.H, a.W, a.rd,
-                       a.base, a.pos, a.ring_k, a.ring_v, (float*)a.o);
+    hipLaunchKernelGGL((attn_decode_kernel<64, float>), grid, dim3(256), 0, st, a.qkv, 0L, a.H,
+                       a.W, a.rd, a.base, a.pos, a.ring_k, a.ring_v, (float*)a.o);
   else
     return -1;
+  return 0;
+}
+
+__global__ void pos_advance_batch_kernel(int64_t* pos, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) pos[b] += 1;
+}
+
+int launch_attention_decode_batch(const AttnArgs& a, int B, hipStream_t st) {
+  if (B <= 0 || B > 65535) return -1;
+  const dim3 grid(a.H, B);
+  const long stride = (long)a.H * a.dh + 2L * a.dh;
+#define DS4G_AD(DH, OT)                                                                       \
+  hipLaunchKernelGGL((attn_decode_kernel<DH, OT>), grid, dim3(256), 0, st, a.qkv, stride, a.H, \
+                     a.W, a.rd, a.base, a.pos, a.ring_k, a.ring_v, (OT*)a.o)
+  if (a.dh == 128) {
+    if (a.o_bf16) DS4G_AD(128, uint16_t); else DS4G_AD(128, float);
+  } else if (a.dh == 64) {
+    if (a.o_bf16) DS4G_AD(64, uint16_t); else DS4G_AD(64, float);
+  } else {
+    return -1;
+  }
+#undef DS4G_AD
+  // every block has read pos[b]: advance the positions
+  hipLaunchKernelGGL(pos_advance_batch_kernel, dim3((B + 255) / 256), dim3(256), 0, st, a.pos, B);
   return 0;
 }
 

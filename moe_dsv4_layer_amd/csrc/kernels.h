@@ -72,6 +72,10 @@ int launch_attention(const AttnArgs& a, hipStream_t st);
 // single-token attention: RoPE of q/k at *pos, write (k, v) to the ring
 // slot, attend over the window; o fp32 [H*dh].  Does not advance *pos.
 int launch_attention_decode(const AttnArgs& a, hipStream_t st);
+// B independent sequences, one token each: row b of qkv at position pos[b],
+// ring b at ring_k / ring_v + b * W * dh; o [B, H*dh] fp32 or bf16 (o_bf16);
+// advances every pos[b] by one afterwards.
+int launch_attention_decode_batch(const AttnArgs& a, int B, hipStream_t st);
 // prefill on the matrix cores: bf16 q (q_bf16 = 1) and o (o_bf16 = 1)
 int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st);
 
