@@ -33,7 +33,7 @@ inline int router_split(int hidden, bool mfma) {
 
 struct Layout {
   size_t xn, c, qkv, q, kc, vc, o, yf, ys, wr3, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
-      count, offset, tiles, ntiles, z, zs, part, psh, total;
+      count, offset, tiles, ntiles, z, zs, part, psh, rope, total;
 };
 
 // Byte offsets of every workspace buffer for T tokens.  fp32-sized slots are
@@ -71,6 +71,7 @@ Layout layout(const ds4g_layer_cfg& c, int T) {
   L.zs = take((size_t)T * Is * 4);
   L.part = take((size_t)T * k * d * 4);
   L.psh = take(d * 4);
+  L.rope = take((size_t)dh * (((size_t)T + 3) & ~(size_t)3) * 4);   // cos, sin [rd/2][T pad 4]
   L.total = o;
   return L;
 }
@@ -161,9 +162,25 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.A = A; g.lda = lda; g.B = B; g.M = M; g.N = N; g.K = K; g.epi = epi; g.C = C; g.ldc = ldc;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   };
-  // c = A x ; qkv = B c
+  // c = A x ; qkv = B c (prefill on the matrix cores: RoPE in the epilogue,
+  // q / k / v written rotated in bf16, as attention reads them)
   gemm(at<void>(ws, L.xn), d, w.qkv_a, T, r, d, bf ? EPI_BF16 : EPI_F32, at<void>(ws, L.c), r);
-  gemm(at<void>(ws, L.c), r, w.qkv_b, T, qkvd, r, EPI_F32, at<void>(ws, L.qkv), qkvd);
+  const bool rope_epi = bf && !batch;
+  const int tpad = (T + 3) & ~3;
+  if (rope_epi) {
+    float* rc_tab = at<float>(ws, L.rope);
+    rc |= launch_rope_table(ring.pos, T, tpad, rd, c.rope_base, rc_tab, rc_tab + (size_t)(rd / 2) * tpad,
+                            st);
+    GemmArgs g{};
+    g.A = at<void>(ws, L.c); g.lda = r; g.B = w.qkv_b; g.M = T; g.N = qkvd; g.K = r;
+    g.epi = EPI_ROPE_QKV; g.C = at<void>(ws, L.q); g.ldc = qd;
+    g.rope_c = rc_tab; g.rope_s = rc_tab + (size_t)(rd / 2) * tpad; g.rope_ld = tpad;
+    g.rope_dh = dh; g.rope_rd = rd;
+    g.rope_kc = at<uint16_t>(ws, L.kc); g.rope_vc = at<uint16_t>(ws, L.vc);
+    rc |= launch_gemm(g, true, 1, st);
+  } else {
+    gemm(at<void>(ws, L.c), r, w.qkv_b, T, qkvd, r, EPI_F32, at<void>(ws, L.qkv), qkvd);
+  }
 
   // RoPE, attention over the window, ring update (*pos += T)
   AttnArgs aa{};
@@ -172,6 +189,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   aa.kc = at<uint16_t>(ws, L.kc); aa.vc = at<uint16_t>(ws, L.vc);
   aa.ring_k = (uint16_t*)ring.k; aa.ring_v = (uint16_t*)ring.v;
   aa.o = at<void>(ws, L.o); aa.o_bf16 = bf ? 1 : 0; aa.heads_per_block = H < 64 ? H : 64;
+  aa.rope_done = rope_epi ? 1 : 0;
   if (batch)   // RoPE at each sequence's position, its own ring, *pos[b] += 1
     rc |= launch_attention_decode_batch(aa, T, st);
   else

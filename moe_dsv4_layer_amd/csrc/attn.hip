@@ -624,10 +624,32 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   }
 }
 
+// cos / sin of every (pair i, row t) of a prefill, for the RoPE epilogue of
+// the QKV GEMM (angle as in rope_cs: fp64, reduced mod 2 pi)
+__global__ void __launch_bounds__(256)
+rope_table_kernel(const int64_t* __restrict__ pos, int T, int ld, int rd, float base,
+                  float* __restrict__ c, float* __restrict__ s) {
+  const int t = blockIdx.x * 256 + threadIdx.x, i = blockIdx.y;
+  if (t >= ld) return;
+  float cv = 1.f, sv = 0.f;
+  if (t < T) rope_cs(*pos + t, i, rd, base, &cv, &sv);
+  c[(long)i * ld + t] = cv;
+  s[(long)i * ld + t] = sv;
+}
+
+int launch_rope_table(const int64_t* pos, int T, int ld, int rd, float base, float* c, float* s,
+                      hipStream_t st) {
+  if (ld < T || ld % 4 || rd < 2) return -1;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((ld + 255) / 256, rd / 2), dim3(256), 0, st, pos, T,
+                     ld, rd, base, c, s);
+  return 0;
+}
+
 int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   if (a.W > 128 || !a.q_bf16 || !a.o_bf16) return -1;
-  hipLaunchKernelGGL((rope_qkv_kernel<uint16_t>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
-                     a.dh, a.rd, a.base, a.pos, (uint16_t*)a.q, a.kc, a.vc);
+  if (!a.rope_done)   // else the QKV GEMM's epilogue wrote rotated q, kc, vc
+    hipLaunchKernelGGL((rope_qkv_kernel<uint16_t>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
+                       a.dh, a.rd, a.base, a.pos, (uint16_t*)a.q, a.kc, a.vc);
   // spans are aligned to absolute positions: one extra span covers the
   // unknown (device-side) offset of the first position within its span
   const dim3 grid((a.T + 15) / 16 + 1, (a.H + 31) / 32);

@@ -180,6 +180,57 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, const f32x16 (&
                                               int row0, int row1, int col0, int lane) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32);
   const int lr = lane & 31, lg = lane >> 5;
+  if (EPI == EPI_ROPE_QKV) {
+    // the partner of column n in its rotation pair (n ^ 1) is in lane ^ 1:
+    // x0' = x0 c - x1 s (even column), x1' = x0 s + x1 c (odd column).
+    // Two rounded products and a rounded sum, no contraction: every tile
+    // shape rounds a row alike, so prefills split anywhere agree bit for bit.
+#pragma clang fp contract(off)
+    const int dh = g.rope_dh, qd = g.N - 2 * dh, off = dh - g.rope_rd;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = col0 + j * 32 + lr;
+      int e;
+      uint16_t* dst;
+      long ld;
+      if (col < qd) { e = col % dh; dst = static_cast<uint16_t*>(g.C) + col; ld = g.ldc; }
+      else if (col < qd + dh) { e = col - qd; dst = g.rope_kc + e; ld = dh; }
+      else { e = col - qd - dh; dst = g.rope_vc + e; ld = dh; }
+      const bool rot = col < qd + dh && e >= off;
+      const long tab = (long)(rot ? (e - off) >> 1 : 0) * g.rope_ld;
+      const float sgn = (col & 1) ? 1.f : -1.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int rb = row0 + i * 32 + 8 * q4 + 4 * lg;
+          const int rt = min(rb, g.rope_ld - 4);   // rows past the table are not stored
+          // lanes lr, lr ^ 1 share the pair: the even one loads cos, the odd
+          // one sin, and they swap halves
+          const float4 mine = *reinterpret_cast<const float4*>(
+              ((col & 1) ? g.rope_s : g.rope_c) + tab + rt);
+          const float m4[4] = {mine.x, mine.y, mine.z, mine.w};
+          float cv[4], sv[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float other = __int_as_float(
+                __builtin_amdgcn_mov_dpp(__float_as_int(m4[k]), 0xB1, 0xF, 0xF, false));
+            cv[k] = (col & 1) ? other : m4[k];
+            sv[k] = (col & 1) ? m4[k] : other;
+          }
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const float own = acc[i][j][4 * q4 + ii];
+            const float oth = __int_as_float(
+                __builtin_amdgcn_mov_dpp(__float_as_int(own), 0xB1, 0xF, 0xF, false));
+            const float v = rot ? own * cv[ii] + sgn * oth * sv[ii] : own;
+            const int row = rb + ii;
+            if (col < g.N && row < row1) dst[(long)row * ld] = f32_to_bf16(v);
+          }
+        }
+    }
+    return;
+  }
   if (EPI == EPI_RESID) {
     float* C = static_cast<float*>(g.C);
 #pragma unroll
@@ -422,6 +473,10 @@ int launch_dma_cfg(const GemmArgs& g, hipStream_t st) {
     case EPI_SWIGLU_BF16:
       hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_SWIGLU_BF16>), grid, block, 0, st,
                          g);
+      break;
+    case EPI_ROPE_QKV:
+      if (g.tiles || nsplit > 1) return -1;
+      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_ROPE_QKV>), grid, block, 0, st, g);
       break;
     default: return -1;
   }

@@ -11,7 +11,10 @@ enum Epi {
   EPI_BF16 = 1,         // C[r, n] = bf16(acc)
   EPI_RESID = 2,        // C[r, n] += acc                     (fp32)
   EPI_SWIGLU_BF16 = 3,  // C[r, n] = bf16(silu(A.G^T) * (A.U^T))
-  EPI_SWIGLU_F32 = 4    // same, fp32 out
+  EPI_SWIGLU_F32 = 4,   // same, fp32 out
+  // [q | k | v] = A.B^T with RoPE applied to q and k, all rounded to bf16:
+  // q -> C [rows, ldc], k -> rope_kc [rows, dh], v -> rope_vc [rows, dh]
+  EPI_ROPE_QKV = 5
 };
 
 struct GemmArgs {
@@ -34,7 +37,19 @@ struct GemmArgs {
   int ksplit;
   long part_stride;
   int xcd_remap;        // MFMA: renumber tiles so each XCD runs a contiguous run
+  // EPI_ROPE_QKV: cos / sin of pair i at row r in rope_c / rope_s [i * rope_ld + r]
+  // (rope_ld a multiple of 4, >= rows); q columns [0, qd) are heads of dh,
+  // then k, then v; pairs (e, e+1) with e >= dh - rd rotate
+  const float* rope_c;
+  const float* rope_s;
+  int rope_ld, rope_dh, rope_rd;
+  uint16_t* rope_kc;
+  uint16_t* rope_vc;
 };
+// cos / sin of pair i for rows t < T at position *pos + t into c / s
+// [i * ld + t] (rows T..ld-1: 1 and 0), i < rd / 2
+int launch_rope_table(const int64_t* pos, int T, int ld, int rd, float base, float* c, float* s,
+                      hipStream_t st);
 int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st);
 
 // ---------------------------------------------------------------- GEMV
@@ -67,6 +82,7 @@ struct AttnArgs {
   void* o;              // [T, H*dh] attention output
   int o_bf16;
   int heads_per_block;
+  int rope_done;        // MFMA prefill: q, kc, vc already rotated (QKV GEMM epilogue)
 };
 int launch_attention(const AttnArgs& a, hipStream_t st);
 // single-token attention: RoPE of q/k at *pos, write (k, v) to the ring
