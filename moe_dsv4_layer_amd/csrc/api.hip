@@ -20,8 +20,9 @@ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kRouterSplit = 24;
 inline int router_split(int hidden, bool mfma) {
   if (mfma) {
-    // 3 * (hidden / 1024) slices of equal length, each a multiple of 64
-    const int s = (hidden % 1024 == 0 && hidden / 1024 <= 8) ? 3 * (hidden / 1024) : 3;
+    // hidden / 1024 slices of K = 3 * hidden (each a multiple of 64); fixed by
+    // the shape alone, so a token's logits never depend on the batch size
+    const int s = (hidden % 1024 == 0 && hidden / 1024 <= 8) ? hidden / 1024 : 1;
     return s;
   }
   int s = hidden / 512;
@@ -200,9 +201,11 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
 
   // y = RMSNorm(h2) * g2: fp32, and (bf16 weights) its three-term bf16 split,
   // whose first term is bf16(y), the expert GEMMs' input
-  if (bf)
+  if (bf)   // fp32 y only when the caller asks for the router input
     rc |= launch_rmsnorm_rows<uint16_t>(x, T, d, (const uint16_t*)w.ffn_norm, c.rms_eps,
-                                        at<float>(ws, L.yf), nullptr, at<uint16_t>(ws, L.ys), st);
+                                        (routing && routing->router_in) ? at<float>(ws, L.yf)
+                                                                        : nullptr,
+                                        nullptr, at<uint16_t>(ws, L.ys), st);
   else
     rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.ffn_norm, c.rms_eps,
                                      at<float>(ws, L.yf), nullptr, nullptr, st);
