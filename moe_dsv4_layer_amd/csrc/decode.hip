@@ -40,57 +40,6 @@
 namespace ds4g {
 
 // ---------------------------------------------------------------------------
-// Router selection: top-k of the E <= 512 logits (descending, ties to the
-// lower index) and the softmax probabilities of the chosen ones, by one wave
-// with the logits in registers (element lane + 64 i).  Each lane keeps its
-// best remaining element (first maximum in i order, so the lowest index among
-// its equal values); a round takes the wave max of those, then the lowest
-// index among the lanes that hold it, and only the winning lane rescans.
-// This runs before the first routed weight load, so it is kept short: a
-// rolled loop over the k rounds, two DPP reductions each.  Lane 0 writes the
-// choices to sel / wsel (this wave's own LDS slots).
-__device__ __forceinline__ void route_wave(const float (&lg)[8], int E, int k, int* sel,
-                                           float* wsel) {
-  const int lane = threadIdx.x & 63;
-  // a NaN score ranks below every number; a chosen expert becomes NaN, which
-  // neither > nor == selects again.  k < E leaves a candidate every round.
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x = lg[i];
-    v[i] = (lane + 64 * i < E) ? (x == x ? x : -INFINITY) : __builtin_nanf("");
-  }
-  auto best = [&](float& bv, int& bi) {
-    bv = -INFINITY;
-    bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (v[i] > bv || (v[i] == bv && lane + 64 * i < bi)) { bv = v[i]; bi = lane + 64 * i; }
-  };
-  float bv;
-  int bi;
-  best(bv, bi);
-  const float m = wave_max(bv);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
-  s = wave_sum(s);
-#pragma unroll 1
-  for (int r = 0; r < k; ++r) {
-    const float top = (r == 0) ? m : wave_max(bv);
-    const int idx = min(wave_min(bv == top ? bi : 0x7fffffff), E - 1);
-    if (lane == 0) { sel[r] = idx; wsel[r] = expf(top - m) / s; }
-    if (lane == (idx & 63)) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (lane + 64 * i == idx) v[i] = __builtin_nanf("");
-      best(bv, bi);
-    }
-  }
-  wave_lds_sync();
-}
-
-// ---------------------------------------------------------------------------
 // GEMV.  A block is 4 waves that split K in KSPLIT parts and the block's rows
 // in 4/KSPLIT groups; each wave handles RB rows at a time with CPL 8-element
 // chunks per lane per row (K <= KSPLIT*CPL*512).  Blocks stride over row

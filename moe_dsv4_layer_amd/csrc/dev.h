@@ -49,6 +49,19 @@ __device__ __forceinline__ uint4 ldg_nt16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer resource for raw buffer loads from base: no stride, no range check
+// (num_records = -1: the caller bounds every offset, 32-bit bytes).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+  r.z = -1;
+  r.w = 0x00020000;         // raw dword access
+  return r;
+}
+
 // raw 8-element chunk holder for either type
 template <typename WT> struct Chunk8;
 template <> struct Chunk8<uint16_t> {
@@ -161,6 +174,57 @@ __device__ __forceinline__ float block_sum(float v, float* red /*[16]*/) {
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
   __builtin_amdgcn_wave_barrier();
+}
+
+// ----------------------------------------------------------- routing
+// Router selection: top-k of the E <= 512 logits (descending, ties to the
+// lower index) and the softmax probabilities of the chosen ones, by one wave
+// with the logits in registers (element lane + 64 i).  Each lane keeps its
+// best remaining element (first maximum in i order, so the lowest index among
+// its equal values); a round takes the wave max of those, then the lowest
+// index among the lanes that hold it, and only the winning lane rescans.
+// This runs before the first routed weight load, so it is kept short: a
+// rolled loop over the k rounds, two DPP reductions each.  Lane 0 writes the
+// choices to sel / wsel (this wave's own LDS slots).
+__device__ __forceinline__ void route_wave(const float (&lg)[8], int E, int k, int* sel,
+                                           float* wsel) {
+  const int lane = threadIdx.x & 63;
+  // a NaN score ranks below every number; a chosen expert becomes NaN, which
+  // neither > nor == selects again.  k < E leaves a candidate every round.
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x = lg[i];
+    v[i] = (lane + 64 * i < E) ? (x == x ? x : -INFINITY) : __builtin_nanf("");
+  }
+  auto best = [&](float& bv, int& bi) {
+    bv = -INFINITY;
+    bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (v[i] > bv || (v[i] == bv && lane + 64 * i < bi)) { bv = v[i]; bi = lane + 64 * i; }
+  };
+  float bv;
+  int bi;
+  best(bv, bi);
+  const float m = wave_max(bv);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
+  s = wave_sum(s);
+#pragma unroll 1
+  for (int r = 0; r < k; ++r) {
+    const float top = (r == 0) ? m : wave_max(bv);
+    const int idx = min(wave_min(bv == top ? bi : 0x7fffffff), E - 1);
+    if (lane == 0) { sel[r] = idx; wsel[r] = expf(top - m) / s; }
+    if (lane == (idx & 63)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (lane + 64 * i == idx) v[i] = __builtin_nanf("");
+      best(bv, bi);
+    }
+  }
+  wave_lds_sync();
 }
 
 // RoPE angle of pair i (of rd rotated dims) at position p: theta =

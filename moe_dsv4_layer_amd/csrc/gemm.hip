@@ -285,17 +285,6 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, const f32x16 (&
 // multiplied.  The loads are issued from inline assembly and counted with
 // explicit vmcnt waits: the compiler's own LDS-DMA tracking would wait for
 // every outstanding load before any LDS read, which defeats the pipeline.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
-  r.z = -1;                 // num_records: offsets are bounded by the caller (32-bit)
-  r.w = 0x00020000;         // raw dword access
-  return r;
-}
 __device__ __forceinline__ void dma16(i32x4_t rs, uint32_t lds_byte, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_byte), "v"(voff), "s"(rs) : "memory");
