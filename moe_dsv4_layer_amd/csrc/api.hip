@@ -18,6 +18,20 @@ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 // vector ALUs; bf16 weights: K = 3 * hidden (the three-term bf16 split of y)
 // on the matrix cores.
 constexpr int kRouterSplit = 24;
+constexpr int kBatchRouterSplit = 12;   // batched decode (<= kRouterSplit)
+
+// Batched decode (a few rows per GEMM): split K so that a dense GEMM runs
+// ~256 blocks instead of one per N tile.  A power of two dividing K / 64, at
+// most 64; 1 beyond 256 rows or on the fp32-weight path.  The tile shapes
+// follow launch_gemm (64 x 256 up to 64 rows, else 128 x 128).
+inline int batch_split(int M, int N, int K, bool mfma) {
+  if (!mfma || M > 256) return 1;
+  const long bm = M <= 64 ? 64 : 128, bn = M <= 64 ? 256 : 128;
+  const long tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  int s = 1;
+  while (s < 64 && tiles * s * 2 <= 256 && K % (64 * s * 2) == 0) s *= 2;
+  return s;
+}
 inline int router_split(int hidden, bool mfma) {
   if (mfma) {
     // hidden / 1024 slices of K = 3 * hidden (each a multiple of 64); fixed by
@@ -34,7 +48,7 @@ inline int router_split(int hidden, bool mfma) {
 
 struct Layout {
   size_t xn, c, qkv, q, kc, vc, o, yf, ys, wr3, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
-      count, offset, tiles, ntiles, z, zs, part, psh, rope, total;
+      count, offset, tiles, ntiles, z, zs, part, psh, skp, rope, total;
 };
 
 // Byte offsets of every workspace buffer for T tokens.  fp32-sized slots are
@@ -72,6 +86,15 @@ Layout layout(const ds4g_layer_cfg& c, int T) {
   L.zs = take((size_t)T * Is * 4);
   L.part = take((size_t)T * k * d * 4);
   L.psh = take(d * 4);
+  {   // split-K partial sums of the batched decode's dense GEMMs
+    const bool mfma = c.wdtype == DS4G_BF16;
+    size_t m = 0;
+    auto need = [&](int N, int K, int parts) {
+      m = std::max(m, (size_t)batch_split(T, N, K, mfma) * T * N * 4 * parts);
+    };
+    need(r, d, 1); need((int)qkvd, r, 1); need(d, (int)qd, 1); need(Is, d, 2); need(d, Is, 1);
+    L.skp = take(T <= 256 ? m : 0);
+  }
   L.rope = take((size_t)dh * (((size_t)T + 3) & ~(size_t)3) * 4);   // cos, sin [rd/2][T pad 4]
   L.total = o;
   return L;
@@ -157,10 +180,30 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.attn_norm, c.rms_eps,
                                      at<float>(ws, L.xn), nullptr, nullptr, st);
 
+  // dense GEMM; batched decode splits K (fp32 partials, then a reduce that
+  // applies the epilogue).  B2: the up projection of a SwiGLU pair.
   auto gemm = [&](const void* A, int lda, const void* B, int M, int N, int K, int epi, void* C,
-                  int ldc) {
+                  int ldc, const void* B2 = nullptr) {
+    const int s = batch ? batch_split(M, N, K, bf) : 1;
+    if (s > 1) {
+      float* part = at<float>(ws, L.skp);
+      const long ps = (long)M * N;
+      GemmArgs g{};
+      g.A = A; g.lda = lda; g.M = M; g.N = N; g.K = K; g.epi = EPI_F32; g.ldc = N;
+      g.ksplit = s; g.part_stride = ps;
+      g.B = B; g.C = part;
+      rc |= launch_gemm(g, bf, 1, st);
+      if (B2) {
+        g.B = B2; g.C = part + (size_t)s * ps;
+        rc |= launch_gemm(g, bf, 1, st);
+      }
+      rc |= launch_splitk_reduce(part, B2 ? part + (size_t)s * ps : nullptr, s, ps, M, N, epi, C,
+                                 ldc, st);
+      return;
+    }
     GemmArgs g{};
-    g.A = A; g.lda = lda; g.B = B; g.M = M; g.N = N; g.K = K; g.epi = epi; g.C = C; g.ldc = ldc;
+    g.A = A; g.lda = lda; g.B = B; g.B2 = B2; g.M = M; g.N = N; g.K = K; g.epi = epi; g.C = C;
+    g.ldc = ldc;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   };
   // c = A x ; qkv = B c (prefill on the matrix cores: RoPE in the epilogue,
@@ -214,7 +257,10 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   // bf16 weights: y1|y2|y3 against [W_r|W_r|W_r] on the matrix cores; fp32
   // weights: fp32 y on the vector ALUs.  Split-K partial sums, added in split
   // order by the top-k kernel.
-  const int rsplit = router_split(d, bf);
+  // batched decode: more slices for more blocks (a function of the shape)
+  const int rsplit = (batch && bf && (3 * d) % (64 * kBatchRouterSplit) == 0)
+                         ? kBatchRouterSplit
+                         : router_split(d, bf);
   {
     GemmArgs g{};
     g.M = T; g.N = E; g.epi = EPI_F32; g.C = at<void>(ws, L.lpart); g.ldc = E;
@@ -256,12 +302,8 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
   // shared gate/up + SwiGLU over every token
-  {
-    GemmArgs g{};
-    g.A = yA; g.lda = ylda; g.B = w.sh_gate; g.B2 = w.sh_up; g.M = T; g.N = Is; g.K = d;
-    g.epi = bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32; g.C = at<void>(ws, L.zs); g.ldc = Is;
-    rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
-  }
+  gemm(yA, ylda, w.sh_gate, T, Is, d, bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32, at<void>(ws, L.zs),
+       Is, w.sh_up);
   // routed down projections -> part (permuted rows; bf16 on the MFMA path,
   // fp32 on the fp32-weight path), combined in fp32 below
   {
@@ -274,12 +316,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
   // shared down (x = h2 + shared), then combine: x += sum_j w_j part_j
-  {
-    GemmArgs g{};
-    g.A = at<void>(ws, L.zs); g.lda = Is; g.B = w.sh_down; g.M = T; g.N = d; g.K = Is;
-    g.epi = EPI_RESID; g.C = x; g.ldc = d;
-    rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
-  }
+  gemm(at<void>(ws, L.zs), Is, w.sh_down, T, d, Is, EPI_RESID, x, d);
   rc |= launch_moe_combine(x, at<void>(ws, L.part), bf ? 1 : 0, ra.pos_of, ra.topk_w, T, d, k, st);
   if (routing) {
     copy_out(routing->topk_idx, ra.topk_idx, (size_t)T * k * 4, st);

@@ -472,6 +472,59 @@ int launch_dma_cfg(const GemmArgs& g, hipStream_t st) {
   return 0;
 }
 
+// Split-K partial sums part[s][m][n] (s < nsplit, stride pstride), then the
+// epilogue: F32, BF16, RESID (C += sum) or SWIGLU_BF16 (C = bf16(silu(sum
+// part) * sum part2)).  A block takes 32 consecutive elements; its 8 groups of
+// 32 threads add the splits g, g + 8, ... of their element, and the 8 group
+// sums are added in group order (a fixed order: results do not depend on
+// timing).  Spreading the splits over threads keeps many loads in flight.
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ part, const float* __restrict__ part2, int nsplit,
+                     long pstride, int M, int N, int epi, void* C, int ldc) {
+  __shared__ float acc[2][8][32];
+  const int e = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const long i = (long)blockIdx.x * 32 + e;
+  const bool live = i < (long)M * N;
+  float v = 0.f, u = 0.f;
+  if (live) {
+#pragma unroll 4
+    for (int s = g; s < nsplit; s += 8) v += part[s * pstride + i];
+    if (epi == EPI_SWIGLU_BF16) {
+#pragma unroll 4
+      for (int s = g; s < nsplit; s += 8) u += part2[s * pstride + i];
+    }
+  }
+  acc[0][g][e] = v;
+  acc[1][g][e] = u;
+  __syncthreads();
+  if (g != 0 || !live) return;
+  v = 0.f;
+  u = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) { v += acc[0][q][e]; u += acc[1][q][e]; }
+  const int m = (int)(i / N), n = (int)(i - (long)m * N);
+  if (epi == EPI_SWIGLU_BF16) {
+    static_cast<uint16_t*>(C)[(long)m * ldc + n] = f32_to_bf16(silu(v) * u);
+  } else if (epi == EPI_BF16) {
+    static_cast<uint16_t*>(C)[(long)m * ldc + n] = f32_to_bf16(v);
+  } else if (epi == EPI_RESID) {
+    float* c = static_cast<float*>(C) + (long)m * ldc + n;
+    *c = *c + v;
+  } else {
+    static_cast<float*>(C)[(long)m * ldc + n] = v;
+  }
+}
+
+int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long pstride, int M,
+                         int N, int epi, void* C, int ldc, hipStream_t st) {
+  if (epi != EPI_F32 && epi != EPI_BF16 && epi != EPI_RESID && epi != EPI_SWIGLU_BF16) return -1;
+  if (epi == EPI_SWIGLU_BF16 && !part2) return -1;
+  const long n = (long)M * N;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, st,
+                     part, part2, nsplit, pstride, M, N, epi, C, ldc);
+  return 0;
+}
+
 int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
   const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
   if (mfma) {

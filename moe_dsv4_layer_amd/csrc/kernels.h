@@ -51,6 +51,11 @@ struct GemmArgs {
 int launch_rope_table(const int64_t* pos, int T, int ld, int rd, float base, float* c, float* s,
                       hipStream_t st);
 int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st);
+// sum of nsplit fp32 partials part[s * pstride + m * N + n] in split order,
+// then the epilogue epi (F32, BF16, RESID: C += sum, SWIGLU_BF16: part2 holds
+// the up projection's partials) into C [M, ldc]
+int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long pstride, int M,
+                         int N, int epi, void* C, int ldc, hipStream_t st);
 
 // ---------------------------------------------------------------- GEMV
 // out[n] (= or +=) sum_k W[n, k] xs[k], xs = x or RMSNorm(x) * gamma.
