@@ -22,6 +22,11 @@ constexpr int SEG = 1024;          // entries per segment / per block
 constexpr int NB1 = 16384;         // level-1 buckets (q <= 1 => key1 <= 0x3F80)
 constexpr int NB2 = 65536;         // level-2 buckets
 constexpr double FX = 35184372088832.0;   // 2^45
+// level-1 keys below KLO (q < 2^-45, exponent field < 82) have no fixed-point
+// mass: fx(q) = 0 there, so their histogram entries stay zero
+constexpr int KLO = 82 << 7;
+constexpr int NKEY = 0x3F80 + 1 - KLO;   // keys KLO..0x3F80 (q <= 1)
+constexpr int QSEGS = 4;                 // segments per samp_q block
 
 __device__ __forceinline__ uint64_t fx(float q) { return (uint64_t)((double)q * FX); }
 
@@ -150,30 +155,45 @@ samp_argmax_kernel(int nb, SampWs w, int* token, float temperature, const float*
   if (threadIdx.x == 0) *token = mi;
 }
 
-__device__ __forceinline__ float global_max(const SampWs& w, int nb) {
+// the largest logit, from the segment maxima (block-wide: every thread;
+// red holds one float per wave)
+__device__ __forceinline__ float global_max(const SampWs& w, int nb, float* red) {
   float m = -INFINITY;
-  for (int b = 0; b < nb; ++b) m = fmaxf(m, w.bmax[b]);
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) m = fmaxf(m, w.bmax[b]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = fmaxf(m, red[i]);
   return m;
 }
 
-// S2: q = exp((l - M) / T); level-1 histogram of fixed-point mass.
-__global__ void __launch_bounds__(256)
-samp_q_kernel(const float* __restrict__ logits, int V, float temperature, const float* tdev,
-              SampWs w) {
+// S2: q = exp((l - M) / T); level-1 histogram of fixed-point mass.  A block
+// of 1024 takes QSEGS segments and sums their masses per key in LDS first, so
+// that equal keys (a narrow logit spread puts thousands of weights in one
+// key) cost one global atomic per block instead of one per entry.
+__global__ void __launch_bounds__(1024)
+samp_q_kernel(const float* __restrict__ logits, int V, int nb, float temperature,
+              const float* tdev, SampWs w) {
   if (!sampling(temperature, tdev)) return;
   if (tdev) temperature = *tdev;
-  __shared__ float Ms;
-  const int nb = gridDim.x;
-  if (threadIdx.x == 0) Ms = global_max(w, nb);
-  __syncthreads();
-  const float M = Ms;
+  __shared__ unsigned long long hist[NKEY];
+  __shared__ float red[16];
+  for (int k = threadIdx.x; k < NKEY; k += blockDim.x) hist[k] = 0;
+  const float M = global_max(w, nb, red);   // ends in a barrier: hist is clear
   if (blockIdx.x == 0 && threadIdx.x == 0) w.st->M = M;
-  for (int i = blockIdx.x * SEG + threadIdx.x; i < min(V, (blockIdx.x + 1) * SEG); i += 256) {
+  const int lo = blockIdx.x * QSEGS * SEG, hi = min(V, lo + QSEGS * SEG);
+  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
     float q = expf((logits[i] - M) / temperature);
-    q = (q == q) ? fminf(q, 1.f) : 0.f;   // a NaN logit weighs nothing; keys stay < NB1
+    q = (q == q) ? fminf(q, 1.f) : 0.f;   // a NaN logit weighs nothing; keys stay <= 0x3F80
     w.q[i] = q;
-    const uint32_t key = __float_as_uint(q) >> 16;
-    atomicAdd(&w.h1[key], (unsigned long long)fx(q));
+    const int key = (int)(__float_as_uint(q) >> 16) - KLO;
+    if (key >= 0) atomicAdd(&hist[key], (unsigned long long)fx(q));
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < NKEY; k += blockDim.x) {
+    const unsigned long long v = hist[k];
+    if (v) atomicAdd(&w.h1[KLO + k], v);
   }
 }
 
@@ -270,33 +290,60 @@ samp_level2_kernel(SampWs w, uint64_t* rng, float min_p, float temperature, cons
     return;
   }
   constexpr int PER = NB2 / 1024;
+  // thread t owns descending positions [t*PER, (t+1)*PER): buckets
+  // NB2-1-t*PER down to NB2-PER-t*PER, contiguous in memory; vector loads
+  const unsigned long long* hb = w.h2 + (NB2 - PER - threadIdx.x * PER);
   unsigned long long s = 0;
-  for (int j = 0; j < PER; ++j) s += w.h2[NB2 - 1 - (threadIdx.x * PER + j)];
+#pragma unroll
+  for (int j = 0; j < PER; j += 2) {
+    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(hb + j);
+    s += v.x + v.y;
+  }
   const unsigned long long inc = block_incl_scan_u64(s, red);
   const double target = st->target;
   const unsigned long long a1 = st->above1;
-  unsigned long long run = a1 + inc - s;
-  for (int j = 0; j < PER; ++j) {
-    const unsigned long long nxt = run + w.h2[NB2 - 1 - (threadIdx.x * PER + j)];
-    if ((double)run < target && (double)nxt >= target) {
-      const uint32_t b2 = NB2 - 1 - (threadIdx.x * PER + j);
-      const uint32_t vbits = (st->b1 << 16) | b2;
-      const unsigned long long qf = fx(__uint_as_float(vbits));
-      const unsigned int cnt = w.c2[b2];
-      // smallest m >= 1 with run + m*qf >= target
-      long long mm = (long long)ceil((target - (double)run) / (double)qf);
-      if (mm < 1) mm = 1;
-      if (mm > (long long)cnt) mm = cnt;
-      while (mm > 1 && (double)(run + (unsigned long long)(mm - 1) * qf) >= target) --mm;
-      while (mm < (long long)cnt && (double)(run + (unsigned long long)mm * qf) < target) ++mm;
-      st->vstar = vbits;
-      st->m = (int)mm;
-      st->above = run;
-      apply_min_p(st, min_p);
-      const uint64_t z = splitmix64_next(rng);
-      st->u = (double)(z >> 40) * (1.0 / 16777216.0);
+  // the thread whose range holds the crossing (the cumulative mass is
+  // non-decreasing and level 1 put the target inside bucket b1)
+  __shared__ int owner;
+  __shared__ unsigned long long owner_run;
+  if (threadIdx.x == 0) owner = -1;
+  __syncthreads();
+  {
+    const unsigned long long run0 = a1 + inc - s;
+    if ((double)run0 < target && (double)(run0 + s) >= target) {
+      owner = threadIdx.x;
+      owner_run = run0;
     }
-    run = nxt;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64 || owner < 0) return;
+  // one wave: lane j takes the owner's position j (descending), prefix sums
+  const int lane = threadIdx.x;
+  const uint32_t b2 = NB2 - 1 - (owner * PER + lane);
+  const unsigned long long hv = w.h2[b2];
+  unsigned long long cum = hv;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long y = __shfl_up(cum, o, 64);
+    if (lane >= o) cum += y;
+  }
+  const unsigned long long run = owner_run + cum - hv;    // mass before position lane
+  if ((double)run < target && (double)(run + hv) >= target) {
+    const uint32_t vbits = (st->b1 << 16) | b2;
+    const unsigned long long qf = fx(__uint_as_float(vbits));
+    const unsigned int cnt = w.c2[b2];
+    // smallest m >= 1 with run + m*qf >= target
+    long long mm = (long long)ceil((target - (double)run) / (double)qf);
+    if (mm < 1) mm = 1;
+    if (mm > (long long)cnt) mm = cnt;
+    while (mm > 1 && (double)(run + (unsigned long long)(mm - 1) * qf) >= target) --mm;
+    while (mm < (long long)cnt && (double)(run + (unsigned long long)mm * qf) < target) ++mm;
+    st->vstar = vbits;
+    st->m = (int)mm;
+    st->above = run;
+    apply_min_p(st, min_p);
+    const uint64_t z = splitmix64_next(rng);
+    st->u = (double)(z >> 40) * (1.0 / 16777216.0);
   }
 }
 
@@ -435,7 +482,8 @@ int launch_sample(const SampleArgs& s, hipStream_t st) {
   if (td || !(T > 0.f))
     hipLaunchKernelGGL(samp_argmax_kernel, dim3(1), dim3(64), 0, st, nb, w, s.token, T, td);
   if (!td && !(T > 0.f)) return 0;
-  hipLaunchKernelGGL(samp_q_kernel, dim3(nb), dim3(256), 0, st, s.logits, s.V, T, td, w);
+  hipLaunchKernelGGL(samp_q_kernel, dim3((nb + QSEGS - 1) / QSEGS), dim3(1024), 0, st, s.logits,
+                     s.V, nb, T, td, w);
   hipLaunchKernelGGL(samp_level1_kernel, dim3(1), dim3(1024), 0, st, s.top_p, w, T, td);
   hipLaunchKernelGGL(samp_hist2_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
   hipLaunchKernelGGL(samp_level2_kernel, dim3(1), dim3(1024), 0, st, w, s.rng, s.min_p, T, td);
