@@ -541,7 +541,30 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
     }
     const long nout = dual ? g.N * 2L : g.N;           // B rows per output row
     const long big_blocks = ((g.M + 255) / 256) * ((nout + 255) / 256) * nsplit;
-    if (big_blocks >= 512) return launch_dma_cfg<256, 256, 2, 4, 2>(g, st);
+    if (big_blocks >= 512) {
+      // Rows past the last whole round of 256x256 tiles (one per CU) run as
+      // 128x128 tiles, a quarter of the work each, when they would fill less
+      // than half of one more round of big tiles.  Every element keeps its K
+      // order, so the split changes no bit of the result.
+      const long nt = (nout + 255) / 256, mt = (g.M + 255) / 256;
+      const long rem = (mt * nt) % 256;
+      const int mb = (int)((mt * nt / 256) * 256 / nt) * 256;   // rows in whole rounds
+      if (nsplit == 1 && g.epi != EPI_ROPE_QKV && rem > 0 && rem <= 128 && mb > 0 && mb < g.M) {
+        GemmArgs hi = g, lo = g;
+        hi.M = mb;
+        lo.M = g.M - mb;
+        if (g.gather) lo.gather = g.gather + mb;
+        else lo.A = static_cast<const uint16_t*>(g.A) + (long)mb * g.lda;
+        const size_t es = (g.epi == EPI_BF16 || g.epi == EPI_SWIGLU_BF16) ? 2 : 4;
+        lo.C = static_cast<char*>(g.C) + (size_t)mb * g.ldc * es;
+        const int r = launch_dma_cfg<256, 256, 2, 4, 2>(hi, st);
+        if (r) return r;
+        const long lblocks = ((lo.M + 127) / 128) * ((nout + 127) / 128);
+        if (lblocks <= 256) return launch_dma_cfg<128, 128, 2, 2, 3>(lo, st);
+        return launch_dma_cfg<128, 128, 2, 2, 2>(lo, st);
+      }
+      return launch_dma_cfg<256, 256, 2, 4, 2>(g, st);
+    }
     if (g.M <= 64) return launch_dma_cfg<64, 256, 1, 4, 3>(g, st);
     const long blocks = ((g.M + 127) / 128) * ((nout + 127) / 128) * nsplit;
     // one block per CU either way: spend the LDS on a deeper pipeline
