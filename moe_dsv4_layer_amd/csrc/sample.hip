@@ -46,6 +46,7 @@ struct SampState {
 struct SampWs {
   float* bmax; int* barg; float* q;
   unsigned long long* h1; unsigned long long* h2; unsigned int* c2;
+  unsigned long long* g2;   // level-2 mass per group of 1024 descending positions
   unsigned long long* seg_gt; int* seg_gtn; int* seg_tie;
   SampState* st;
 };
@@ -63,6 +64,7 @@ __host__ __device__ inline SampWs carve(void* base, int V) {
   w.h1 = (unsigned long long*)(p + o); o = align256(o + NB1 * 8);
   w.h2 = (unsigned long long*)(p + o); o = align256(o + NB2 * 8);
   w.c2 = (unsigned int*)(p + o); o = align256(o + NB2 * 4);
+  w.g2 = (unsigned long long*)(p + o); o = align256(o + (NB2 / 1024) * 8);
   w.seg_gt = (unsigned long long*)(p + o); o = align256(o + nb * 8);
   w.seg_gtn = (int*)(p + o); o = align256(o + nb * 4);
   w.seg_tie = (int*)(p + o); o = align256(o + nb * 4);
@@ -78,6 +80,7 @@ size_t carve_bytes(int V) {
   o = align256(o + NB1 * 8);
   o = align256(o + NB2 * 8);
   o = align256(o + NB2 * 4);
+  o = align256(o + (NB2 / 1024) * 8);
   o = align256(o + nb * 8);
   o = align256(o + nb * 4);
   o = align256(o + nb * 4);
@@ -271,6 +274,23 @@ __device__ __forceinline__ void apply_min_p(SampState* st, float min_p) {
   }
 }
 
+// S5a: level-2 mass per group of 1024 descending positions (group g: buckets
+// NB2-1-1024g down to NB2-1024-1024g, contiguous), one block per group.
+__global__ void __launch_bounds__(256)
+samp_l2sum_kernel(SampWs w, float temperature, const float* tdev) {
+  if (!sampling(temperature, tdev) || w.st->all) return;
+  __shared__ unsigned long long ws[4];
+  const unsigned long long* hb = w.h2 + (NB2 - 1024 - blockIdx.x * 1024) + threadIdx.x * 4;
+  const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(hb);
+  const ulonglong2 b = *reinterpret_cast<const ulonglong2*>(hb + 2);
+  unsigned long long s = a.x + a.y + b.x + b.y;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) w.g2[blockIdx.x] = ws[0] + ws[1] + ws[2] + ws[3];
+}
+
 // S5 (one block of 1024): exact cut weight q*, how many equal-to-q* entries
 // are kept (top-p, then min-p), and the generator draw u.
 __global__ void __launch_bounds__(1024)
@@ -289,45 +309,36 @@ samp_level2_kernel(SampWs w, uint64_t* rng, float min_p, float temperature, cons
     }
     return;
   }
-  constexpr int PER = NB2 / 1024;
-  // thread t owns descending positions [t*PER, (t+1)*PER): buckets
-  // NB2-1-t*PER down to NB2-PER-t*PER, contiguous in memory; vector loads
-  const unsigned long long* hb = w.h2 + (NB2 - PER - threadIdx.x * PER);
-  unsigned long long s = 0;
-#pragma unroll
-  for (int j = 0; j < PER; j += 2) {
-    const ulonglong2 v = *reinterpret_cast<const ulonglong2*>(hb + j);
-    s += v.x + v.y;
-  }
-  const unsigned long long inc = block_incl_scan_u64(s, red);
   const double target = st->target;
   const unsigned long long a1 = st->above1;
-  // the thread whose range holds the crossing (the cumulative mass is
-  // non-decreasing and level 1 put the target inside bucket b1)
-  __shared__ int owner;
-  __shared__ unsigned long long owner_run;
-  if (threadIdx.x == 0) owner = -1;
+  // the group of 1024 positions that holds the crossing (the cumulative mass
+  // is non-decreasing and level 1 put the target inside bucket b1): wave 0
+  // scans the 64 group sums
+  __shared__ int grp;
+  __shared__ unsigned long long grun;
+  if (threadIdx.x == 0) grp = -1;
   __syncthreads();
-  {
-    const unsigned long long run0 = a1 + inc - s;
-    if ((double)run0 < target && (double)(run0 + s) >= target) {
-      owner = threadIdx.x;
-      owner_run = run0;
+  if (threadIdx.x < NB2 / 1024) {
+    const int lane = threadIdx.x;
+    const unsigned long long gs = w.g2[lane];
+    unsigned long long cum = gs;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long y = __shfl_up(cum, o, 64);
+      if (lane >= o) cum += y;
+    }
+    const unsigned long long run0 = a1 + cum - gs;
+    if ((double)run0 < target && (double)(run0 + gs) >= target) {
+      grp = lane;
+      grun = run0;
     }
   }
   __syncthreads();
-  if (threadIdx.x >= 64 || owner < 0) return;
-  // one wave: lane j takes the owner's position j (descending), prefix sums
-  const int lane = threadIdx.x;
-  const uint32_t b2 = NB2 - 1 - (owner * PER + lane);
+  if (grp < 0) return;
+  // the group's positions, one per thread (descending), prefix-summed
+  const uint32_t b2 = NB2 - 1 - (grp * 1024 + threadIdx.x);
   const unsigned long long hv = w.h2[b2];
-  unsigned long long cum = hv;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long y = __shfl_up(cum, o, 64);
-    if (lane >= o) cum += y;
-  }
-  const unsigned long long run = owner_run + cum - hv;    // mass before position lane
+  const unsigned long long run = grun + block_incl_scan_u64(hv, red) - hv;   // mass before b2
   if ((double)run < target && (double)(run + hv) >= target) {
     const uint32_t vbits = (st->b1 << 16) | b2;
     const unsigned long long qf = fx(__uint_as_float(vbits));
@@ -486,6 +497,7 @@ int launch_sample(const SampleArgs& s, hipStream_t st) {
                      s.V, nb, T, td, w);
   hipLaunchKernelGGL(samp_level1_kernel, dim3(1), dim3(1024), 0, st, s.top_p, w, T, td);
   hipLaunchKernelGGL(samp_hist2_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
+  hipLaunchKernelGGL(samp_l2sum_kernel, dim3(NB2 / 1024), dim3(256), 0, st, w, T, td);
   hipLaunchKernelGGL(samp_level2_kernel, dim3(1), dim3(1024), 0, st, w, s.rng, s.min_p, T, td);
   hipLaunchKernelGGL(samp_segsum_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
   hipLaunchKernelGGL(samp_pick_kernel, dim3(1), dim3(1024), 0, st, s.V, nb, w, s.token, T, td);
