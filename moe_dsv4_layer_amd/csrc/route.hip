@@ -183,31 +183,43 @@ __device__ int block_excl_scan(int* a, int n, int* wsum /*[4]*/) {
 }
 
 // ------------------------------------------------------------ expert ranks
-// Block e walks the tokens in order; a token that chose e gets the number of
-// earlier tokens that chose e (a ballot prefix count); count[e] = total.
-__global__ void __launch_bounds__(256)
+// Block e walks the tokens in order, 1024 at a time; a token that chose e
+// gets the number of earlier tokens that chose e (a ballot prefix count);
+// count[e] = total.  The next chunk's expert ids are loaded before the
+// current chunk is counted, and the per-wave counts alternate between two LDS
+// rows, so each chunk costs one barrier.
+__global__ void __launch_bounds__(1024)
 expert_rank_kernel(const int* __restrict__ idx, int T, int k, int* __restrict__ rank,
                    int* __restrict__ count) {
-  __shared__ int wsum[4];
+  __shared__ int wsum[2][16];
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int nv[8];
+  auto load = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) nv[j] = (t < T && j < k) ? idx[(long)t * k + j] : -1;
+  };
+  load(threadIdx.x);
   int base = 0;
-  for (int t0 = 0; t0 < T; t0 += 256) {
-    const int t = t0 + threadIdx.x;
+  for (int t0 = 0, it = 0; t0 < T; t0 += 1024, ++it) {
     int slot = -1;
-    if (t < T) {
-      for (int j = 0; j < k; ++j)
-        if (idx[(long)t * k + j] == e) slot = j;
-    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (nv[j] == e) slot = j;
+    if (t0 + 1024 < T) load(t0 + 1024 + threadIdx.x);
     const unsigned long long b = __ballot(slot >= 0);
     const int before = __popcll(b & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[it & 1][wid] = __popcll(b);
     __syncthreads();
-    if (lane == 0) wsum[wid] = __popcll(b);
-    __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wid; ++w) wbase += wsum[w];
-    if (slot >= 0) rank[(long)t * k + slot] = base + wbase + before;
-    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    int wbase = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int c = wsum[it & 1][w];
+      wbase += (w < wid) ? c : 0;
+      tot += c;
+    }
+    if (slot >= 0) rank[(long)(t0 + threadIdx.x) * k + slot] = base + wbase + before;
+    base += tot;
   }
   if (threadIdx.x == 0) count[e] = base;
 }
@@ -256,7 +268,7 @@ int launch_route(const RouteArgs& r, hipStream_t st) {
   if (r.E > 512 || r.k > 8) return -1;
   hipLaunchKernelGGL(topk_kernel, dim3((r.T + 3) / 4), dim3(256), 0, st, r.logits, r.nsplit,
                      r.logits_sum, r.T, r.E, r.k, r.topk_idx, r.topk_w);
-  hipLaunchKernelGGL(expert_rank_kernel, dim3(r.E), dim3(256), 0, st, r.topk_idx, r.T, r.k,
+  hipLaunchKernelGGL(expert_rank_kernel, dim3(r.E), dim3(1024), 0, st, r.topk_idx, r.T, r.k,
                      r.rank, r.count);
   const int nent = r.T * r.k;
   hipLaunchKernelGGL(route_scatter_kernel, dim3((nent + 255) / 256), dim3(256), 0, st, r);
