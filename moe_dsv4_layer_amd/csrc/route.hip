@@ -102,15 +102,34 @@ topk_kernel(const float* __restrict__ logits, int nsplit, float* __restrict__ ls
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // the partial sums of all 8 experts of a lane, 4 splits at a time, are
+  // loaded before any is added; the adds run in split order
   float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int z0 = 0; z0 < nsplit; z0 += 4) {
+    float p[4][8];
+#pragma unroll
+    for (int zz = 0; zz < 4; ++zz)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = lane + 64 * i;
+        p[zz][i] = (z0 + zz < nsplit && e < E) ? logits[((long)(z0 + zz) * T + t) * E + e] : 0.f;
+      }
+#pragma unroll
+    for (int zz = 0; zz < 4; ++zz)
+      if (z0 + zz < nsplit) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] += p[zz][i];
+      }
+  }
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int e = lane + 64 * i;
     float a = -INFINITY;
     if (e < E) {
-      a = 0.f;
-      for (int z = 0; z < nsplit; ++z) a += logits[((long)z * T + t) * E + e];
+      a = v[i];
       lsum[(long)t * E + e] = a;
       if (a != a) a = -INFINITY;   // a NaN score ranks below every number
     }
