@@ -239,6 +239,19 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
   __shared__ float red[KG][DH];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int h = blockIdx.x;
+  const int qd = H * DH;
+  // the token's q (this head), k and v need no position: load them first
+  // (pairs: tid < DH/2 -> q, DH/2 <= tid < DH -> k, DH <= tid < 2 DH -> v)
+  float ta = 0.f, tb = 0.f;
+  if (tid < DH) {
+    const bool isq = tid < DH / 2;
+    const int e0 = 2 * (isq ? tid : tid - DH / 2);
+    const float* src = isq ? qkv + (long)h * DH : qkv + qd;
+    ta = src[e0];
+    tb = src[e0 + 1];
+  } else if (tid < 2 * DH) {
+    ta = qkv[qd + DH + (tid - DH)];
+  }
   const long p = *pos;
   const long lo = p - W + 1 > 0 ? p - W + 1 : 0;
   const int n = (int)(p - lo + 1);                 // window keys; the token is key n-1
@@ -267,12 +280,10 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
   const int off = DH - rd;
   for (int i = tid; i < rd / 2; i += 256) rope_cs(p, i, rd, base, &cs[i], &sn[i]);
   __syncthreads();
-  const int qd = H * DH;
   if (tid < DH) {   // pairs: tid < DH/2 -> q, else -> k
     const bool isq = tid < DH / 2;
     const int e0 = 2 * (isq ? tid : tid - DH / 2);
-    const float* src = isq ? qkv + (long)h * DH : qkv + qd;
-    float a = src[e0], b = src[e0 + 1];
+    float a = ta, b = tb;
     if (e0 >= off) {
       const int i = (e0 - off) / 2;
       const float c = cs[i], s = sn[i];
@@ -282,8 +293,7 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
     if (isq) { qs[e0] = a; qs[e0 + 1] = b; }
     else { kself[e0] = f32_to_bf16(a); kself[e0 + 1] = f32_to_bf16(b); }
   } else if (tid < 2 * DH) {
-    const int e = tid - DH;
-    vself[e] = f32_to_bf16(qkv[qd + DH + e]);
+    vself[tid - DH] = f32_to_bf16(ta);
   }
   __syncthreads();
   if (h == 0) {
