@@ -534,7 +534,10 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
     // byte offsets of the direct loads are 32-bit
     if ((double)g.N * g.K * 2 >= 4294967296.0) return -1;
     if (g.tiles) {   // the tile list was built for exactly rows_hint rows per tile
-      if (g.rows_hint == 64) return launch_dma_cfg<64, 256, 1, 4, 3>(g, st);
+      // 64-row tiles (few rows per expert: a 2048-token prefill, batched
+      // decode): 128 columns per tile, so small calls have more blocks to
+      // spread over the CUs and two blocks fit a CU's LDS
+      if (g.rows_hint == 64) return launch_dma_cfg<64, 128, 2, 2, 3>(g, st);
       if (g.rows_hint == 128) return launch_dma_cfg<128, 256, 2, 4, 3>(g, st);
       if (g.rows_hint == 256) return launch_dma_cfg<256, 256, 2, 4, 2>(g, st);
       return -1;
