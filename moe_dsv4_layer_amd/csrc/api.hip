@@ -47,7 +47,7 @@ inline int router_split(int hidden, bool mfma) {
 }
 
 struct Layout {
-  size_t xn, c, qkv, q, kc, vc, o, yf, ys, wr3, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
+  size_t xn, c, qkv, q, kc, vc, o, yf, ys, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
       count, offset, tiles, ntiles, z, zs, part, psh, skp, rope, total;
 };
 
@@ -69,7 +69,6 @@ Layout layout(const ds4g_layer_cfg& c, int T) {
   L.o = take((size_t)T * qd * 4);
   L.yf = take((size_t)T * d * 4);
   L.ys = take((size_t)T * 3 * d * 2);
-  L.wr3 = take(E * 3 * d * 2);
   L.logits = take((size_t)T * E * 4);
   L.lpart = take((size_t)T * E * 4 * kRouterSplit);
   L.tidx = take((size_t)T * k * 4);
@@ -266,8 +265,8 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.M = T; g.N = E; g.epi = EPI_F32; g.C = at<void>(ws, L.lpart); g.ldc = E;
     g.ksplit = rsplit; g.part_stride = (long)T * E;
     if (bf) {
-      rc |= launch_repeat3((const uint16_t*)w.router, E, d, at<uint16_t>(ws, L.wr3), st);
-      g.A = at<void>(ws, L.ys); g.lda = 3 * d; g.B = at<void>(ws, L.wr3); g.K = 3 * d;
+      // y1|y2|y3 against W_r repeated three times along K (read in place)
+      g.A = at<void>(ws, L.ys); g.lda = 3 * d; g.B = w.router; g.brep = d; g.K = 3 * d;
     } else {
       g.A = at<void>(ws, L.yf); g.lda = d; g.B = w.router; g.K = d;
     }
@@ -317,7 +316,10 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   }
   // shared down (x = h2 + shared), then combine: x += sum_j w_j part_j
   gemm(at<void>(ws, L.zs), Is, w.sh_down, T, d, Is, EPI_RESID, x, d);
-  rc |= launch_moe_combine(x, at<void>(ws, L.part), bf ? 1 : 0, ra.pos_of, ra.topk_w, T, d, k, st);
+  // batched decode: the combine also advances each sequence's position (the
+  // attention kernel read it; nothing after the combine does)
+  rc |= launch_moe_combine(x, at<void>(ws, L.part), bf ? 1 : 0, ra.pos_of, ra.topk_w, T, d, k,
+                           batch ? ring.pos : nullptr, st);
   if (routing) {
     copy_out(routing->topk_idx, ra.topk_idx, (size_t)T * k * 4, st);
     copy_out(routing->topk_w, ra.topk_w, (size_t)T * k * 4, st);

@@ -376,11 +376,6 @@ int launch_attention_decode(const AttnArgs& a, hipStream_t st) {
   return 0;
 }
 
-__global__ void pos_advance_batch_kernel(int64_t* pos, int B) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < B) pos[b] += 1;
-}
-
 int launch_attention_decode_batch(const AttnArgs& a, int B, hipStream_t st) {
   if (B <= 0 || B > 65535) return -1;
   const dim3 grid(a.H, B);
@@ -397,7 +392,6 @@ int launch_attention_decode_batch(const AttnArgs& a, int B, hipStream_t st) {
   }
 #undef DS4G_AD
   // every block has read pos[b]: advance the positions
-  hipLaunchKernelGGL(pos_advance_batch_kernel, dim3((B + 255) / 256), dim3(256), 0, st, a.pos, B);
   return 0;
 }
 

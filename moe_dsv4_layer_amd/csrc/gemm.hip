@@ -377,7 +377,7 @@ gemm_dma_kernel(GemmArgs g) {
         which[j] = 1;
         brow = ncol0 + r;
       }
-      voff[j] = (uint32_t)(((long)min(brow, g.N - 1) * g.K + c * 8) * 2);
+      voff[j] = (uint32_t)(((long)min(brow, g.N - 1) * (g.brep ? g.brep : g.K) + c * 8) * 2);
     }
   }
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(&smem[0][0]);
@@ -386,12 +386,16 @@ gemm_dma_kernel(GemmArgs g) {
   const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
   const int kbase = (int)blockIdx.z * (g.K / nsplit);
   const int nk = g.K / nsplit / BK;
+  // k of step kt; a repeated B (brep) reads its column k % brep
   auto issue = [&](int kt, int st) {
+    const int k = kbase + kt * BK;
+    const int kb = g.brep ? k % g.brep : k;
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const uint32_t dst = lds0 + (uint32_t)(st * ROWS * 128 + (wid * NDMA + j) * 1024);
       const i32x4_t rs = which[j] == 0 ? rsA : (which[j] == 1 ? rsB : rsB2);
-      dma16(rs, __builtin_amdgcn_readfirstlane(dst), voff[j] + (uint32_t)((kbase + kt * BK) * 2));
+      dma16(rs, __builtin_amdgcn_readfirstlane(dst),
+            voff[j] + (uint32_t)((which[j] == 0 ? k : kb) * 2));
     }
   };
 
@@ -532,7 +536,8 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
     if (g.K % (64 * nsplit)) return -1;
     if (nsplit > 1 && (g.epi != EPI_F32 || g.tiles)) return -1;
     // byte offsets of the direct loads are 32-bit
-    if ((double)g.N * g.K * 2 >= 4294967296.0) return -1;
+    if ((double)g.N * (g.brep ? g.brep : g.K) * 2 >= 4294967296.0) return -1;
+    if (g.brep && (g.brep % 64 || g.K % g.brep)) return -1;
     if (g.tiles) {   // the tile list was built for exactly rows_hint rows per tile
       // 64-row tiles (few rows per expert: a 2048-token prefill, batched
       // decode): 128 columns per tile, so small calls have more blocks to
@@ -576,6 +581,7 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
   } else {
     const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
     if (g.K % (16 * nsplit)) return -1;
+    if (g.brep) return -1;   // the repeated B operand is an MFMA-path feature
     if (nsplit > 1 && (dual || g.epi != EPI_F32)) return -1;
     const int mt = g.tiles ? g.max_tiles : (g.M + 63) / 64;
     dim3 grid((g.N + 63) / 64, mt, nsplit);

@@ -24,6 +24,8 @@ struct GemmArgs {
   const void* B;        // weights [N, K] (group g at B + g*b_stride)
   const void* B2;       // SwiGLU: up weights (B holds gate)
   long b_stride;
+  int brep;             // MFMA: B [N, brep] is repeated along K (K = a multiple of brep);
+                        // B rows at stride brep, column k % brep (0: B is [N, K])
   int M, N, K;          // M: rows when not grouped
   const int* tiles;     // grouped: packed (group << 16 | m_tile), device
   const int* ntiles;    // grouped: number of valid tiles, device
@@ -94,8 +96,8 @@ int launch_attention(const AttnArgs& a, hipStream_t st);
 // slot, attend over the window; o fp32 [H*dh].  Does not advance *pos.
 int launch_attention_decode(const AttnArgs& a, hipStream_t st);
 // B independent sequences, one token each: row b of qkv at position pos[b],
-// ring b at ring_k / ring_v + b * W * dh; o [B, H*dh] fp32 or bf16 (o_bf16);
-// advances every pos[b] by one afterwards.
+// ring b at ring_k / ring_v + b * W * dh; o [B, H*dh] fp32 or bf16 (o_bf16).
+// Does not advance pos (the layer's last kernel, the combine, does).
 int launch_attention_decode_batch(const AttnArgs& a, int B, hipStream_t st);
 // prefill on the matrix cores: bf16 q (q_bf16 = 1) and o (o_bf16 = 1)
 int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st);
@@ -127,7 +129,6 @@ int launch_moe_decode(const MoeDecodeArgs& a, float* x, int64_t* pos_inc, hipStr
 template <typename WT>
 int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps,
                         float* out_f32, uint16_t* out_bf16, uint16_t* out_split3, hipStream_t st);
-int launch_repeat3(const uint16_t* w, int E, int d, uint16_t* out, hipStream_t st);
 
 struct RouteArgs {
   const float* logits;  // nsplit partial sums [nsplit][T][E], added in order
@@ -150,9 +151,10 @@ struct RouteArgs {
 };
 int launch_route(const RouteArgs& r, hipStream_t st);
 // x[t] += sum_j w[t,j] part[pos_of[t*k+j]] (fixed j order); part is fp32, or bf16
-// when part_bf16 (the bf16 path rounds each routed expert output to bf16)
+// when part_bf16 (the bf16 path rounds each routed expert output to bf16).
+// pos_inc (optional, batched decode): pos_inc[t] += 1 for every row t.
 int launch_moe_combine(float* x, const void* part, int part_bf16, const int* pos_of,
-                       const float* w, int T, int d, int k, hipStream_t st);
+                       const float* w, int T, int d, int k, int64_t* pos_inc, hipStream_t st);
 
 // ---------------------------------------------------------------- sampler
 struct SampleArgs {

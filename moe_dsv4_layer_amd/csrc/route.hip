@@ -74,23 +74,6 @@ template int launch_rmsnorm_rows<uint16_t>(const float*, int, int, const uint16_
 template int launch_rmsnorm_rows<float>(const float*, int, int, const float*, float, float*,
                                         uint16_t*, uint16_t*, hipStream_t);
 
-// [W | W | W]: each row of the [E, d] bf16 router weight repeated three times
-// ([E, 3d]), the B operand of the router GEMM over the three-term split of y.
-__global__ void __launch_bounds__(256)
-repeat3_kernel(const uint16_t* __restrict__ w, int d, uint16_t* __restrict__ out) {
-  const long e = blockIdx.x;
-  for (int i = threadIdx.x * 8; i < d; i += 256 * 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(w + e * d + i);
-#pragma unroll
-    for (int p = 0; p < 3; ++p) *reinterpret_cast<uint4*>(out + e * 3 * d + p * d + i) = v;
-  }
-}
-int launch_repeat3(const uint16_t* w, int E, int d, uint16_t* out, hipStream_t st) {
-  if (d % 8) return -1;
-  hipLaunchKernelGGL(repeat3_kernel, dim3(E), dim3(256), 0, st, w, d, out);
-  return 0;
-}
-
 // ------------------------------------------------------------ top-k per token
 // One wave per token: k rounds of a wave arg-max (lower index wins ties) over
 // the E logits, and the softmax probability of each pick.
@@ -309,8 +292,10 @@ __device__ __forceinline__ float4 load4(const uint16_t* p) {
 template <typename PT>
 __global__ void __launch_bounds__(256)
 moe_combine_kernel(float* __restrict__ x, const PT* __restrict__ part,
-                   const int* __restrict__ pos_of, const float* __restrict__ w, int d, int k) {
+                   const int* __restrict__ pos_of, const float* __restrict__ w, int d, int k,
+                   int64_t* __restrict__ pos_inc) {
   const int t = blockIdx.x;
+  if (pos_inc && threadIdx.x == 0) pos_inc[t] += 1;   // batched decode: row t's sequence
   __shared__ int rows[8];
   __shared__ float ws[8];
   if (threadIdx.x < k) {
@@ -329,14 +314,14 @@ moe_combine_kernel(float* __restrict__ x, const PT* __restrict__ part,
 }
 
 int launch_moe_combine(float* x, const void* part, int part_bf16, const int* pos_of,
-                       const float* w, int T, int d, int k, hipStream_t st) {
+                       const float* w, int T, int d, int k, int64_t* pos_inc, hipStream_t st) {
   if (d % 4 || k > 8) return -1;
   if (part_bf16)
     hipLaunchKernelGGL(moe_combine_kernel<uint16_t>, dim3(T), dim3(256), 0, st, x,
-                       static_cast<const uint16_t*>(part), pos_of, w, d, k);
+                       static_cast<const uint16_t*>(part), pos_of, w, d, k, pos_inc);
   else
     hipLaunchKernelGGL(moe_combine_kernel<float>, dim3(T), dim3(256), 0, st, x,
-                       static_cast<const float*>(part), pos_of, w, d, k);
+                       static_cast<const float*>(part), pos_of, w, d, k, pos_inc);
   return 0;
 }
 
