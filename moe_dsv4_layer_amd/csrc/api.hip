@@ -183,6 +183,13 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   // applies the epilogue).  B2: the up projection of a SwiGLU pair.
   auto gemm = [&](const void* A, int lda, const void* B, int M, int N, int K, int epi, void* C,
                   int ldc, const void* B2 = nullptr) {
+    if (batch && bf && M <= 8) {   // a few rows: stream each weight row once (multi-row GEMV)
+      GemvRowsArgs v{};
+      v.W = static_cast<const uint16_t*>(B); v.W2 = static_cast<const uint16_t*>(B2);
+      v.N = N; v.K = K; v.X = static_cast<const uint16_t*>(A); v.lda = lda; v.M = M;
+      v.epi = epi; v.C = C; v.ldc = ldc;
+      if (launch_gemv_rows(v, st) == 0) return;
+    }
     const int s = batch ? batch_split(M, N, K, bf) : 1;
     if (s > 1) {
       float* part = at<float>(ws, L.skp);

@@ -188,6 +188,146 @@ template int launch_gemv<uint16_t>(const GemvArgs&, hipStream_t);
 template int launch_gemv<float>(const GemvArgs&, hipStream_t);
 
 // ---------------------------------------------------------------------------
+// Multi-row GEMV: the dense projections of a batched decode call (M <= 8
+// rows).  Each weight row is streamed once for all M rows.  The block layout
+// is gemv_kernel's: 4 waves split K in KSPLIT parts and the block's rows in
+// 4/KSPLIT groups; a wave keeps its K slice of all M activation rows in
+// registers (bf16, MR x CPL chunks of 8) and streams RB weight rows at a time,
+// issuing the next rows' loads before the current rows' reductions.
+template <int MR, int KSPLIT, int CPL, int RB, bool DUAL>
+__global__ void __launch_bounds__(256)
+gemv_rows_kernel(GemvRowsArgs a) {
+  constexpr int RSPLIT = 4 / KSPLIT;
+  constexpr int NV = DUAL ? 2 : 1;
+  __shared__ float red[4][RB][MR][NV];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int kpart = wid % KSPLIT, rgroup = wid / KSPLIT;
+  const int N = a.N, K = a.K, nchunk = K >> 3;
+  const int rows_per_block = RB * RSPLIT;
+  const int stride = gridDim.x * rows_per_block;
+
+  uint4 xr[MR][CPL];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = (kpart * CPL + i) * 64 + lane;
+      xr[m][i] = (m < a.M && c < nchunk)
+                     ? *reinterpret_cast<const uint4*>(a.X + (long)m * a.lda + c * 8)
+                     : make_uint4(0u, 0u, 0u, 0u);
+    }
+  Chunk8<uint16_t> cw[RB][CPL], cu[DUAL ? RB : 1][CPL];
+  auto load_rows = [&](int r0) __attribute__((always_inline)) {
+    const int rbase = r0 + rgroup * RB;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = (kpart * CPL + i) * 64 + lane;
+        if (rbase + r < N && c < nchunk) {
+          cw[r][i].load(a.W + (long)(rbase + r) * K + c * 8);
+          if (DUAL) cu[DUAL ? r : 0][i].load(a.W2 + (long)(rbase + r) * K + c * 8);
+        }
+      }
+  };
+  int r0 = blockIdx.x * rows_per_block;
+  if (r0 < N) load_rows(r0);
+  for (; r0 < N; r0 += stride) {
+    const int rbase = r0 + rgroup * RB;
+    float acc[RB][MR][NV];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[r][m][v] = 0.f;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = (kpart * CPL + i) * 64 + lane;
+        if (rbase + r < N && c < nchunk) {
+          float w[8], u[8];
+          cw[r][i].widen(w);
+          if (DUAL) cu[DUAL ? r : 0][i].widen(u);
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            float x[8];
+            unpack8(xr[m][i], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              acc[r][m][0] += w[e] * x[e];
+              if (DUAL) acc[r][m][NV - 1] += u[e] * x[e];
+            }
+          }
+        }
+      }
+    if (r0 + stride < N) load_rows(r0 + stride);
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[r][m][v] = wave_sum(acc[r][m][v]);
+    __syncthreads();   // the previous row group's sums have been read
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+          for (int v = 0; v < NV; ++v) red[wid][r][m][v] = acc[r][m][v];
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < RSPLIT * RB * MR) {
+      const int rg = t / (RB * MR), r = (t / MR) % RB, m = t % MR;
+      const int n = r0 + rg * RB + r;
+      if (n < N && m < a.M) {
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int p = 0; p < KSPLIT; ++p) {
+          g += red[rg * KSPLIT + p][r][m][0];
+          if (DUAL) u += red[rg * KSPLIT + p][r][m][NV - 1];
+        }
+        const long o = (long)m * a.ldc + n;
+        if (DUAL) static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(silu(g) * u);
+        else if (a.epi == EPI_BF16) static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(g);
+        else if (a.epi == EPI_RESID) static_cast<float*>(a.C)[o] += g;
+        else static_cast<float*>(a.C)[o] = g;
+      }
+    }
+  }
+}
+
+template <int MR, bool DUAL>
+int launch_gemv_rows_mr(const GemvRowsArgs& a, hipStream_t st) {
+  constexpr int RB = 2;
+  auto go = [&](auto kern, int ksplit) {
+    const int rpb = RB * (4 / ksplit);
+    long grid = (a.N + rpb - 1) / rpb;
+    if (grid > DS4G_GEMV_GRID_MAX) grid = DS4G_GEMV_GRID_MAX;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, a);
+    return 0;
+  };
+  if (a.K <= 1024) return go(gemv_rows_kernel<MR, 1, 2, RB, DUAL>, 1);
+  return go(gemv_rows_kernel<MR, 4, 2, RB, DUAL>, 4);
+}
+
+int launch_gemv_rows(const GemvRowsArgs& a, hipStream_t st) {
+  const bool dual = a.epi == EPI_SWIGLU_BF16;
+  // K <= 4096: with 8 rows, a wider K slice per lane (K = 8192, W_o) needs
+  // ~330-390 VGPRs, one wave per SIMD, and streamed at half the split-K
+  // GEMM's rate (47 against 20 us at B = 8)
+  if (a.M < 1 || a.M > 8 || a.K % 8 || a.K > 4096 || a.N < 1 || (dual && !a.W2)) return -1;
+  if (!dual && a.epi != EPI_F32 && a.epi != EPI_BF16 && a.epi != EPI_RESID) return -1;
+  if (a.lda % 8) return -1;   // 16-byte activation chunks
+  if (a.M <= 2) return dual ? launch_gemv_rows_mr<2, true>(a, st) : launch_gemv_rows_mr<2, false>(a, st);
+  if (a.M <= 4) return dual ? launch_gemv_rows_mr<4, true>(a, st) : launch_gemv_rows_mr<4, false>(a, st);
+  return dual ? launch_gemv_rows_mr<8, true>(a, st) : launch_gemv_rows_mr<8, false>(a, st);
+}
+
+// ---------------------------------------------------------------------------
 // MoE decode for one token, three kernels:
 //   router_shared_decode  logits = W_r y and the shared expert's
 //                         z_sh = silu(G_sh y) * (U_sh y), y = RMSNorm(h2) * g2

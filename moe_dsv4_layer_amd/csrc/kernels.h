@@ -74,6 +74,23 @@ struct GemvArgs {
 template <typename WT>
 int launch_gemv(const GemvArgs& a, hipStream_t st);
 
+// out[m, n] = sum_k W[n, k] X[m, k] for the M <= 8 rows of a batched decode
+// call: W [N, K] bf16 (row stride K), X [M, K] bf16 (row stride lda).  epi:
+// EPI_F32, EPI_BF16, EPI_RESID (C[m, n] += out) or EPI_SWIGLU_BF16 (W: gate,
+// W2: up, C = bf16(silu(gate) * up)); C [M, ldc].  -1 when the shape is not
+// covered (M > 8, K > 4096, K % 8), launching nothing.
+struct GemvRowsArgs {
+  const uint16_t* W;
+  const uint16_t* W2;
+  int N, K;
+  const uint16_t* X;
+  int lda, M;
+  int epi;
+  void* C;
+  int ldc;
+};
+int launch_gemv_rows(const GemvRowsArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
   const float* qkv;     // [T, H*dh + 2*dh] fp32

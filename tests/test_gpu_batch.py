@@ -103,6 +103,14 @@ def test_batch_small_bf16_mixed_histories():
         assert rel_l2(bt.rv[b].float().cpu().numpy(), bt.orc[b].v) < 1e-2
 
 
+def test_batch_two_sequences_bf16():
+    # B = 2: the smallest row count of the multi-row GEMV path
+    bt = Batch(small_shape(), 33, hist=[7, 0])
+    for j in range(2):
+        xin, x, bufs, outs = bt.step(j)
+        _check_step(f"batch of two, step {j}", bt, xin, x, bufs, outs)
+
+
 def test_batch_fp32_weights():
     bt = Batch(small_shape(wdtype=synth.F32), 32, hist=[5, 0, 21])
     xin, x, bufs, outs = bt.step(0)
