@@ -108,3 +108,39 @@ def test_fp32_weights_tiny_stack_layer():
                                              "router_logits") else v for k, v in bufs.items()}
         _compare_layer(f"fp32 decode pos={t}", shape, gl, h[t:t + 1], x.reshape(1, -1),
                        bufs, orc)
+
+
+LIMIT_SHAPES = {
+    # the largest supported routing (512 experts, top-8), the longest window,
+    # head_dim 128 with RoPE on its last 64 entries only
+    "limits": (dict(hidden=256, n_heads=4, head_dim=128, qkv_rank=64, window=128,
+                    n_experts=512, top_k=8, ffn_inter=64, rope_dim=64), 300),
+    # degenerate: a window of one (each token attends to itself only) and
+    # top-8 of 9 experts
+    "degenerate": (dict(hidden=128, n_heads=4, head_dim=64, qkv_rank=64, window=1,
+                        n_experts=9, top_k=8, ffn_inter=64), 40),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LIMIT_SHAPES))
+def test_prefill_and_decode_at_the_limits(name):
+    dims, T = LIMIT_SHAPES[name]
+    shape = synth.LayerShape(wdtype=synth.BF16, **dims)
+    n_dec = 3
+    log(f"{name}: prefill {T} + {n_dec} decode steps")
+    gl = GpuLayer(shape, seed=14, max_tokens=T)
+    h = synth.hidden(T + n_dec, shape.hidden, 14, device="cuda")
+    ring = _oracle_ring(shape)
+    wh = gl.host_weights()
+    x, bufs = gl.prefill(h[:T])
+    orc = oracle.layer_forward(shape, wh, ring, h[:T].cpu().numpy())
+    _compare_layer(f"{name} prefill", shape, gl, h[:T], x, bufs, orc)
+    for t in range(T, T + n_dec):
+        x, bufs = gl.decode(h[t])
+        orc = oracle.layer_forward(shape, wh, ring, h[t:t + 1].cpu().numpy())
+        bufs = {k: v.reshape(1, -1) if k in ("topk_idx", "topk_w", "router_in",
+                                             "router_logits") else v for k, v in bufs.items()}
+        _compare_layer(f"{name} decode pos={t}", shape, gl, h[t:t + 1], x.reshape(1, -1), bufs,
+                       orc)
+    assert int(gl.pos.item()) == T + n_dec
+    assert rel_l2(gl.ring_k.float().cpu().numpy(), ring.k) < 1e-2
