@@ -18,24 +18,46 @@ namespace ds4g {
 // 3d): y1 = bf16(y), y2 = bf16(y - y1), y3 = bf16(y - y1 - y2).  Products of
 // the terms with bf16 weights are exact in fp32 and y - y1 - y2 - y3 is below
 // 2^-27 |y|, so a bf16 MFMA GEMM over the split gives fp32-quality results.
+constexpr int RMS_CHUNKS = 16;   // rows up to 16384 wide
+__device__ __forceinline__ void load_gain4(const uint16_t* g, int i, float* o) {
+  const uint2 q = *reinterpret_cast<const uint2*>(g + i);
+  o[0] = __uint_as_float(q.x << 16); o[1] = __uint_as_float(q.x & 0xFFFF0000u);
+  o[2] = __uint_as_float(q.y << 16); o[3] = __uint_as_float(q.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load_gain4(const float* g, int i, float* o) {
+  const float4 q = *reinterpret_cast<const float4*>(g + i);
+  o[0] = q.x; o[1] = q.y; o[2] = q.z; o[3] = q.w;
+}
+
 template <typename WT>
 __global__ void __launch_bounds__(256)
 rmsnorm_rows_kernel(const float* __restrict__ x, int d, const WT* __restrict__ gamma, float eps,
                     float* __restrict__ of, uint16_t* __restrict__ ob, uint16_t* __restrict__ os3) {
+  // the row stays in registers between the sum of squares and the scaling
+  // (d <= 256 * 4 * RMS_CHUNKS); all of a thread's loads go out together
   __shared__ float red[16];
   const long t = blockIdx.x;
   const float* row = x + t * d;
+  float4 xv[RMS_CHUNKS];
   float ss = 0.f;
-  for (int i = threadIdx.x * 4; i < d; i += blockDim.x * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(row + i);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int c = 0; c < RMS_CHUNKS; ++c) {
+    const int i = threadIdx.x * 4 + c * 1024;
+    xv[c] = i < d ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+#pragma unroll
+  for (int c = 0; c < RMS_CHUNKS; ++c)
+    ss += xv[c].x * xv[c].x + xv[c].y * xv[c].y + xv[c].z * xv[c].z + xv[c].w * xv[c].w;
   ss = block_sum(ss, red);
   const float rs = rsqrtf(ss / (float)d + eps);
-  for (int i = threadIdx.x * 4; i < d; i += blockDim.x * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(row + i);
-    float y[4] = {v.x * rs * ldw(gamma, i), v.y * rs * ldw(gamma, i + 1),
-                  v.z * rs * ldw(gamma, i + 2), v.w * rs * ldw(gamma, i + 3)};
+#pragma unroll
+  for (int c = 0; c < RMS_CHUNKS; ++c) {
+    const int i = threadIdx.x * 4 + c * 1024;
+    if (i >= d) break;
+    const float4 v = xv[c];
+    float g[4];
+    load_gain4(gamma, i, g);
+    float y[4] = {v.x * rs * g[0], v.y * rs * g[1], v.z * rs * g[2], v.w * rs * g[3]};
     if (of) *reinterpret_cast<float4*>(of + t * d + i) = make_float4(y[0], y[1], y[2], y[3]);
     uint16_t b1[4], b2[4], b3[4];
 #pragma unroll
@@ -64,7 +86,7 @@ rmsnorm_rows_kernel(const float* __restrict__ x, int d, const WT* __restrict__ g
 template <typename WT>
 int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps, float* of,
                         uint16_t* ob, uint16_t* os3, hipStream_t st) {
-  if (d % 4) return -1;
+  if (d % 4 || d > 1024 * RMS_CHUNKS) return -1;
   hipLaunchKernelGGL((rmsnorm_rows_kernel<WT>), dim3(T), dim3(256), 0, st, x, d, gamma, eps, of,
                      ob, os3);
   return 0;
