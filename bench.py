@@ -43,9 +43,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 # 8 steps; FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0, the factors that make a
 # 1 GiB device copy read 1 GiB and write 1 GiB).  Valid only for the decode
 # sources it was measured on: any change to them reports traffic as null.
-DECODE_TRAFFIC_BYTES = 274055612
+DECODE_TRAFFIC_BYTES = 274063385
 DECODE_TRAFFIC_SOURCES = ("api.hip", "attn.hip", "decode.hip", "dev.h", "kernels.h")
-DECODE_TRAFFIC_SHA1 = "45a3008dc4c5cd50629e8834fed7efeb5ee28031"
+DECODE_TRAFFIC_SHA1 = "b5cb6045aa4e934094b068d55473b824794638f8"
 
 
 def decode_traffic():
