@@ -103,12 +103,15 @@ def test_batch_small_bf16_mixed_histories():
         assert rel_l2(bt.rv[b].float().cpu().numpy(), bt.orc[b].v) < 1e-2
 
 
-def test_batch_two_sequences_bf16():
-    # B = 2: the smallest row count of the multi-row GEMV path
-    bt = Batch(small_shape(), 33, hist=[7, 0])
+@pytest.mark.parametrize("hist", [[9], [7, 0], [3, 0, 17, 1, 16, 5, 0, 2, 30, 8, 12, 4]],
+                         ids=["B1", "B2", "B12"])
+def test_batch_sizes_bf16(hist):
+    # B = 1 and 2: the multi-row GEMV with rows masked; B = 12: past its
+    # 8-row limit, the split-K GEMM path
+    bt = Batch(small_shape(), 33, hist=hist)
     for j in range(2):
         xin, x, bufs, outs = bt.step(j)
-        _check_step(f"batch of two, step {j}", bt, xin, x, bufs, outs)
+        _check_step(f"batch of {len(hist)}, step {j}", bt, xin, x, bufs, outs)
 
 
 def test_batch_fp32_weights():
