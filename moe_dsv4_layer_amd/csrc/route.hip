@@ -3,7 +3,7 @@
 //
 // ds4-learning 端到端推理流程, 阶段四 4.2 单层前向: x_norm = RMSNorm(x);
 // scores = x_norm @ W_router (256 experts); top6 = TopK(scores, 6).  The
-// grouping is this build's layout for running each expert once over all of its
+// grouping is this library's layout for running each expert once over all of its
 // tokens (阶段三 逐层批处理): entries t*k + j, grouped by expert, in token order
 // inside an expert; built with per-expert prefix sums, so it is deterministic
 // (no atomics decide an order).
