@@ -36,8 +36,11 @@
  *     decode step can be captured in a HIP graph and replayed.
  *   - Every argument check runs on the host before anything is enqueued; on
  *     an error nothing is written and a negative ds4g_status is returned.
- *     DS4G_ERR_HIP reports a failed launch (the stream state is then
- *     undefined).
+ *     A call first walks its whole launch sequence without enqueuing (each
+ *     kernel launcher checks the shape it is given), so a size that some
+ *     kernel does not implement is DS4G_ERR_UNSUPPORTED before the first
+ *     launch, never a partial update.  DS4G_ERR_HIP reports a launch the HIP
+ *     runtime refused (the stream state is then undefined).
  *   - A ring and a workspace must not be used by two calls at once.
  */
 #ifndef DS4G_H
@@ -60,10 +63,20 @@ typedef enum {
 
 typedef enum { DS4G_F32 = 0, DS4G_BF16 = 1 } ds4g_dtype;
 
+/* The three layer calls, for ds4g_layer_supported. */
+typedef enum {
+  DS4G_MODE_PREFILL = 0,       /* ds4g_layer_prefill, T tokens            */
+  DS4G_MODE_DECODE = 1,        /* ds4g_layer_decode, T = 1                */
+  DS4G_MODE_DECODE_BATCH = 2   /* ds4g_layer_decode_batch, T sequences    */
+} ds4g_mode;
+
 /* Layer dimensions.  Supported: head_dim in {64, 128}; rope_dim even and
  * <= head_dim (0 = head_dim); window in [1, 128]; n_experts in [top_k+1, 512];
- * top_k in [1, 8]; hidden, qkv_rank, ffn_inter, shared_inter multiples of 64;
- * n_heads*head_dim a multiple of 64. */
+ * top_k in [1, 8]; n_heads a multiple of 4; hidden, qkv_rank, ffn_inter,
+ * shared_inter and n_heads*head_dim multiples of 64; hidden, qkv_rank and
+ * n_heads*head_dim <= 16384 (hidden <= 8192 for ds4g_layer_decode);
+ * ffn_inter, shared_inter <= 2048 and top_k*ffn_inter + shared_inter <=
+ * 12288.  ds4g_layer_supported answers for a given shape. */
 typedef struct {
   int32_t hidden;        /* d: residual width (4096)                         */
   int32_t n_heads;       /* H: query heads (64); one K/V head (MQA)          */
@@ -120,6 +133,14 @@ typedef struct {
  * alone).  Returns 0 on invalid arguments. */
 size_t ds4g_workspace_bytes(const ds4g_layer_cfg *cfg, int32_t max_tokens,
                             int32_t vocab);
+
+/* Whether a layer call of this mode with these dimensions would be accepted
+ * (DS4G_OK), or the status it would return for a shape reason
+ * (DS4G_ERR_INVALID_ARG, DS4G_ERR_UNSUPPORTED).  Runs the host checks and
+ * the call's launch sequence without enqueuing anything; needs no device and
+ * touches no memory.  T: tokens (prefill), 1 (decode), or sequences (batched
+ * decode).  Pointer, alignment and workspace-size checks are not covered. */
+int ds4g_layer_supported(const ds4g_layer_cfg *cfg, int32_t T, int32_t mode);
 
 /* Layer-major prefill of T >= 1 tokens at positions *ring->pos ..
  * *ring->pos + T - 1 (阶段三 逐层批处理; 阶段四 4.2 for the layer).

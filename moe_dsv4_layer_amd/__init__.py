@@ -16,10 +16,11 @@ LIB_PATH = os.environ.get("DS4G_LIB") or os.path.join(HERE, "libds4g.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
+MODE_PREFILL, MODE_DECODE, MODE_DECODE_BATCH = 0, 1, 2
 
 # ds4g.h declares these functions; the ABI test checks the header agrees.
-EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_prefill", "ds4g_layer_decode",
-           "ds4g_layer_decode_batch",
+EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_supported", "ds4g_layer_prefill",
+           "ds4g_layer_decode", "ds4g_layer_decode_batch",
            "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_status_string")
 
 
@@ -88,6 +89,8 @@ def _load() -> ctypes.CDLL:
     P = ctypes.c_void_p
     lib.ds4g_workspace_bytes.restype = ctypes.c_size_t
     lib.ds4g_workspace_bytes.argtypes = [ctypes.POINTER(LayerCfg), ctypes.c_int32, ctypes.c_int32]
+    lib.ds4g_layer_supported.restype = ctypes.c_int
+    lib.ds4g_layer_supported.argtypes = [ctypes.POINTER(LayerCfg), ctypes.c_int32, ctypes.c_int32]
     lib.ds4g_layer_prefill.restype = ctypes.c_int
     lib.ds4g_layer_prefill.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
                                        ctypes.POINTER(KvRing), P, ctypes.c_int32,
@@ -170,6 +173,12 @@ def make_routing(bufs: Optional[Dict[str, "torch.Tensor"]]) -> Optional[Routing]
 def workspace_bytes(cfg: Optional[LayerCfg], max_tokens: int, vocab: int = 0) -> int:
     return int(lib.ds4g_workspace_bytes(ctypes.byref(cfg) if cfg is not None else None,
                                         max_tokens, vocab))
+
+
+def layer_supported(cfg: Optional[LayerCfg], T: int, mode: int) -> int:
+    """Status a layer call of `mode` over T tokens / sequences would return
+    for its shape (0 = accepted); needs no device."""
+    return int(lib.ds4g_layer_supported(ctypes.byref(cfg) if cfg is not None else None, T, mode))
 
 
 def layer_prefill(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x, T: int, ws,

@@ -139,8 +139,11 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Status of a real (non-dry) launch sequence.  Its dry run accepted the same
+// arguments, so a launcher cannot refuse here; a refusal would be a bug and
+// is reported as a launch failure.
 int hip_status(int launch_rc) {
-  if (launch_rc != 0) return DS4G_ERR_UNSUPPORTED;
+  if (launch_rc != 0) return DS4G_ERR_HIP;
   const hipError_t e = hipGetLastError();
   if (e == hipSuccess) return DS4G_OK;
   fprintf(stderr, "ds4g: HIP launch error: %s\n", hipGetErrorString(e));
@@ -152,8 +155,19 @@ int hip_status(int launch_rc) {
 void clear_stale_error() { (void)hipGetLastError(); }
 
 // copy an optional routing output
-void copy_out(void* dst, const void* src, size_t bytes, hipStream_t st) {
-  if (dst && bytes) (void)hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+void copy_out(void* dst, const void* src, size_t bytes, Exec st) {
+  if (dst && bytes && !st.dry)
+    (void)hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st.stream);
+}
+
+// Run a call's launch sequence dry (every launcher checks its preconditions,
+// nothing is enqueued), then for real.  A shape that any launcher refuses is
+// reported as DS4G_ERR_UNSUPPORTED before the first kernel is enqueued.
+template <typename F>
+int dry_then_run(hipStream_t stream, F&& seq) {
+  if (seq(Exec{stream, true}) != 0) return DS4G_ERR_UNSUPPORTED;
+  clear_stale_error();
+  return hip_status(seq(Exec{stream, false}));
 }
 
 // ------------------------------------------------------------------ prefill
@@ -161,7 +175,7 @@ void copy_out(void* dst, const void* src, size_t bytes, hipStream_t st) {
 // token of each of T independent sequences: the same GEMMs, router and
 // experts over T rows; only the attention stage differs.
 int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring& ring,
-                 float* x, int T, ds4g_routing* routing, void* ws, hipStream_t st,
+                 float* x, int T, ds4g_routing* routing, void* ws, Exec st,
                  bool batch = false) {
   const Layout L = layout(c, T);
   const bool bf = c.wdtype == DS4G_BF16;
@@ -334,13 +348,13 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     copy_out(routing->router_in, at<void>(ws, L.yf), (size_t)T * d * 4, st);
     copy_out(routing->router_logits, ra.logits_sum, (size_t)T * E * 4, st);
   }
-  return hip_status(rc);
+  return rc;
 }
 
 // ------------------------------------------------------------------ decode
 template <typename WT>
 int decode_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring& ring,
-                float* x, ds4g_routing* routing, void* ws, hipStream_t st) {
+                float* x, ds4g_routing* routing, void* ws, Exec st) {
   const Layout L = layout(c, 1);
   const int d = c.hidden, r = c.qkv_rank, H = c.n_heads, dh = c.head_dim, qd = H * dh,
             qkvd = qd + 2 * dh, E = c.n_experts;
@@ -390,7 +404,47 @@ int decode_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ri
   }
   rc |= launch_moe_decode<WT>(m, x, ring.pos, st);
   if (routing) copy_out(routing->router_logits, logits, (size_t)E * 4, st);
-  return hip_status(rc);
+  return rc;
+}
+
+// Row-count limits of a layer call (T tokens, or T sequences of a batched
+// decode).  The MFMA GEMMs address their 16-bit operands with 32-bit byte
+// offsets: no operand may reach 4 GiB.
+int check_rows(const ds4g_layer_cfg& c, int T, int mode) {
+  if (mode == DS4G_MODE_DECODE) return T == 1 ? DS4G_OK : DS4G_ERR_INVALID_ARG;
+  if (mode == DS4G_MODE_DECODE_BATCH && T > 65535) return DS4G_ERR_UNSUPPORTED;
+  if ((long)T * c.top_k >= (1 << 24) || T > (1 << 20)) return DS4G_ERR_UNSUPPORTED;
+  if (c.wdtype == DS4G_BF16) {
+    const double widest = std::max({3.0 * c.hidden, (double)c.n_heads * c.head_dim,
+                                    (double)c.qkv_rank, (double)c.shared_inter,
+                                    (double)c.top_k * c.ffn_inter});
+    if ((double)T * widest * 2.0 >= 4294967296.0) return DS4G_ERR_UNSUPPORTED;
+  }
+  return DS4G_OK;
+}
+
+// Every host-side check of a layer call, in order: dimensions, pointers,
+// workspace alignment, row limits, workspace size.
+int check_call(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, const ds4g_kv_ring* ring,
+               const float* x, int T, const void* ws, size_t ws_bytes, int mode) {
+  int s = check_cfg(cfg);
+  if (s != DS4G_OK) return s;
+  if ((s = check_weights(w)) != DS4G_OK) return s;
+  if ((s = check_ring(ring)) != DS4G_OK) return s;
+  if (!x || !ws || T <= 0) return DS4G_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
+  if ((s = check_rows(*cfg, T, mode)) != DS4G_OK) return s;
+  if (ws_bytes < layout(*cfg, T).total) return DS4G_ERR_WORKSPACE;
+  return DS4G_OK;
+}
+
+// The launch sequence of a layer call of the given mode.
+int layer_seq(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring& ring, float* x,
+              int T, ds4g_routing* routing, void* ws, Exec ex, int mode) {
+  if (mode == DS4G_MODE_DECODE)
+    return c.wdtype == DS4G_BF16 ? decode_impl<uint16_t>(c, w, ring, x, routing, ws, ex)
+                                 : decode_impl<float>(c, w, ring, x, routing, ws, ex);
+  return prefill_impl(c, w, ring, x, T, routing, ws, ex, mode == DS4G_MODE_DECODE_BATCH);
 }
 
 }  // namespace
@@ -418,53 +472,46 @@ size_t ds4g_workspace_bytes(const ds4g_layer_cfg* cfg, int32_t max_tokens, int32
 int ds4g_layer_prefill(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
                        ds4g_kv_ring* ring, float* x, int32_t T, ds4g_routing* routing, void* ws,
                        size_t ws_bytes, void* stream) {
-  int s = check_cfg(cfg);
+  int s = check_call(cfg, w, ring, x, T, ws, ws_bytes, DS4G_MODE_PREFILL);
   if (s != DS4G_OK) return s;
-  if ((s = check_weights(w)) != DS4G_OK) return s;
-  if ((s = check_ring(ring)) != DS4G_OK) return s;
-  if (!x || !ws || T <= 0) return DS4G_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
-  if ((long)T * cfg->top_k >= (1 << 24) || T > (1 << 20)) return DS4G_ERR_UNSUPPORTED;
-  if (cfg->wdtype == DS4G_BF16) {
-    // the MFMA GEMMs address their bf16 operands with 32-bit byte offsets
-    const double widest = std::max({3.0 * cfg->hidden, (double)cfg->n_heads * cfg->head_dim,
-                                    (double)cfg->qkv_rank, (double)cfg->shared_inter,
-                                    (double)cfg->top_k * cfg->ffn_inter});
-    if ((double)T * widest * 2.0 >= 4294967296.0) return DS4G_ERR_UNSUPPORTED;
-  }
-  if (ws_bytes < layout(*cfg, T).total) return DS4G_ERR_WORKSPACE;
-  clear_stale_error();
-  return prefill_impl(*cfg, *w, *ring, x, T, routing, ws, (hipStream_t)stream);
+  return dry_then_run((hipStream_t)stream, [&](Exec ex) {
+    return prefill_impl(*cfg, *w, *ring, x, T, routing, ws, ex);
+  });
 }
 
 int ds4g_layer_decode_batch(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
                             ds4g_kv_ring* rings, float* x, int32_t B, ds4g_routing* routing,
                             void* ws, size_t ws_bytes, void* stream) {
-  int s = check_cfg(cfg);
+  int s = check_call(cfg, w, rings, x, B, ws, ws_bytes, DS4G_MODE_DECODE_BATCH);
   if (s != DS4G_OK) return s;
-  if ((s = check_weights(w)) != DS4G_OK) return s;
-  if ((s = check_ring(rings)) != DS4G_OK) return s;
-  if (!x || !ws || B <= 0) return DS4G_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
-  if (B > 65535) return DS4G_ERR_UNSUPPORTED;
-  if (ws_bytes < layout(*cfg, B).total) return DS4G_ERR_WORKSPACE;
-  clear_stale_error();
-  return prefill_impl(*cfg, *w, *rings, x, B, routing, ws, (hipStream_t)stream, true);
+  return dry_then_run((hipStream_t)stream, [&](Exec ex) {
+    return prefill_impl(*cfg, *w, *rings, x, B, routing, ws, ex, true);
+  });
 }
 
 int ds4g_layer_decode(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, ds4g_kv_ring* ring,
                       float* x, ds4g_routing* routing, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_call(cfg, w, ring, x, 1, ws, ws_bytes, DS4G_MODE_DECODE);
+  if (s != DS4G_OK) return s;
+  return dry_then_run((hipStream_t)stream, [&](Exec ex) {
+    return layer_seq(*cfg, *w, *ring, x, 1, routing, ws, ex, DS4G_MODE_DECODE);
+  });
+}
+
+int ds4g_layer_supported(const ds4g_layer_cfg* cfg, int32_t T, int32_t mode) {
   int s = check_cfg(cfg);
   if (s != DS4G_OK) return s;
-  if ((s = check_weights(w)) != DS4G_OK) return s;
-  if ((s = check_ring(ring)) != DS4G_OK) return s;
-  if (!x || !ws) return DS4G_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
-  if (ws_bytes < layout(*cfg, 1).total) return DS4G_ERR_WORKSPACE;
-  clear_stale_error();
-  if (cfg->wdtype == DS4G_BF16)
-    return decode_impl<uint16_t>(*cfg, *w, *ring, x, routing, ws, (hipStream_t)stream);
-  return decode_impl<float>(*cfg, *w, *ring, x, routing, ws, (hipStream_t)stream);
+  if (mode != DS4G_MODE_PREFILL && mode != DS4G_MODE_DECODE && mode != DS4G_MODE_DECODE_BATCH)
+    return DS4G_ERR_INVALID_ARG;
+  if (T <= 0 || (mode == DS4G_MODE_DECODE && T != 1)) return DS4G_ERR_INVALID_ARG;
+  if ((s = check_rows(*cfg, T, mode)) != DS4G_OK) return s;
+  // the launch sequence, dry, over placeholder addresses (never dereferenced)
+  void* const p = reinterpret_cast<void*>(uintptr_t(1) << 40);
+  ds4g_layer_weights w{p, p, p, p, p, p, p, p, p, p, p, p};
+  ds4g_kv_ring ring{p, p, static_cast<int64_t*>(p)};
+  return layer_seq(*cfg, w, ring, static_cast<float*>(p), T, nullptr, p, Exec{nullptr, true}, mode)
+             ? DS4G_ERR_UNSUPPORTED
+             : DS4G_OK;
 }
 
 int ds4g_lmhead_sample_ex(int32_t hidden, int32_t vocab, int32_t wdtype, const void* final_norm,
@@ -484,9 +531,8 @@ int ds4g_lmhead_sample_ex(int32_t hidden, int32_t vocab, int32_t wdtype, const v
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
   if (hidden % 8 || hidden > 16384 || vocab > (1 << 18)) return DS4G_ERR_UNSUPPORTED;
   if (ws_bytes < sample_ws_bytes(vocab)) return DS4G_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+  return dry_then_run((hipStream_t)stream, [&](Exec st) {
   int rc = 0;
-  clear_stale_error();
   {
     GemvArgs g{};
     g.W = w_lm; g.N = vocab; g.K = hidden; g.x = x; g.gamma = final_norm; g.eps = rms_eps;
@@ -500,7 +546,8 @@ int ds4g_lmhead_sample_ex(int32_t hidden, int32_t vocab, int32_t wdtype, const v
   rc |= launch_sample(sa, st);
   if (embed_table)
     rc |= launch_embed(embed_table, wdtype == DS4G_BF16, token, 1, vocab, hidden, x_next, st);
-  return hip_status(rc);
+  return rc;
+  });
 }
 
 int ds4g_lmhead_sample(int32_t hidden, int32_t vocab, int32_t wdtype, const void* final_norm,
@@ -518,10 +565,9 @@ int ds4g_embed(int32_t vocab, int32_t hidden, int32_t wdtype, const void* table,
   if (vocab <= 0 || hidden <= 0 || T <= 0 || !table || !ids || !x) return DS4G_ERR_INVALID_ARG;
   if (wdtype != DS4G_F32 && wdtype != DS4G_BF16) return DS4G_ERR_INVALID_ARG;
   if (hidden % 8) return DS4G_ERR_UNSUPPORTED;
-  clear_stale_error();
-  const int rc = launch_embed(table, wdtype == DS4G_BF16, ids, T, vocab, hidden, x,
-                              (hipStream_t)stream);
-  return hip_status(rc);
+  return dry_then_run((hipStream_t)stream, [&](Exec ex) {
+    return launch_embed(table, wdtype == DS4G_BF16, ids, T, vocab, hidden, x, ex);
+  });
 }
 
 const char* ds4g_status_string(int status) {

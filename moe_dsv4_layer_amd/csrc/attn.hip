@@ -164,24 +164,24 @@ ring_commit_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__
 }
 __global__ void ring_advance_kernel(int64_t* pos, int T) { *pos += T; }
 
-static void ring_commit(const AttnArgs& a, hipStream_t st) {
+static void ring_commit(const AttnArgs& a, Exec st) {
   const int cnt = a.T < a.W ? a.T : a.W;
-  hipLaunchKernelGGL(ring_commit_kernel, dim3(cnt), dim3(64), 0, st, a.kc, a.vc, a.T, a.W, a.dh,
+  DS4G_LAUNCH(ring_commit_kernel, dim3(cnt), dim3(64), 0, st, a.kc, a.vc, a.T, a.W, a.dh,
                      a.ring_k, a.ring_v, a.pos);
-  hipLaunchKernelGGL(ring_advance_kernel, dim3(1), dim3(1), 0, st, a.pos, a.T);
+  DS4G_LAUNCH(ring_advance_kernel, dim3(1), dim3(1), 0, st, a.pos, a.T);
 }
 
-int launch_attention(const AttnArgs& a, hipStream_t st) {
+int launch_attention(const AttnArgs& a, Exec st) {
   if (a.q_bf16)
-    hipLaunchKernelGGL((rope_qkv_kernel<uint16_t>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
+    DS4G_LAUNCH((rope_qkv_kernel<uint16_t>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
                        a.dh, a.rd, a.base, a.pos, (uint16_t*)a.q, a.kc, a.vc);
   else
-    hipLaunchKernelGGL((rope_qkv_kernel<float>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
+    DS4G_LAUNCH((rope_qkv_kernel<float>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
                        a.dh, a.rd, a.base, a.pos, (float*)a.q, a.kc, a.vc);
   const int HG = a.heads_per_block;
   dim3 grid(a.T, (a.H + HG - 1) / HG);
 #define DS4G_ATT(OT, DH)                                                                      \
-  hipLaunchKernelGGL((attn_window_kernel<OT, DH>), grid, dim3(256), 0, st, (const float*)a.q, \
+  DS4G_LAUNCH((attn_window_kernel<OT, DH>), grid, dim3(256), 0, st, (const float*)a.q, \
                      a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, HG, (OT*)a.o)
   if (a.dh == 128) {
     if (a.o_bf16) DS4G_ATT(uint16_t, 128); else DS4G_ATT(float, 128);
@@ -363,25 +363,25 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
   }
 }
 
-int launch_attention_decode(const AttnArgs& a, hipStream_t st) {
+int launch_attention_decode(const AttnArgs& a, Exec st) {
   const dim3 grid(a.H);
   if (a.dh == 128)
-    hipLaunchKernelGGL((attn_decode_kernel<128, float>), grid, dim3(256), 0, st, a.qkv, 0L, a.H,
+    DS4G_LAUNCH((attn_decode_kernel<128, float>), grid, dim3(256), 0, st, a.qkv, 0L, a.H,
                        a.W, a.rd, a.base, a.pos, a.ring_k, a.ring_v, (float*)a.o);
   else if (a.dh == 64)
-    hipLaunchKernelGGL((attn_decode_kernel<64, float>), grid, dim3(256), 0, st, a.qkv, 0L, a.H,
+    DS4G_LAUNCH((attn_decode_kernel<64, float>), grid, dim3(256), 0, st, a.qkv, 0L, a.H,
                        a.W, a.rd, a.base, a.pos, a.ring_k, a.ring_v, (float*)a.o);
   else
     return -1;
   return 0;
 }
 
-int launch_attention_decode_batch(const AttnArgs& a, int B, hipStream_t st) {
+int launch_attention_decode_batch(const AttnArgs& a, int B, Exec st) {
   if (B <= 0 || B > 65535) return -1;
   const dim3 grid(a.H, B);
   const long stride = (long)a.H * a.dh + 2L * a.dh;
 #define DS4G_AD(DH, OT)                                                                       \
-  hipLaunchKernelGGL((attn_decode_kernel<DH, OT>), grid, dim3(256), 0, st, a.qkv, stride, a.H, \
+  DS4G_LAUNCH((attn_decode_kernel<DH, OT>), grid, dim3(256), 0, st, a.qkv, stride, a.H, \
                      a.W, a.rd, a.base, a.pos, a.ring_k, a.ring_v, (OT*)a.o)
   if (a.dh == 128) {
     if (a.o_bf16) DS4G_AD(128, uint16_t); else DS4G_AD(128, float);
@@ -642,26 +642,26 @@ rope_table_kernel(const int64_t* __restrict__ pos, int T, int ld, int rd, float 
 }
 
 int launch_rope_table(const int64_t* pos, int T, int ld, int rd, float base, float* c, float* s,
-                      hipStream_t st) {
+                      Exec st) {
   if (ld < T || ld % 4 || rd < 2) return -1;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((ld + 255) / 256, rd / 2), dim3(256), 0, st, pos, T,
+  DS4G_LAUNCH(rope_table_kernel, dim3((ld + 255) / 256, rd / 2), dim3(256), 0, st, pos, T,
                      ld, rd, base, c, s);
   return 0;
 }
 
-int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st) {
+int launch_attention_prefill_mfma(const AttnArgs& a, Exec st) {
   if (a.W > 128 || !a.q_bf16 || !a.o_bf16) return -1;
   if (!a.rope_done)   // else the QKV GEMM's epilogue wrote rotated q, kc, vc
-    hipLaunchKernelGGL((rope_qkv_kernel<uint16_t>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
+    DS4G_LAUNCH((rope_qkv_kernel<uint16_t>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
                        a.dh, a.rd, a.base, a.pos, (uint16_t*)a.q, a.kc, a.vc);
   // spans are aligned to absolute positions: one extra span covers the
   // unknown (device-side) offset of the first position within its span
   const dim3 grid((a.T + 15) / 16 + 1, (a.H + 31) / 32);
   if (a.dh == 128)
-    hipLaunchKernelGGL((attn_prefill_mfma<128>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
+    DS4G_LAUNCH((attn_prefill_mfma<128>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
                        a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
   else if (a.dh == 64)
-    hipLaunchKernelGGL((attn_prefill_mfma<64>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
+    DS4G_LAUNCH((attn_prefill_mfma<64>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
                        a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, (uint16_t*)a.o);
   else
     return -1;

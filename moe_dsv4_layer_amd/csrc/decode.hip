@@ -164,7 +164,7 @@ gemv_kernel(GemvArgs a) {
 }
 
 template <typename WT>
-int launch_gemv(const GemvArgs& a, hipStream_t st) {
+int launch_gemv(const GemvArgs& a, Exec st) {
   const int nchunk = a.K / 8;
   const int N = a.N;
 #define DS4G_GEMV(KS, C, R)                                                            \
@@ -172,7 +172,7 @@ int launch_gemv(const GemvArgs& a, hipStream_t st) {
     const int rpb = R * (4 / KS);                                                      \
     int grid = (N + rpb - 1) / rpb;                                                    \
     if (grid > DS4G_GEMV_GRID_MAX) grid = DS4G_GEMV_GRID_MAX;                          \
-    hipLaunchKernelGGL((gemv_kernel<WT, KS, C, R>), dim3(grid), dim3(256), 0, st, a); \
+    DS4G_LAUNCH((gemv_kernel<WT, KS, C, R>), dim3(grid), dim3(256), 0, st, a); \
     return 0;                                                                          \
   }
   if (nchunk <= 64) DS4G_GEMV(1, 1, 2)          // K <= 512
@@ -184,8 +184,8 @@ int launch_gemv(const GemvArgs& a, hipStream_t st) {
 #undef DS4G_GEMV
   return -1;
 }
-template int launch_gemv<uint16_t>(const GemvArgs&, hipStream_t);
-template int launch_gemv<float>(const GemvArgs&, hipStream_t);
+template int launch_gemv<uint16_t>(const GemvArgs&, Exec);
+template int launch_gemv<float>(const GemvArgs&, Exec);
 
 // ---------------------------------------------------------------------------
 // Multi-row GEMV: the dense projections of a batched decode call (M <= 8
@@ -301,20 +301,20 @@ gemv_rows_kernel(GemvRowsArgs a) {
 }
 
 template <int MR, bool DUAL>
-int launch_gemv_rows_mr(const GemvRowsArgs& a, hipStream_t st) {
+int launch_gemv_rows_mr(const GemvRowsArgs& a, Exec st) {
   constexpr int RB = 2;
   auto go = [&](auto kern, int ksplit) {
     const int rpb = RB * (4 / ksplit);
     long grid = (a.N + rpb - 1) / rpb;
     if (grid > DS4G_GEMV_GRID_MAX) grid = DS4G_GEMV_GRID_MAX;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, a);
+    DS4G_LAUNCH(kern, dim3((unsigned)grid), dim3(256), 0, st, a);
     return 0;
   };
   if (a.K <= 1024) return go(gemv_rows_kernel<MR, 1, 2, RB, DUAL>, 1);
   return go(gemv_rows_kernel<MR, 4, 2, RB, DUAL>, 4);
 }
 
-int launch_gemv_rows(const GemvRowsArgs& a, hipStream_t st) {
+int launch_gemv_rows(const GemvRowsArgs& a, Exec st) {
   const bool dual = a.epi == EPI_SWIGLU_BF16;
   // K <= 4096: with 8 rows, a wider K slice per lane (K = 8192, W_o) needs
   // ~330-390 VGPRs, one wave per SIMD, and streamed at half the split-K
@@ -702,7 +702,7 @@ moe_down_decode(MoeDecodeArgs a, float* x, int64_t* pos_inc) {
 }
 
 template <typename WT>
-int launch_moe_decode(const MoeDecodeArgs& a0, float* x, int64_t* pos_inc, hipStream_t st) {
+int launch_moe_decode(const MoeDecodeArgs& a0, float* x, int64_t* pos_inc, Exec st) {
   if (a0.k > 8 || a0.E > 512 || a0.d % 8 || a0.I % 8 || a0.Is % 8) return -1;
   const int nchunk = a0.d / 8;
   const int cpl = (nchunk + 255) / 256;      // K = d over 4 waves
@@ -714,7 +714,7 @@ int launch_moe_decode(const MoeDecodeArgs& a0, float* x, int64_t* pos_inc, hipSt
   {
     constexpr int RB = DS4G_ROUTER_SHARED_RB;
     const int ng = (a.E + RB - 1) / RB + (a.Is + RB - 1) / RB;
-#define DS4G_RS(C) hipLaunchKernelGGL((router_shared_decode<WT, C, RB>), dim3(ng), dim3(256), 0, st, a)
+#define DS4G_RS(C) DS4G_LAUNCH((router_shared_decode<WT, C, RB>), dim3(ng), dim3(256), 0, st, a)
     if (cpl == 1) DS4G_RS(1); else if (cpl == 2) DS4G_RS(2); else DS4G_RS(4);
 #undef DS4G_RS
   }
@@ -727,7 +727,7 @@ int launch_moe_decode(const MoeDecodeArgs& a0, float* x, int64_t* pos_inc, hipSt
     int grid = (ntask + RB - 1) / RB;
     if (grid > DS4G_GATEUP_GRID_MAX) grid = DS4G_GATEUP_GRID_MAX;
     grid += a.nsd;
-#define DS4G_GU(C, C2) hipLaunchKernelGGL((moe_gateup_decode<WT, C, RB, C2>), dim3(grid), dim3(256), 0, st, a)
+#define DS4G_GU(C, C2) DS4G_LAUNCH((moe_gateup_decode<WT, C, RB, C2>), dim3(grid), dim3(256), 0, st, a)
 #define DS4G_GU2(C) { if (cpls == 1) DS4G_GU(C, 1); else if (cpls == 2) DS4G_GU(C, 2); else DS4G_GU(C, 4); }
     if (cpl == 1) DS4G_GU2(1) else if (cpl == 2) DS4G_GU2(2) else DS4G_GU2(4)
 #undef DS4G_GU2
@@ -737,13 +737,13 @@ int launch_moe_decode(const MoeDecodeArgs& a0, float* x, int64_t* pos_inc, hipSt
   {
     constexpr int RB2 = DS4G_DOWN_RB;
     const int grid2 = (a.d + RB2 - 1) / RB2;
-#define DS4G_DN(C) hipLaunchKernelGGL((moe_down_decode<WT, C, RB2>), dim3(grid2), dim3(512), 0, st, a, x, pos_inc)
+#define DS4G_DN(C) DS4G_LAUNCH((moe_down_decode<WT, C, RB2>), dim3(grid2), dim3(512), 0, st, a, x, pos_inc)
     if (cpld == 1) DS4G_DN(1); else if (cpld == 2) DS4G_DN(2); else DS4G_DN(4);
 #undef DS4G_DN
   }
   return 0;
 }
-template int launch_moe_decode<uint16_t>(const MoeDecodeArgs&, float*, int64_t*, hipStream_t);
-template int launch_moe_decode<float>(const MoeDecodeArgs&, float*, int64_t*, hipStream_t);
+template int launch_moe_decode<uint16_t>(const MoeDecodeArgs&, float*, int64_t*, Exec);
+template int launch_moe_decode<float>(const MoeDecodeArgs&, float*, int64_t*, Exec);
 
 }  // namespace ds4g

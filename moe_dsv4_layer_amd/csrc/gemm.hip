@@ -447,7 +447,7 @@ gemm_dma_kernel(GemmArgs g) {
 }
 
 template <int BM, int BN, int WM, int WN, int S>
-int launch_dma_cfg(const GemmArgs& g, hipStream_t st) {
+int launch_dma_cfg(const GemmArgs& g, Exec st) {
   const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
   const int bn_out = dual ? BN / 2 : BN;
   const int mt = g.tiles ? g.max_tiles : (g.M + BM - 1) / BM;
@@ -455,21 +455,21 @@ int launch_dma_cfg(const GemmArgs& g, hipStream_t st) {
   const dim3 grid((g.N + bn_out - 1) / bn_out, mt, nsplit), block(64 * WM * WN);
   switch (g.epi) {
     case EPI_F32:
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_F32>), grid, block, 0, st, g);
+      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_F32>), grid, block, 0, st, g);
       break;
     case EPI_BF16:
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_BF16>), grid, block, 0, st, g);
+      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_BF16>), grid, block, 0, st, g);
       break;
     case EPI_RESID:
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_RESID>), grid, block, 0, st, g);
+      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_RESID>), grid, block, 0, st, g);
       break;
     case EPI_SWIGLU_BF16:
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_SWIGLU_BF16>), grid, block, 0, st,
+      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_SWIGLU_BF16>), grid, block, 0, st,
                          g);
       break;
     case EPI_ROPE_QKV:
       if (g.tiles || nsplit > 1) return -1;
-      hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_ROPE_QKV>), grid, block, 0, st, g);
+      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_ROPE_QKV>), grid, block, 0, st, g);
       break;
     default: return -1;
   }
@@ -520,16 +520,16 @@ splitk_reduce_kernel(const float* __restrict__ part, const float* __restrict__ p
 }
 
 int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long pstride, int M,
-                         int N, int epi, void* C, int ldc, hipStream_t st) {
+                         int N, int epi, void* C, int ldc, Exec st) {
   if (epi != EPI_F32 && epi != EPI_BF16 && epi != EPI_RESID && epi != EPI_SWIGLU_BF16) return -1;
   if (epi == EPI_SWIGLU_BF16 && !part2) return -1;
   const long n = (long)M * N;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, st,
+  DS4G_LAUNCH(splitk_reduce_kernel, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, st,
                      part, part2, nsplit, pstride, M, N, epi, C, ldc);
   return 0;
 }
 
-int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
+int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, Exec st) {
   const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
   if (mfma) {
     const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
@@ -586,11 +586,11 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st) {
     const int mt = g.tiles ? g.max_tiles : (g.M + 63) / 64;
     dim3 grid((g.N + 63) / 64, mt, nsplit);
     if (wdtype_bf16) {
-      if (dual) hipLaunchKernelGGL((gemm_simt_kernel<uint16_t, true>), grid, dim3(256), 0, st, g);
-      else hipLaunchKernelGGL((gemm_simt_kernel<uint16_t, false>), grid, dim3(256), 0, st, g);
+      if (dual) DS4G_LAUNCH((gemm_simt_kernel<uint16_t, true>), grid, dim3(256), 0, st, g);
+      else DS4G_LAUNCH((gemm_simt_kernel<uint16_t, false>), grid, dim3(256), 0, st, g);
     } else {
-      if (dual) hipLaunchKernelGGL((gemm_simt_kernel<float, true>), grid, dim3(256), 0, st, g);
-      else hipLaunchKernelGGL((gemm_simt_kernel<float, false>), grid, dim3(256), 0, st, g);
+      if (dual) DS4G_LAUNCH((gemm_simt_kernel<float, true>), grid, dim3(256), 0, st, g);
+      else DS4G_LAUNCH((gemm_simt_kernel<float, false>), grid, dim3(256), 0, st, g);
     }
   }
   return 0;

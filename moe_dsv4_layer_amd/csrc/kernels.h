@@ -5,6 +5,19 @@
 
 namespace ds4g {
 
+// Where a launcher enqueues its kernels.  With dry set it only checks its
+// preconditions and returns their verdict (0 or -1) without enqueuing
+// anything: the C ABI runs every call's whole launch sequence dry first, so
+// a shape some launcher cannot handle is rejected before any kernel runs.
+struct Exec {
+  hipStream_t stream;
+  bool dry;
+};
+#define DS4G_LAUNCH(kern, grid, block, shm, ex, ...)                              \
+  do {                                                                           \
+    if (!(ex).dry) hipLaunchKernelGGL(kern, grid, block, shm, (ex).stream, __VA_ARGS__); \
+  } while (0)
+
 // ---------------------------------------------------------------- GEMM
 enum Epi {
   EPI_F32 = 0,          // C[r, n] = acc                      (fp32)
@@ -51,13 +64,13 @@ struct GemmArgs {
 // cos / sin of pair i for rows t < T at position *pos + t into c / s
 // [i * ld + t] (rows T..ld-1: 1 and 0), i < rd / 2
 int launch_rope_table(const int64_t* pos, int T, int ld, int rd, float base, float* c, float* s,
-                      hipStream_t st);
-int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, hipStream_t st);
+                      Exec st);
+int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, Exec st);
 // sum of nsplit fp32 partials part[s * pstride + m * N + n] in split order,
 // then the epilogue epi (F32, BF16, RESID: C += sum, SWIGLU_BF16: part2 holds
 // the up projection's partials) into C [M, ldc]
 int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long pstride, int M,
-                         int N, int epi, void* C, int ldc, hipStream_t st);
+                         int N, int epi, void* C, int ldc, Exec st);
 
 // ---------------------------------------------------------------- GEMV
 // out[n] (= or +=) sum_k W[n, k] xs[k], xs = x or RMSNorm(x) * gamma.
@@ -72,7 +85,7 @@ struct GemvArgs {
   float* router_in;     // optional copy of xs (block 0)
 };
 template <typename WT>
-int launch_gemv(const GemvArgs& a, hipStream_t st);
+int launch_gemv(const GemvArgs& a, Exec st);
 
 // out[m, n] = sum_k W[n, k] X[m, k] for the M <= 8 rows of a batched decode
 // call: W [N, K] bf16 (row stride K), X [M, K] bf16 (row stride lda).  epi:
@@ -89,7 +102,7 @@ struct GemvRowsArgs {
   void* C;
   int ldc;
 };
-int launch_gemv_rows(const GemvRowsArgs& a, hipStream_t st);
+int launch_gemv_rows(const GemvRowsArgs& a, Exec st);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
@@ -108,16 +121,16 @@ struct AttnArgs {
   int heads_per_block;
   int rope_done;        // MFMA prefill: q, kc, vc already rotated (QKV GEMM epilogue)
 };
-int launch_attention(const AttnArgs& a, hipStream_t st);
+int launch_attention(const AttnArgs& a, Exec st);
 // single-token attention: RoPE of q/k at *pos, write (k, v) to the ring
 // slot, attend over the window; o fp32 [H*dh].  Does not advance *pos.
-int launch_attention_decode(const AttnArgs& a, hipStream_t st);
+int launch_attention_decode(const AttnArgs& a, Exec st);
 // B independent sequences, one token each: row b of qkv at position pos[b],
 // ring b at ring_k / ring_v + b * W * dh; o [B, H*dh] fp32 or bf16 (o_bf16).
 // Does not advance pos (the layer's last kernel, the combine, does).
-int launch_attention_decode_batch(const AttnArgs& a, int B, hipStream_t st);
+int launch_attention_decode_batch(const AttnArgs& a, int B, Exec st);
 // prefill on the matrix cores: bf16 q (q_bf16 = 1) and o (o_bf16 = 1)
-int launch_attention_prefill_mfma(const AttnArgs& a, hipStream_t st);
+int launch_attention_prefill_mfma(const AttnArgs& a, Exec st);
 
 // ---------------------------------------------------------------- decode MoE
 struct MoeDecodeArgs {
@@ -140,12 +153,12 @@ struct MoeDecodeArgs {
 // router logits + shared expert, routed gate/up (+ shared down), routed down
 // + combine + residual: three launches
 template <typename WT>
-int launch_moe_decode(const MoeDecodeArgs& a, float* x, int64_t* pos_inc, hipStream_t st);
+int launch_moe_decode(const MoeDecodeArgs& a, float* x, int64_t* pos_inc, Exec st);
 
 // ---------------------------------------------------------------- prefill misc
 template <typename WT>
 int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps,
-                        float* out_f32, uint16_t* out_bf16, uint16_t* out_split3, hipStream_t st);
+                        float* out_f32, uint16_t* out_bf16, uint16_t* out_split3, Exec st);
 
 struct RouteArgs {
   const float* logits;  // nsplit partial sums [nsplit][T][E], added in order
@@ -166,12 +179,12 @@ struct RouteArgs {
   // optional user copies
   int* out_count; int* out_offset;
 };
-int launch_route(const RouteArgs& r, hipStream_t st);
+int launch_route(const RouteArgs& r, Exec st);
 // x[t] += sum_j w[t,j] part[pos_of[t*k+j]] (fixed j order); part is fp32, or bf16
 // when part_bf16 (the bf16 path rounds each routed expert output to bf16).
 // pos_inc (optional, batched decode): pos_inc[t] += 1 for every row t.
 int launch_moe_combine(float* x, const void* part, int part_bf16, const int* pos_of,
-                       const float* w, int T, int d, int k, int64_t* pos_inc, hipStream_t st);
+                       const float* w, int T, int d, int k, int64_t* pos_inc, Exec st);
 
 // ---------------------------------------------------------------- sampler
 struct SampleArgs {
@@ -185,7 +198,7 @@ struct SampleArgs {
 };
 size_t sample_ws_bytes(int V);
 int launch_embed(const void* table, int wdtype_bf16, const int* ids, int T, int vocab, int hidden,
-                 float* x, hipStream_t st);
-int launch_sample(const SampleArgs& s, hipStream_t st);
+                 float* x, Exec st);
+int launch_sample(const SampleArgs& s, Exec st);
 
 }  // namespace ds4g

@@ -85,16 +85,16 @@ rmsnorm_rows_kernel(const float* __restrict__ x, int d, const WT* __restrict__ g
 
 template <typename WT>
 int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps, float* of,
-                        uint16_t* ob, uint16_t* os3, hipStream_t st) {
+                        uint16_t* ob, uint16_t* os3, Exec st) {
   if (d % 4 || d > 1024 * RMS_CHUNKS) return -1;
-  hipLaunchKernelGGL((rmsnorm_rows_kernel<WT>), dim3(T), dim3(256), 0, st, x, d, gamma, eps, of,
+  DS4G_LAUNCH((rmsnorm_rows_kernel<WT>), dim3(T), dim3(256), 0, st, x, d, gamma, eps, of,
                      ob, os3);
   return 0;
 }
 template int launch_rmsnorm_rows<uint16_t>(const float*, int, int, const uint16_t*, float,
-                                           float*, uint16_t*, uint16_t*, hipStream_t);
+                                           float*, uint16_t*, uint16_t*, Exec);
 template int launch_rmsnorm_rows<float>(const float*, int, int, const float*, float, float*,
-                                        uint16_t*, uint16_t*, hipStream_t);
+                                        uint16_t*, uint16_t*, Exec);
 
 // ------------------------------------------------------------ top-k per token
 // One wave per token: k rounds of a wave arg-max (lower index wins ties) over
@@ -288,14 +288,14 @@ route_scatter_kernel(RouteArgs r) {
   }
 }
 
-int launch_route(const RouteArgs& r, hipStream_t st) {
+int launch_route(const RouteArgs& r, Exec st) {
   if (r.E > 512 || r.k > 8) return -1;
-  hipLaunchKernelGGL(topk_kernel, dim3((r.T + 3) / 4), dim3(256), 0, st, r.logits, r.nsplit,
+  DS4G_LAUNCH(topk_kernel, dim3((r.T + 3) / 4), dim3(256), 0, st, r.logits, r.nsplit,
                      r.logits_sum, r.T, r.E, r.k, r.topk_idx, r.topk_w);
-  hipLaunchKernelGGL(expert_rank_kernel, dim3(r.E), dim3(1024), 0, st, r.topk_idx, r.T, r.k,
+  DS4G_LAUNCH(expert_rank_kernel, dim3(r.E), dim3(1024), 0, st, r.topk_idx, r.T, r.k,
                      r.rank, r.count);
   const int nent = r.T * r.k;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3((nent + 255) / 256), dim3(256), 0, st, r);
+  DS4G_LAUNCH(route_scatter_kernel, dim3((nent + 255) / 256), dim3(256), 0, st, r);
   return 0;
 }
 
@@ -336,13 +336,13 @@ moe_combine_kernel(float* __restrict__ x, const PT* __restrict__ part,
 }
 
 int launch_moe_combine(float* x, const void* part, int part_bf16, const int* pos_of,
-                       const float* w, int T, int d, int k, int64_t* pos_inc, hipStream_t st) {
+                       const float* w, int T, int d, int k, int64_t* pos_inc, Exec st) {
   if (d % 4 || k > 8) return -1;
   if (part_bf16)
-    hipLaunchKernelGGL(moe_combine_kernel<uint16_t>, dim3(T), dim3(256), 0, st, x,
+    DS4G_LAUNCH(moe_combine_kernel<uint16_t>, dim3(T), dim3(256), 0, st, x,
                        static_cast<const uint16_t*>(part), pos_of, w, d, k, pos_inc);
   else
-    hipLaunchKernelGGL(moe_combine_kernel<float>, dim3(T), dim3(256), 0, st, x,
+    DS4G_LAUNCH(moe_combine_kernel<float>, dim3(T), dim3(256), 0, st, x,
                        static_cast<const float*>(part), pos_of, w, d, k, pos_inc);
   return 0;
 }

@@ -482,25 +482,25 @@ samp_pick_kernel(int V, int nb, SampWs w, int* token, float temperature, const f
   }
 }
 
-int launch_sample(const SampleArgs& s, hipStream_t st) {
+int launch_sample(const SampleArgs& s, Exec st) {
   const int nb = (s.V + SEG - 1) / SEG;
   if (nb > 1024 || s.V > (1 << 18)) return -1;
   SampWs w = carve(s.ws, s.V);
   const float T = s.temperature;
   const float* td = s.temperature_dev;
-  hipLaunchKernelGGL(samp_max_kernel, dim3(nb), dim3(256), 0, st, s.logits, s.V, w);
+  DS4G_LAUNCH(samp_max_kernel, dim3(nb), dim3(256), 0, st, s.logits, s.V, w);
   // a host temperature picks the path here; a device one, inside every kernel
   if (td || !(T > 0.f))
-    hipLaunchKernelGGL(samp_argmax_kernel, dim3(1), dim3(64), 0, st, nb, w, s.token, T, td);
+    DS4G_LAUNCH(samp_argmax_kernel, dim3(1), dim3(64), 0, st, nb, w, s.token, T, td);
   if (!td && !(T > 0.f)) return 0;
-  hipLaunchKernelGGL(samp_q_kernel, dim3((nb + QSEGS - 1) / QSEGS), dim3(1024), 0, st, s.logits,
+  DS4G_LAUNCH(samp_q_kernel, dim3((nb + QSEGS - 1) / QSEGS), dim3(1024), 0, st, s.logits,
                      s.V, nb, T, td, w);
-  hipLaunchKernelGGL(samp_level1_kernel, dim3(1), dim3(1024), 0, st, s.top_p, w, T, td);
-  hipLaunchKernelGGL(samp_hist2_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
-  hipLaunchKernelGGL(samp_l2sum_kernel, dim3(NB2 / 1024), dim3(256), 0, st, w, T, td);
-  hipLaunchKernelGGL(samp_level2_kernel, dim3(1), dim3(1024), 0, st, w, s.rng, s.min_p, T, td);
-  hipLaunchKernelGGL(samp_segsum_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
-  hipLaunchKernelGGL(samp_pick_kernel, dim3(1), dim3(1024), 0, st, s.V, nb, w, s.token, T, td);
+  DS4G_LAUNCH(samp_level1_kernel, dim3(1), dim3(1024), 0, st, s.top_p, w, T, td);
+  DS4G_LAUNCH(samp_hist2_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
+  DS4G_LAUNCH(samp_l2sum_kernel, dim3(NB2 / 1024), dim3(256), 0, st, w, T, td);
+  DS4G_LAUNCH(samp_level2_kernel, dim3(1), dim3(1024), 0, st, w, s.rng, s.min_p, T, td);
+  DS4G_LAUNCH(samp_segsum_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
+  DS4G_LAUNCH(samp_pick_kernel, dim3(1), dim3(1024), 0, st, s.V, nb, w, s.token, T, td);
   return 0;
 }
 
@@ -529,13 +529,13 @@ embed_kernel(const WT* __restrict__ table, const int* __restrict__ ids, int voca
 }
 
 int launch_embed(const void* table, int wdtype_bf16, const int* ids, int T, int vocab, int hidden,
-                 float* x, hipStream_t st) {
+                 float* x, Exec st) {
   if (hidden % 8 || T <= 0) return -1;
   if (wdtype_bf16)
-    hipLaunchKernelGGL((embed_kernel<uint16_t>), dim3(T), dim3(256), 0, st,
+    DS4G_LAUNCH((embed_kernel<uint16_t>), dim3(T), dim3(256), 0, st,
                        (const uint16_t*)table, ids, vocab, hidden, x);
   else
-    hipLaunchKernelGGL((embed_kernel<float>), dim3(T), dim3(256), 0, st, (const float*)table, ids,
+    DS4G_LAUNCH((embed_kernel<float>), dim3(T), dim3(256), 0, st, (const float*)table, ids,
                        vocab, hidden, x);
   return 0;
 }

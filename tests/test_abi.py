@@ -146,3 +146,114 @@ def test_sample_ex_rejects_before_launch():
     # a device temperature may ask for sampling at run time: the generator is required
     assert call(P(0.0, 0.95, 0.0, 0x1000), rng=None) == ds4g.ERR_INVALID_ARG
     assert call(P(0.7, float("nan"), 0.0, None)) == ds4g.ERR_INVALID_ARG
+
+
+def _decode(cfg, nbytes):
+    w = _weights()
+    ring = ds4g.KvRing(0x1000, 0x1000, 0x1000)
+    return ds4g.lib.ds4g_layer_decode(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ring),
+                                      0x1000, None, 0x1000, nbytes, None)
+
+
+def _batch(cfg, B, nbytes):
+    w = _weights()
+    ring = ds4g.KvRing(0x1000, 0x1000, 0x1000)
+    return ds4g.lib.ds4g_layer_decode_batch(ctypes.byref(cfg), ctypes.byref(w),
+                                            ctypes.byref(ring), 0x1000, B, None, 0x1000, nbytes,
+                                            None)
+
+
+def test_decode_rejects_hidden_past_its_kernels():
+    # the decode MoE kernels hold a wave's K slice of y in registers: hidden
+    # <= 8192.  A wider layer passes the dimension checks (prefill takes it)
+    # and must be refused before the first launch, not after QKV and W_o ran.
+    c = _cfg(hidden=16384)
+    assert ds4g.layer_supported(c, 1, ds4g.MODE_DECODE) == ds4g.ERR_UNSUPPORTED
+    assert ds4g.layer_supported(c, 64, ds4g.MODE_PREFILL) == ds4g.OK
+    assert _decode(c, 1 << 62) == ds4g.ERR_UNSUPPORTED
+    assert ds4g.layer_supported(_cfg(hidden=8192), 1, ds4g.MODE_DECODE) == ds4g.OK
+
+
+def test_batch_rejects_past_32bit_operand_offsets():
+    # the MFMA GEMMs address 16-bit operands with 32-bit byte offsets; the
+    # router operand of B rows is B x 3*hidden bf16 (4.9 GB at B = 50000)
+    c = _cfg(hidden=16384)
+    assert ds4g.layer_supported(c, 50000, ds4g.MODE_DECODE_BATCH) == ds4g.ERR_UNSUPPORTED
+    assert _batch(c, 50000, 1 << 62) == ds4g.ERR_UNSUPPORTED
+    assert ds4g.layer_supported(c, 40000, ds4g.MODE_DECODE_BATCH) == ds4g.OK
+    assert ds4g.layer_supported(_cfg(), 65536, ds4g.MODE_DECODE_BATCH) == ds4g.ERR_UNSUPPORTED
+
+
+def _documented(c, T, mode):
+    """The support matrix the header states (ds4g_layer_cfg's comment)."""
+    rd = c.rope_dim or c.head_dim
+    qd = c.n_heads * c.head_dim
+    ok = (c.head_dim in (64, 128) and rd % 2 == 0 and rd <= c.head_dim and 1 <= c.window <= 128
+          and c.top_k + 1 <= c.n_experts <= 512 and 1 <= c.top_k <= 8 and c.n_heads % 4 == 0
+          and all(v % 64 == 0 for v in (c.hidden, c.qkv_rank, c.ffn_inter, c.shared_inter, qd))
+          and max(c.hidden, c.qkv_rank, qd) <= 16384 and max(c.ffn_inter, c.shared_inter) <= 2048
+          and c.top_k * c.ffn_inter + c.shared_inter <= 12288)
+    if mode == ds4g.MODE_DECODE:
+        ok = ok and c.hidden <= 8192
+    if mode == ds4g.MODE_DECODE_BATCH:
+        ok = ok and T <= 65535
+    if c.wdtype == ds4g.BF16:
+        widest = max(3 * c.hidden, qd, c.qkv_rank, c.shared_inter, c.top_k * c.ffn_inter)
+        ok = ok and T * widest * 2 < 2 ** 32
+    return ok and T * c.top_k < 2 ** 24 and T <= 2 ** 20
+
+
+def test_support_matrix_sweep():
+    """Every configuration inside the documented limits is accepted by the
+    launch sequence of each call (no kernel launcher refuses it), every one
+    outside is refused, and a refused shape is refused by the call itself
+    before anything is launched (these calls run without a GPU: a call that
+    got as far as a launch would report a HIP error instead)."""
+    import itertools
+    n = 0
+    for hidden, dh, window, E, k, inter, wd, rope, heads in itertools.product(
+            (256, 4096, 8192, 16384), (64, 96, 128), (1, 128, 129), (8, 256, 512, 600),
+            (1, 6, 8, 9), (64, 512, 2048, 4096), (ds4g.F32, ds4g.BF16), (0, 32, 33), (4, 64, 6)):
+        c = _cfg(hidden=hidden, head_dim=dh, window=window, n_experts=E, top_k=k,
+                 ffn_inter=inter, shared_inter=inter, wdtype=wd, rope_dim=rope, n_heads=heads)
+        for T, mode in ((1, ds4g.MODE_DECODE), (1, ds4g.MODE_PREFILL), (300, ds4g.MODE_PREFILL),
+                        (16994, ds4g.MODE_PREFILL), (8, ds4g.MODE_DECODE_BATCH),
+                        (128, ds4g.MODE_DECODE_BATCH)):
+            st = ds4g.layer_supported(c, T, mode)
+            want = _documented(c, T, mode)
+            assert (st == ds4g.OK) == want, (hidden, dh, window, E, k, inter, wd, rope, heads, T,
+                                             mode, st)
+            if st != ds4g.OK and n % 7 == 0:    # a sample of refusals through the calls
+                if mode == ds4g.MODE_DECODE:
+                    assert _decode(c, 1 << 62) == st
+                elif mode == ds4g.MODE_PREFILL:
+                    ring = ds4g.KvRing(0x1000, 0x1000, 0x1000)
+                    assert _prefill(c, _weights(), ring, 0x1000, T, 0x1000, 1 << 62) == st
+                else:
+                    assert _batch(c, T, 1 << 62) == st
+            n += 1
+    assert n > 10000
+
+
+def test_binding_refuses_two_hip_runtimes():
+    """The binding imports torch (and its HIP runtime) before the library, and
+    refuses to load when a second runtime has been mapped: a fresh process
+    that maps /opt/rocm's runtime first must get an ImportError naming both."""
+    import subprocess
+    import sys
+    rocm = "/opt/rocm/lib/libamdhip64.so"
+    if not os.path.exists(rocm):
+        pytest.skip("no /opt/rocm runtime in this image")
+    code = ("import ctypes, sys; ctypes.CDLL(%r, mode=ctypes.RTLD_GLOBAL)\n"
+            "sys.path.insert(0, %r)\n"
+            "try:\n    import moe_dsv4_layer_amd\nexcept ImportError as e:\n"
+            "    print('REFUSED', e); sys.exit(0)\n"
+            "print('LOADED', moe_dsv4_layer_amd._hip_runtimes())\n") % (rocm, ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    # either the two runtimes are distinct files (refused) or they are the
+    # same file (one runtime: loading is fine)
+    if r.stdout.startswith("LOADED"):
+        assert len(eval(r.stdout.split(" ", 1)[1])) == 1, r.stdout
+    else:
+        assert "two HIP runtimes" in r.stdout, r.stdout

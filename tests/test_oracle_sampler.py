@@ -1,6 +1,6 @@
 """Pins of the oracle's sampler (阶段四 4.3 采样): closed forms on small
-vocabularies, the page's own roulette loop, temperature -> 0 and
-top_p -> 0 limits."""
+vocabularies, the roulette as an interval lookup over prefix sums,
+temperature -> 0 and top_p -> 0 limits."""
 import math
 
 import numpy as np
@@ -11,18 +11,16 @@ from oracle.sampler import sample, nucleus, argmax
 
 
 def _page_roulette(probs, kept, u):
-    # the page's loop: rnd = u * sum; for i: rnd -= probs[i]; if rnd <= 0: return i
-    total = sum(p for p, k in zip(probs, kept) if k)
-    rnd = u * total
-    last = None
-    for i, (p, k) in enumerate(zip(probs, kept)):
-        if not k:
-            continue
-        last = i
-        rnd -= p
-        if rnd <= 0.0:
-            return i
-    return last
+    """The roulette of 阶段四 4.3 (采样), stated as an interval lookup: kept
+    token i owns the interval (C_{i-1}, C_i] of the running kept mass C (in
+    vocabulary order), and the draw r = u * C_last falls in exactly one of
+    them.  Bisection over the prefix sums finds the first kept token whose
+    running sum reaches r; a rounding overshoot past the total picks the
+    last kept token."""
+    kept_idx = np.nonzero(np.asarray(kept, dtype=bool))[0]
+    c = np.cumsum(np.asarray(probs, dtype=np.float64)[kept_idx])
+    j = int(np.searchsorted(c, u * c[-1], side="left"))
+    return int(kept_idx[min(j, kept_idx.size - 1)])
 
 
 def test_argmax_first_index():
@@ -156,8 +154,8 @@ def test_min_p_one_is_argmax():
             assert sample(l, 1.3, 1.0, u, min_p=2.5)["token"] == argmax(l)
 
 
-def test_min_p_brute_force_against_page_loop():
-    # kept set by definition, token by the page's own loop over it
+def test_min_p_brute_force_interval_lookup():
+    # kept set by definition, token by the interval lookup over its prefix sums
     r = np.random.default_rng(13)
     for trial in range(20):
         l = r.normal(size=40) * 3
