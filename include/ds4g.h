@@ -23,7 +23,8 @@
  *
  * Conventions shared by every call:
  *   - Every pointer argument named "device" is HIP device memory owned by the
- *     caller; the library allocates nothing and keeps no global state.
+ *     caller; the library allocates nothing and keeps no global state (one
+ *     exception: the static scratch array of ds4g_layer_decode_noalloc).
  *   - Weight matrices are row-major [out, in], all in cfg->wdtype
  *     (DS4G_BF16: raw bf16 bits; DS4G_F32: float).  Expert stacks are
  *     [n_experts, out, in].  Gains (norm weights) are in wdtype too.
@@ -162,6 +163,22 @@ int ds4g_layer_prefill(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
 int ds4g_layer_decode(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
                       ds4g_kv_ring *ring, float *x, ds4g_routing *routing,
                       void *ws, size_t ws_bytes, void *stream);
+
+/* ds4g_layer_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as ds4g_layer_decode, minus
+ * the workspace: the step's scratch is a static device array of 2 MiB that
+ * the library holds on every GPU it runs on until the process ends (the
+ * first call on a device looks up its address; nothing is allocated, ever).
+ * Every decode shape ds4g_layer_supported accepts fits in it; a layer whose
+ * decode would need more returns DS4G_ERR_WORKSPACE.  The array keeps what
+ * the last call left, and no byte of it needs to start at zero (every byte a
+ * step reads was written earlier in the same step).  All calls on one GPU
+ * share the array: calls that overlap on one GPU (two streams, two host
+ * threads) race and must be serialised by the caller. */
+int ds4g_layer_decode_noalloc(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
+                              ds4g_kv_ring *ring, float *x, ds4g_routing *routing,
+                              void *stream);
 
 /* Batched decode: one token of each of B >= 1 independent sequences through
  * the layer (the throughput form of 阶段四 4.2's single-token step; the

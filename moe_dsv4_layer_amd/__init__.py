@@ -20,7 +20,7 @@ MODE_PREFILL, MODE_DECODE, MODE_DECODE_BATCH = 0, 1, 2
 
 # ds4g.h declares these functions; the ABI test checks the header agrees.
 EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_supported", "ds4g_layer_prefill",
-           "ds4g_layer_decode", "ds4g_layer_decode_batch",
+           "ds4g_layer_decode", "ds4g_layer_decode_noalloc", "ds4g_layer_decode_batch",
            "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_status_string")
 
 
@@ -99,6 +99,11 @@ def _load() -> ctypes.CDLL:
     lib.ds4g_layer_decode.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
                                       ctypes.POINTER(KvRing), P, ctypes.POINTER(Routing), P,
                                       ctypes.c_size_t, P]
+    lib.ds4g_layer_decode_noalloc.restype = ctypes.c_int
+    lib.ds4g_layer_decode_noalloc.argtypes = [ctypes.POINTER(LayerCfg),
+                                              ctypes.POINTER(LayerWeights),
+                                              ctypes.POINTER(KvRing), P, ctypes.POINTER(Routing),
+                                              P]
     lib.ds4g_layer_decode_batch.restype = ctypes.c_int
     lib.ds4g_layer_decode_batch.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
                                             ctypes.POINTER(KvRing), P, ctypes.c_int32,
@@ -197,6 +202,16 @@ def layer_decode(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x, ws,
                                ctypes.byref(routing) if routing is not None else None,
                                ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "ds4g_layer_decode")
+
+
+def layer_decode_noalloc(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x,
+                         routing: Optional[Routing] = None, stream=None) -> None:
+    """ds4g_layer_decode with the library's static scratch (no workspace)."""
+    rc = lib.ds4g_layer_decode_noalloc(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ring),
+                                       x.data_ptr(),
+                                       ctypes.byref(routing) if routing is not None else None,
+                                       _stream(stream))
+    _check(rc, "ds4g_layer_decode_noalloc")
 
 
 def layer_decode_batch(cfg: LayerCfg, w: LayerWeights, rings: KvRing, x, B: int, ws,

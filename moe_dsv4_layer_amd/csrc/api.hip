@@ -4,6 +4,7 @@
 #include "../../include/ds4g.h"
 #include "kernels.h"
 #include <algorithm>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 #include <stdio.h>
@@ -447,6 +448,35 @@ int layer_seq(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring
   return prefill_impl(c, w, ring, x, T, routing, ws, ex, mode == DS4G_MODE_DECODE_BATCH);
 }
 
+// Scratch of ds4g_layer_decode_noalloc: a file-scope device array, one copy
+// per GPU at that GPU's own address, kept until the process ends.  Its name
+// on the host is only a stand-in: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoallocScratchBytes = size_t(2) << 20;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on each device (with that device current) and kept; nullptr if HIP
+// refuses.
+void* scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      fprintf(stderr, "ds4g: hipGetSymbolAddress(scratch) failed: %s\n", hipGetErrorString(e));
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 }  // namespace ds4g
 
@@ -496,6 +526,27 @@ int ds4g_layer_decode(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, ds
   return dry_then_run((hipStream_t)stream, [&](Exec ex) {
     return layer_seq(*cfg, *w, *ring, x, 1, routing, ws, ex, DS4G_MODE_DECODE);
   });
+}
+
+int ds4g_layer_decode_noalloc(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
+                              ds4g_kv_ring* ring, float* x, ds4g_routing* routing, void* stream) {
+  // every check, and the dry launch sequence, before the device is touched
+  // (a placeholder stands for the scratch address until then)
+  void* const placeholder = reinterpret_cast<void*>(uintptr_t(1) << 40);
+  const int s = check_call(cfg, w, ring, x, 1, placeholder, kNoallocScratchBytes,
+                           DS4G_MODE_DECODE);
+  if (s == DS4G_ERR_WORKSPACE)
+    fprintf(stderr, "ds4g_layer_decode_noalloc: the layer needs %zu bytes of scratch, the "
+            "library holds %zu\n", layout(*cfg, 1).total, kNoallocScratchBytes);
+  if (s != DS4G_OK) return s;
+  if (layer_seq(*cfg, *w, *ring, x, 1, routing, placeholder, Exec{(hipStream_t)stream, true},
+                DS4G_MODE_DECODE) != 0)
+    return DS4G_ERR_UNSUPPORTED;
+  void* ws = scratch_ptr();
+  if (!ws) return DS4G_ERR_HIP;
+  clear_stale_error();
+  return hip_status(layer_seq(*cfg, *w, *ring, x, 1, routing, ws,
+                              Exec{(hipStream_t)stream, false}, DS4G_MODE_DECODE));
 }
 
 int ds4g_layer_supported(const ds4g_layer_cfg* cfg, int32_t T, int32_t mode) {

@@ -257,3 +257,23 @@ def test_binding_refuses_two_hip_runtimes():
         assert len(eval(r.stdout.split(" ", 1)[1])) == 1, r.stdout
     else:
         assert "two HIP runtimes" in r.stdout, r.stdout
+
+
+def test_decode_noalloc_rejects_before_touching_the_device():
+    # every check and the dry launch sequence run before the scratch address
+    # is looked up: these refusals need no device
+    L = ds4g.lib
+    w = _weights()
+    ring = ds4g.KvRing(0x1000, 0x1000, 0x1000)
+
+    def call(cfg, x=0x1000, wts=w, rg=ring):
+        return L.ds4g_layer_decode_noalloc(ctypes.byref(cfg) if cfg is not None else None,
+                                           ctypes.byref(wts) if wts is not None else None,
+                                           ctypes.byref(rg) if rg is not None else None,
+                                           x, None, None)
+    assert call(None) == ds4g.ERR_INVALID_ARG
+    assert call(_cfg(), x=None) == ds4g.ERR_INVALID_ARG
+    assert call(_cfg(), wts=_weights(False)) == ds4g.ERR_INVALID_ARG
+    assert call(_cfg(), rg=ds4g.KvRing(0x1000, 0, 0x1000)) == ds4g.ERR_INVALID_ARG
+    assert call(_cfg(head_dim=96)) == ds4g.ERR_UNSUPPORTED
+    assert call(_cfg(hidden=16384)) == ds4g.ERR_UNSUPPORTED     # refused by the dry run
