@@ -263,7 +263,7 @@ def main() -> int:
     w_cpu = None
     for l in range(args.weight_sets):
         w = synth.layer_weights(s, wl.seed, layer=l, device=dev)
-        rk = torch.zeros((s.window, s.head_dim), dtype=torch.bfloat16, device=dev)
+        rk = torch.zeros((s.window, s.head_dim), dtype=torch.float16, device=dev)
         rv = torch.zeros_like(rk)
         pos = torch.zeros(1, dtype=torch.int64, device=dev)
         layers.append(dict(w=w, cw=ds4g.make_weights(w), rk=rk, rv=rv, pos=pos,
@@ -360,7 +360,7 @@ def main() -> int:
     # projections, router and experts run over the B rows, weights read once)
     batch = {}
     for B in (8, 32, 128):
-        rkb = torch.zeros((B, s.window, s.head_dim), dtype=torch.bfloat16, device=dev)
+        rkb = torch.zeros((B, s.window, s.head_dim), dtype=torch.float16, device=dev)
         rvb = torch.zeros_like(rkb)
         posb = torch.full((B,), s.window, dtype=torch.int64, device=dev)
         ringb = ds4g.make_ring(rkb, rvb, posb)

@@ -29,9 +29,17 @@
  *     (DS4G_BF16: raw bf16 bits; DS4G_F32: float).  Expert stacks are
  *     [n_experts, out, in].  Gains (norm weights) are in wdtype too.
  *   - The residual stream x is fp32, updated in place.
- *   - The KV ring holds K (after RoPE) and V as bf16 [window, head_dim];
- *     position p lives in slot p % window; *pos (device int64) is the
- *     position of the next token and is advanced by every call.
+ *   - The KV ring holds K (after RoPE) and V as fp16 (IEEE binary16)
+ *     [window, head_dim]; position p lives in slot p % window; *pos (device
+ *     int64) is the position of the next token and is advanced by every call.
+ *   - With bf16 weights, a prefill (and a batched decode) carries the
+ *     attention path -- normalised input, low-rank code, q, k, v, attention
+ *     probabilities and output -- in fp16 on the matrix cores, against fp16
+ *     images of QKV-A, QKV-B and W_o that the call makes in its workspace
+ *     (each row scaled by a power of two; exact for every value at least 2^-32
+ *     times the row's largest).  These activations must stay inside fp16's range
+ *     (|v| < 65504).  The expert path stays bf16; the router sees fp32-quality
+ *     inputs.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream).  They never synchronise and never call the allocator, so a
  *     decode step can be captured in a HIP graph and replayed.
@@ -112,8 +120,8 @@ typedef struct {
 
 /* One layer's KV ring (device memory). */
 typedef struct {
-  void *k;        /* bf16 [window, head_dim], K after RoPE                   */
-  void *v;        /* bf16 [window, head_dim]                                 */
+  void *k;        /* fp16 [window, head_dim], K after RoPE                   */
+  void *v;        /* fp16 [window, head_dim]                                 */
   int64_t *pos;   /* position of the next token (>= 0)                       */
 } ds4g_kv_ring;
 
@@ -129,9 +137,11 @@ typedef struct {
   float *router_logits;    /* [T, E]  s                                       */
 } ds4g_routing;
 
-/* Bytes of workspace a layer call needs for up to max_tokens tokens, or that
- * ds4g_lmhead_sample needs for `vocab` (pass cfg = NULL for the lm_head
- * alone).  Returns 0 on invalid arguments. */
+/* Bytes of workspace that covers every layer call for up to max_tokens
+ * tokens (the largest need is a prefill's: its activations plus the fp16
+ * images of QKV-A, QKV-B and W_o), and ds4g_lmhead_sample for `vocab` (pass
+ * cfg = NULL for the lm_head alone).  ds4g_layer_decode needs less; each call
+ * checks ws_bytes against its own need.  Returns 0 on invalid arguments. */
 size_t ds4g_workspace_bytes(const ds4g_layer_cfg *cfg, int32_t max_tokens,
                             int32_t vocab);
 

@@ -49,12 +49,16 @@ inline int router_split(int hidden, bool mfma) {
 
 struct Layout {
   size_t xn, c, qkv, q, kc, vc, o, yf, ys, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
-      count, offset, tiles, ntiles, z, zs, part, psh, skp, rope, total;
+      count, offset, tiles, ntiles, z, zs, part, psh, skp, rope, img[3], inv[3], total;
 };
 
 // Byte offsets of every workspace buffer for T tokens.  fp32-sized slots are
-// used for buffers that hold bf16 on the MFMA path and fp32 on the SIMT path.
-Layout layout(const ds4g_layer_cfg& c, int T) {
+// used for buffers that hold 16-bit values on the MFMA path and fp32 on the
+// SIMT path.  images: the fp16 images of QKV-A, QKV-B and W_o (and their row
+// factors) that the attention path's MFMA GEMMs read; prefill and batched
+// decode with bf16 weights only (the single-token decode streams the bf16
+// weights themselves).
+Layout layout(const ds4g_layer_cfg& c, int T, bool images) {
   const size_t d = c.hidden, r = c.qkv_rank, qd = (size_t)c.n_heads * c.head_dim,
                qkvd = qd + 2 * (size_t)c.head_dim, E = c.n_experts, k = c.top_k,
                I = c.ffn_inter, Is = c.shared_inter, dh = c.head_dim;
@@ -96,6 +100,14 @@ Layout layout(const ds4g_layer_cfg& c, int T) {
     L.skp = take(T <= 256 ? m : 0);
   }
   L.rope = take((size_t)dh * (((size_t)T + 3) & ~(size_t)3) * 4);   // cos, sin [rd/2][T pad 4]
+  {
+    const bool on = images && c.wdtype == DS4G_BF16;
+    const size_t n[3] = {r, qkvd, d}, k[3] = {d, r, qd};
+    for (int m = 0; m < 3; ++m) {
+      L.img[m] = take(on ? n[m] * k[m] * 2 : 0);
+      L.inv[m] = take(on ? n[m] * 4 : 0);
+    }
+  }
   L.total = o;
   return L;
 }
@@ -178,7 +190,7 @@ int dry_then_run(hipStream_t stream, F&& seq) {
 int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring& ring,
                  float* x, int T, ds4g_routing* routing, void* ws, Exec st,
                  bool batch = false) {
-  const Layout L = layout(c, T);
+  const Layout L = layout(c, T, true);
   const bool bf = c.wdtype == DS4G_BF16;
   const int d = c.hidden, r = c.qkv_rank, H = c.n_heads, dh = c.head_dim, qd = H * dh,
             qkvd = qd + 2 * dh, E = c.n_experts, k = c.top_k, I = c.ffn_inter,
@@ -186,24 +198,47 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   const int rd = c.rope_dim ? c.rope_dim : dh;
   int rc = 0;
 
-  // x_norm = RMSNorm(h) * g1
+  // x_norm = RMSNorm(h) * g1.  bf16 weights: the attention path (x_norm, c,
+  // q, k, v, probabilities, o) runs in fp16 on the matrix cores; fp32
+  // weights: fp32 on the vector ALUs.
   if (bf)
     rc |= launch_rmsnorm_rows<uint16_t>(x, T, d, (const uint16_t*)w.attn_norm, c.rms_eps, nullptr,
-                                        at<uint16_t>(ws, L.xn), nullptr, st);
+                                        nullptr, at<uint16_t>(ws, L.xn), nullptr, st);
   else
     rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.attn_norm, c.rms_eps,
-                                     at<float>(ws, L.xn), nullptr, nullptr, st);
+                                     at<float>(ws, L.xn), nullptr, nullptr, nullptr, st);
+
+  // fp16 images of the attention path's weights (QKV-A, QKV-B, W_o), each
+  // made right before the first GEMM that reads it
+  const void* const wsrc[3] = {w.qkv_a, w.qkv_b, w.wo};
+  const int wN[3] = {r, qkvd, d}, wK[3] = {d, r, qd};
+  bool made[3] = {false, false, false};
+  auto image = [&](int m) {
+    if (!made[m]) {
+      rc |= launch_f16_image(static_cast<const uint16_t*>(wsrc[m]), wN[m], wK[m],
+                             at<uint16_t>(ws, L.img[m]), at<float>(ws, L.inv[m]), st);
+      made[m] = true;
+    }
+  };
 
   // dense GEMM; batched decode splits K (fp32 partials, then a reduce that
-  // applies the epilogue).  B2: the up projection of a SwiGLU pair.
+  // applies the epilogue).  B2: the up projection of a SwiGLU pair.  img >= 0:
+  // A is fp16 and B is attention-path weight img, read from its fp16 image
+  // (the multi-row GEMV reads the bf16 weights directly).
   auto gemm = [&](const void* A, int lda, const void* B, int M, int N, int K, int epi, void* C,
-                  int ldc, const void* B2 = nullptr) {
+                  int ldc, const void* B2 = nullptr, int img = -1) {
     if (batch && bf && M <= 8) {   // a few rows: stream each weight row once (multi-row GEMV)
       GemvRowsArgs v{};
       v.W = static_cast<const uint16_t*>(B); v.W2 = static_cast<const uint16_t*>(B2);
-      v.N = N; v.K = K; v.X = static_cast<const uint16_t*>(A); v.lda = lda; v.M = M;
-      v.epi = epi; v.C = C; v.ldc = ldc;
+      v.N = N; v.K = K; v.X = static_cast<const uint16_t*>(A); v.x_f16 = img >= 0 ? 1 : 0;
+      v.lda = lda; v.M = M; v.epi = epi; v.C = C; v.ldc = ldc;
       if (launch_gemv_rows(v, st) == 0) return;
+    }
+    const float* cs = nullptr;
+    if (bf && img >= 0) {
+      image(img);
+      B = at<void>(ws, L.img[img]);
+      cs = at<float>(ws, L.inv[img]);
     }
     const int s = batch ? batch_split(M, N, K, bf) : 1;
     if (s > 1) {
@@ -211,7 +246,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
       const long ps = (long)M * N;
       GemmArgs g{};
       g.A = A; g.lda = lda; g.M = M; g.N = N; g.K = K; g.epi = EPI_F32; g.ldc = N;
-      g.ksplit = s; g.part_stride = ps;
+      g.ksplit = s; g.part_stride = ps; g.f16 = img >= 0 ? 1 : 0;
       g.B = B; g.C = part;
       rc |= launch_gemm(g, bf, 1, st);
       if (B2) {
@@ -219,41 +254,45 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
         rc |= launch_gemm(g, bf, 1, st);
       }
       rc |= launch_splitk_reduce(part, B2 ? part + (size_t)s * ps : nullptr, s, ps, M, N, epi, C,
-                                 ldc, st);
+                                 ldc, cs, st);
       return;
     }
     GemmArgs g{};
     g.A = A; g.lda = lda; g.B = B; g.B2 = B2; g.M = M; g.N = N; g.K = K; g.epi = epi; g.C = C;
-    g.ldc = ldc;
+    g.ldc = ldc; g.f16 = (bf && img >= 0) ? 1 : 0; g.colscale = cs;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   };
   // c = A x ; qkv = B c (prefill on the matrix cores: RoPE in the epilogue,
-  // q / k / v written rotated in bf16, as attention reads them)
-  gemm(at<void>(ws, L.xn), d, w.qkv_a, T, r, d, bf ? EPI_BF16 : EPI_F32, at<void>(ws, L.c), r);
+  // q / k / v written rotated in fp16, as attention reads them)
+  gemm(at<void>(ws, L.xn), d, w.qkv_a, T, r, d, bf ? EPI_F16 : EPI_F32, at<void>(ws, L.c), r,
+       nullptr, 0);
   const bool rope_epi = bf && !batch;
   const int tpad = (T + 3) & ~3;
   if (rope_epi) {
     float* rc_tab = at<float>(ws, L.rope);
     rc |= launch_rope_table(ring.pos, T, tpad, rd, c.rope_base, rc_tab, rc_tab + (size_t)(rd / 2) * tpad,
                             st);
+    image(1);
     GemmArgs g{};
-    g.A = at<void>(ws, L.c); g.lda = r; g.B = w.qkv_b; g.M = T; g.N = qkvd; g.K = r;
+    g.A = at<void>(ws, L.c); g.lda = r; g.B = at<void>(ws, L.img[1]); g.M = T; g.N = qkvd; g.K = r;
+    g.f16 = 1; g.colscale = at<float>(ws, L.inv[1]);
     g.epi = EPI_ROPE_QKV; g.C = at<void>(ws, L.q); g.ldc = qd;
     g.rope_c = rc_tab; g.rope_s = rc_tab + (size_t)(rd / 2) * tpad; g.rope_ld = tpad;
     g.rope_dh = dh; g.rope_rd = rd;
     g.rope_kc = at<uint16_t>(ws, L.kc); g.rope_vc = at<uint16_t>(ws, L.vc);
     rc |= launch_gemm(g, true, 1, st);
   } else {
-    gemm(at<void>(ws, L.c), r, w.qkv_b, T, qkvd, r, EPI_F32, at<void>(ws, L.qkv), qkvd);
+    gemm(at<void>(ws, L.c), r, w.qkv_b, T, qkvd, r, EPI_F32, at<void>(ws, L.qkv), qkvd, nullptr,
+         1);
   }
 
   // RoPE, attention over the window, ring update (*pos += T)
   AttnArgs aa{};
   aa.qkv = at<float>(ws, L.qkv); aa.T = T; aa.H = H; aa.dh = dh; aa.rd = rd; aa.W = c.window;
-  aa.base = c.rope_base; aa.pos = ring.pos; aa.q = at<void>(ws, L.q); aa.q_bf16 = bf ? 1 : 0;
+  aa.base = c.rope_base; aa.pos = ring.pos; aa.q = at<void>(ws, L.q); aa.q_f16 = bf ? 1 : 0;
   aa.kc = at<uint16_t>(ws, L.kc); aa.vc = at<uint16_t>(ws, L.vc);
   aa.ring_k = (uint16_t*)ring.k; aa.ring_v = (uint16_t*)ring.v;
-  aa.o = at<void>(ws, L.o); aa.o_bf16 = bf ? 1 : 0; aa.heads_per_block = H < 64 ? H : 64;
+  aa.o = at<void>(ws, L.o); aa.o_f16 = bf ? 1 : 0; aa.heads_per_block = H < 64 ? H : 64;
   aa.rope_done = rope_epi ? 1 : 0;
   if (batch)   // RoPE at each sequence's position, its own ring, *pos[b] += 1
     rc |= launch_attention_decode_batch(aa, T, st);
@@ -261,7 +300,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     rc |= bf ? launch_attention_prefill_mfma(aa, st) : launch_attention(aa, st);
 
   // h2 = h + W_o o   (in place in x)
-  gemm(at<void>(ws, L.o), qd, w.wo, T, d, qd, EPI_RESID, x, d);
+  gemm(at<void>(ws, L.o), qd, w.wo, T, d, qd, EPI_RESID, x, d, nullptr, 2);
 
   // y = RMSNorm(h2) * g2: fp32, and (bf16 weights) its three-term bf16 split,
   // whose first term is bf16(y), the expert GEMMs' input
@@ -269,10 +308,10 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     rc |= launch_rmsnorm_rows<uint16_t>(x, T, d, (const uint16_t*)w.ffn_norm, c.rms_eps,
                                         (routing && routing->router_in) ? at<float>(ws, L.yf)
                                                                         : nullptr,
-                                        nullptr, at<uint16_t>(ws, L.ys), st);
+                                        nullptr, nullptr, at<uint16_t>(ws, L.ys), st);
   else
     rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.ffn_norm, c.rms_eps,
-                                     at<float>(ws, L.yf), nullptr, nullptr, st);
+                                     at<float>(ws, L.yf), nullptr, nullptr, nullptr, st);
 
   // router logits at fp32 quality (they decide integer expert choices):
   // bf16 weights: y1|y2|y3 against [W_r|W_r|W_r] on the matrix cores; fp32
@@ -356,7 +395,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
 template <typename WT>
 int decode_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring& ring,
                 float* x, ds4g_routing* routing, void* ws, Exec st) {
-  const Layout L = layout(c, 1);
+  const Layout L = layout(c, 1, false);
   const int d = c.hidden, r = c.qkv_rank, H = c.n_heads, dh = c.head_dim, qd = H * dh,
             qkvd = qd + 2 * dh, E = c.n_experts;
   const int rd = c.rope_dim ? c.rope_dim : dh;
@@ -435,7 +474,7 @@ int check_call(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, const ds4
   if (!x || !ws || T <= 0) return DS4G_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
   if ((s = check_rows(*cfg, T, mode)) != DS4G_OK) return s;
-  if (ws_bytes < layout(*cfg, T).total) return DS4G_ERR_WORKSPACE;
+  if (ws_bytes < layout(*cfg, T, mode != DS4G_MODE_DECODE).total) return DS4G_ERR_WORKSPACE;
   return DS4G_OK;
 }
 
@@ -488,7 +527,7 @@ size_t ds4g_workspace_bytes(const ds4g_layer_cfg* cfg, int32_t max_tokens, int32
   size_t n = 0;
   if (cfg) {
     if (check_cfg(cfg) != DS4G_OK || max_tokens <= 0) return 0;
-    n = layout(*cfg, max_tokens).total;
+    n = layout(*cfg, max_tokens, true).total;
   }
   if (vocab > 0) {
     const size_t s = sample_ws_bytes(vocab);
@@ -537,7 +576,7 @@ int ds4g_layer_decode_noalloc(const ds4g_layer_cfg* cfg, const ds4g_layer_weight
                            DS4G_MODE_DECODE);
   if (s == DS4G_ERR_WORKSPACE)
     fprintf(stderr, "ds4g_layer_decode_noalloc: the layer needs %zu bytes of scratch, the "
-            "library holds %zu\n", layout(*cfg, 1).total, kNoallocScratchBytes);
+            "library holds %zu\n", layout(*cfg, 1, false).total, kNoallocScratchBytes);
   if (s != DS4G_OK) return s;
   if (layer_seq(*cfg, *w, *ring, x, 1, routing, placeholder, Exec{(hipStream_t)stream, true},
                 DS4G_MODE_DECODE) != 0)

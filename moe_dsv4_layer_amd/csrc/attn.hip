@@ -4,9 +4,9 @@
 // position, (k, v) is appended to the KV cache, then all 64 query heads attend
 // to the same keys (MQA) inside a 128-token window.  The cache is a W-slot
 // ring: position p lives in slot p % W, so a token sees exactly the slots
-// still in its window.  Keys and values are cached in bf16; every key a query
-// sees (its own included) is the cached bf16 value, so prefill and decode see
-// identical numbers.
+// still in its window.  Keys and values are cached in fp16 (IEEE binary16);
+// every key a query sees (its own included) is the cached fp16 value, so
+// prefill and decode see identical numbers.
 #include "dev.h"
 #include "kernels.h"
 
@@ -14,9 +14,9 @@ namespace ds4g {
 
 // ---------------------------------------------------------------------------
 // rope_qkv: qkv fp32 [T, H*dh + 2*dh] (raw projection) ->
-//   q  [T, H, dh]  rotated (QT = float or bf16)
-//   kc [T, dh]     rotated, bf16
-//   vc [T, dh]     bf16
+//   q  [T, H, dh]  rotated (QT = float or fp16)
+//   kc [T, dh]     rotated, fp16
+//   vc [T, dh]     fp16
 // Pair i of the rotated tail turns by (pos0 + t) * base^(-2i/rd) (angle in
 // fp64, see rope_cs).  One block per token.
 template <typename QT>
@@ -46,20 +46,20 @@ rope_qkv_kernel(const float* __restrict__ qkv, int T, int H, int dh, int rd, flo
     }
     if (head < H) {
       QT* dst = q + (long)t * qd + head * dh + e0;
-      if constexpr (sizeof(QT) == 2) { dst[0] = f32_to_bf16(a); dst[1] = f32_to_bf16(b); }
+      if constexpr (sizeof(QT) == 2) { dst[0] = f32_to_f16(a); dst[1] = f32_to_f16(b); }
       else { dst[0] = a; dst[1] = b; }
     } else {
-      kc[(long)t * dh + e0] = f32_to_bf16(a);
-      kc[(long)t * dh + e0 + 1] = f32_to_bf16(b);
+      kc[(long)t * dh + e0] = f32_to_f16(a);
+      kc[(long)t * dh + e0 + 1] = f32_to_f16(b);
     }
   }
   for (int e = threadIdx.x; e < dh; e += blockDim.x)
-    vc[(long)t * dh + e] = f32_to_bf16(row[qd + dh + e]);
+    vc[(long)t * dh + e] = f32_to_f16(row[qd + dh + e]);
 }
 
 // ---------------------------------------------------------------------------
 // Windowed MQA, SIMT: one block per (token, group of HG heads).  The window's
-// keys (transposed) and values are staged in LDS as bf16; a wave takes one
+// keys (transposed) and values are staged in LDS as fp16; a wave takes one
 // head at a time: lanes own keys for q.k, lanes own dims for p.v.
 // Key of position j < pos0 comes from ring slot j % W, else from kc/vc.
 template <typename OT, int DH>
@@ -112,8 +112,8 @@ attn_window_kernel(const float* __restrict__ q, const uint16_t* __restrict__ kc,
       float a0 = 0.f, a1 = 0.f;
       for (int e = 0; e < DH; ++e) {
         const float qe = qs[wid][e];
-        a0 += qe * bf16_to_f32(kT[e][lane]);
-        a1 += qe * bf16_to_f32(kT[e][lane + 64]);
+        a0 += qe * f16_to_f32(kT[e][lane]);
+        a1 += qe * f16_to_f32(kT[e][lane + 64]);
       }
       if (lane < n) s0 = a0 * scale;
       if (lane + 64 < n) s1 = a1 * scale;
@@ -129,13 +129,13 @@ attn_window_kernel(const float* __restrict__ q, const uint16_t* __restrict__ kc,
     float o0 = 0.f, o1 = 0.f;
     for (int j = 0; j < n; ++j) {
       const float pj = ps[wid][j];
-      o0 += pj * bf16_to_f32(vs[j][lane]);
-      if (DH > 64) o1 += pj * bf16_to_f32(vs[j][lane + 64]);
+      o0 += pj * f16_to_f32(vs[j][lane]);
+      if (DH > 64) o1 += pj * f16_to_f32(vs[j][lane + 64]);
     }
     OT* dst = o + ((long)t * H + h) * DH;
     if constexpr (sizeof(OT) == 2) {
-      dst[lane] = f32_to_bf16(o0);
-      if (DH > 64) dst[lane + 64] = f32_to_bf16(o1);
+      dst[lane] = f32_to_f16(o0);
+      if (DH > 64) dst[lane + 64] = f32_to_f16(o1);
     } else {
       dst[lane] = o0;
       if (DH > 64) dst[lane + 64] = o1;
@@ -172,7 +172,7 @@ static void ring_commit(const AttnArgs& a, Exec st) {
 }
 
 int launch_attention(const AttnArgs& a, Exec st) {
-  if (a.q_bf16)
+  if (a.q_f16)
     DS4G_LAUNCH((rope_qkv_kernel<uint16_t>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
                        a.dh, a.rd, a.base, a.pos, (uint16_t*)a.q, a.kc, a.vc);
   else
@@ -184,9 +184,9 @@ int launch_attention(const AttnArgs& a, Exec st) {
   DS4G_LAUNCH((attn_window_kernel<OT, DH>), grid, dim3(256), 0, st, (const float*)a.q, \
                      a.kc, a.vc, a.ring_k, a.ring_v, a.pos, a.T, a.H, a.W, HG, (OT*)a.o)
   if (a.dh == 128) {
-    if (a.o_bf16) DS4G_ATT(uint16_t, 128); else DS4G_ATT(float, 128);
+    if (a.o_f16) DS4G_ATT(uint16_t, 128); else DS4G_ATT(float, 128);
   } else if (a.dh == 64) {
-    if (a.o_bf16) DS4G_ATT(uint16_t, 64); else DS4G_ATT(float, 64);
+    if (a.o_f16) DS4G_ATT(uint16_t, 64); else DS4G_ATT(float, 64);
   } else {
     return -1;
   }
@@ -212,7 +212,7 @@ int launch_attention(const AttnArgs& a, Exec st) {
 // overwrite it while the other blocks read.  *pos is advanced by a later
 // kernel.  Batched decode: blockIdx.y is the sequence b, with its own qkv row
 // (stride qkv_stride), ring (b * W * DH), position pos[b] and o row (H * DH);
-// o is fp32 or bf16 (OT).
+// o is fp32 or fp16 (OT).
 template <int DH, typename OT>
 __global__ void __launch_bounds__(256)
 attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W, int rd,
@@ -276,7 +276,7 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
     const long at = (j < n - 1) ? (long)slot * DH + dg * 8 : 0;
     vreg[u] = *reinterpret_cast<const uint4*>(ring_v + at);
   }
-  // ---- RoPE of q (this head) and k; the token's k, v in bf16 like the ring
+  // ---- RoPE of q (this head) and k; the token's k, v in fp16 like the ring
   const int off = DH - rd;
   for (int i = tid; i < rd / 2; i += 256) rope_cs(p, i, rd, base, &cs[i], &sn[i]);
   __syncthreads();
@@ -291,9 +291,9 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
       a = na; b = nb;
     }
     if (isq) { qs[e0] = a; qs[e0 + 1] = b; }
-    else { kself[e0] = f32_to_bf16(a); kself[e0 + 1] = f32_to_bf16(b); }
+    else { kself[e0] = f32_to_f16(a); kself[e0 + 1] = f32_to_f16(b); }
   } else if (tid < 2 * DH) {
-    vself[tid - DH] = f32_to_bf16(ta);
+    vself[tid - DH] = f32_to_f16(ta);
   }
   __syncthreads();
   if (h == 0) {
@@ -313,7 +313,7 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       float f[8];
-      unpack8(kreg[c], f);
+      unpack8_f16(kreg[c], f);
       const float4 q0 = *reinterpret_cast<const float4*>(&qs[hk * (DH / 2) + c * 8]);
       const float4 q1 = *reinterpret_cast<const float4*>(&qs[hk * (DH / 2) + c * 8 + 4]);
       acc += q0.x * f[0] + q0.y * f[1] + q0.z * f[2] + q0.w * f[3] +
@@ -344,7 +344,7 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
         uint4 v4 = vreg[u];
         if (j == n - 1) v4 = *reinterpret_cast<const uint4*>(vself + dg * 8);
         float f[8];
-        unpack8(v4, f);
+        unpack8_f16(v4, f);
         const float pj = pr[j];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += pj * f[e];
@@ -358,7 +358,7 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
     float v = 0.f;
 #pragma unroll
     for (int g = 0; g < KG; ++g) v += red[g][tid];
-    if constexpr (sizeof(OT) == 2) o[(long)h * DH + tid] = f32_to_bf16(v * inv);
+    if constexpr (sizeof(OT) == 2) o[(long)h * DH + tid] = f32_to_f16(v * inv);
     else o[(long)h * DH + tid] = v * inv;
   }
 }
@@ -384,9 +384,9 @@ int launch_attention_decode_batch(const AttnArgs& a, int B, Exec st) {
   DS4G_LAUNCH((attn_decode_kernel<DH, OT>), grid, dim3(256), 0, st, a.qkv, stride, a.H, \
                      a.W, a.rd, a.base, a.pos, a.ring_k, a.ring_v, (OT*)a.o)
   if (a.dh == 128) {
-    if (a.o_bf16) DS4G_AD(128, uint16_t); else DS4G_AD(128, float);
+    if (a.o_f16) DS4G_AD(128, uint16_t); else DS4G_AD(128, float);
   } else if (a.dh == 64) {
-    if (a.o_bf16) DS4G_AD(64, uint16_t); else DS4G_AD(64, float);
+    if (a.o_f16) DS4G_AD(64, uint16_t); else DS4G_AD(64, float);
   } else {
     return -1;
   }
@@ -396,12 +396,12 @@ int launch_attention_decode_batch(const AttnArgs& a, int B, Exec st) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill attention on the matrix cores (bf16 q, K, V; fp32 accumulate).
+// Prefill attention on the matrix cores (fp16 q, K, V, P; fp32 accumulate).
 //
 // A block takes the tokens of one 16-position-aligned span of absolute
 // positions [A, A + 16) and 32 heads.  Block key row j is position
 // A - W + 1 + j, so token tl (0..15) of the span sees rows [tl, tl + W - 1].
-// The block stages its key rows once (bf16, XOR-swizzled rows) and the values
+// The block stages its key rows once (fp16, XOR-swizzled rows) and the values
 // transposed (8 consecutive keys of one dim are 16 contiguous bytes) in LDS.
 // Aligning spans to absolute positions (not to the batch start) gives every
 // token the same key-to-lane placement and reduction order whatever batch it
@@ -413,20 +413,20 @@ int launch_attention_decode_batch(const AttnArgs& a, int B, Exec st) {
 // transposed, keys on the rows, so that the scores never leave registers:
 //   S^T = K Q^T   key tiles of 32 rows from the pair's window start rounded
 //                 down to 8 (4.5 tiles: the pair needs at most 136 rows), x
-//                 dh/16 steps of v_mfma_f32_32x32x16_bf16
+//                 dh/16 steps of v_mfma_f32_32x32x16_f16
 //   mask, column max / sum: within the lane, then with lane ^ 32
 //   O^T = V^T P^T dh/32 output tiles x 9 key steps of 16; the B operand P^T is
-//                 the S^T accumulator rounded to bf16 in place
+//                 the S^T accumulator rounded to fp16 in place
 // The accumulator of a 32x32 MFMA gives lane l the column l % 32 and rows
 // 8g + 4(l / 32) + i (g, i < 4); the B operand wants 8 consecutive keys
 // 8(l / 32) .. + 7 of a 16-key step.  Feeding K row pi(r) to A-operand row r,
 // pi(8g + 4h + i) = 16(g / 2) + 8h + 4(g % 2) + i, makes the accumulator rows
 // of g = 2s, 2s + 1 exactly the keys of step s, so P^T needs no shuffle.
 // Keys before the batch come from the ring (slot pos % W); the batch's own
-// keys from kc/vc (already rotated and rounded to bf16).
+// keys from kc/vc (already rotated and rounded to fp16).
 // 4 waves and 74 KB of LDS per block: two blocks per CU, so one block's
 // staging overlaps the other's arithmetic.
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short attn_bf16x8;
+typedef _Float16 attn_f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float attn_f32x16;
 
 // K rows are 16-B chunk-swizzled so that the 8 rows {x..x+3, x+8..x+11}
@@ -466,18 +466,18 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const int head = hg * 16 + (lr & 15);
   // Q^T B operand of pair p: column lr is token 2p + lr/16, head lr % 16 of
   // the group; zero outside the batch (branch-free: such lanes load row 0)
-  auto load_q = [&](int p, attn_bf16x8 (&dst)[DH / 16]) {
+  auto load_q = [&](int p, attn_f16x8 (&dst)[DH / 16]) {
     const long t = t0 + 2 * p + ((lr >> 4) & 1);
     const bool ok = p < BQ / 2 && t >= 0 && t < T && head < H;
     const uint16_t* src = ok ? q + (t * H + head) * DH + hf * 8 : q;
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + (ok ? ks * 16 : 0));
-      dst[ks] = __builtin_bit_cast(attn_bf16x8, ok ? v : u32x4_t{0, 0, 0, 0});
+      dst[ks] = __builtin_bit_cast(attn_f16x8, ok ? v : u32x4_t{0, 0, 0, 0});
     }
   };
   // the first pair's q goes out ahead of the staging loads
-  attn_bf16x8 qf[DH / 16];
+  attn_f16x8 qf[DH / 16];
   load_q(wid >> 1, qf);
   // every load of a thread goes out before its first LDS store (one wait, not
   // one round trip per chunk)
@@ -525,7 +525,7 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
   const long kmin = kbase < 0 ? -kbase : 0;       // first key row inside the sequence
   for (int p = wid >> 1; p < BQ / 2; p += 2) {
     // the next pair's q goes out before this pair's math
-    attn_bf16x8 qn[KSTEP];
+    attn_f16x8 qn[KSTEP];
     load_q(p + 2, qn);
     const int tl = 2 * p;
     const int tc = tl + ((lr >> 4) & 1);             // this lane's column token
@@ -545,8 +545,8 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ++ks) {
         const uint4 v = *reinterpret_cast<const uint4*>(krow + (((2 * ks + hf) ^ sw) * 8));
-        sacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const attn_bf16x8*>(&v), qf[ks], sacc[m], 0, 0, 0);
+        sacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            *reinterpret_cast<const attn_f16x8*>(&v), qf[ks], sacc[m], 0, 0, 0);
       }
     }
     // ---- mask to the window [tc, tc + W - 1] and the sequence start where a
@@ -579,7 +579,7 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float mo = -mx * sl2;
     float sm = 0.f;
-    attn_bf16x8 pf[9];
+    attn_f16x8 pf[9];
 #pragma unroll
     for (int m = 0; m < 5; ++m)
 #pragma unroll
@@ -590,9 +590,9 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
           e[k] = __builtin_amdgcn_exp2f(fmaf(sacc[m][8 * s + k], sl2, mo));   // masked: 0
           sm += e[k];
         }
-        const u32x4_t pk = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]),
-                            pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
-        pf[2 * m + s] = __builtin_bit_cast(attn_bf16x8, pk);
+        const u32x4_t pk = {pack_f16x2(e[0], e[1]), pack_f16x2(e[2], e[3]),
+                            pack_f16x2(e[4], e[5]), pack_f16x2(e[6], e[7])};
+        pf[2 * m + s] = __builtin_bit_cast(attn_f16x8, pk);
       }
     sm += __shfl_xor(sm, 32, kWave);
     // ---- O^T = V^T P^T
@@ -604,8 +604,8 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
       for (int st = 0; st < 9; ++st) {
         const uint4 v = *reinterpret_cast<const uint4*>(vrow + 16 * st);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const attn_bf16x8*>(&v), pf[st], oacc[dt], 0, 0, 0);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            *reinterpret_cast<const attn_f16x8*>(&v), pf[st], oacc[dt], 0, 0, 0);
       }
     }
     // lane holds dims dt*32 + 8g + 4hf + (0..3) of its column
@@ -617,8 +617,8 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           uint2 w;
-          w.x = pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv);
-          w.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+          w.x = pack_f16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv);
+          w.y = pack_f16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
           *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g) = w;
         }
     }
@@ -650,7 +650,7 @@ int launch_rope_table(const int64_t* pos, int T, int ld, int rd, float base, flo
 }
 
 int launch_attention_prefill_mfma(const AttnArgs& a, Exec st) {
-  if (a.W > 128 || !a.q_bf16 || !a.o_bf16) return -1;
+  if (a.W > 128 || !a.q_f16 || !a.o_f16) return -1;
   if (!a.rope_done)   // else the QKV GEMM's epilogue wrote rotated q, kc, vc
     DS4G_LAUNCH((rope_qkv_kernel<uint16_t>), dim3(a.T), dim3(256), 0, st, a.qkv, a.T, a.H,
                        a.dh, a.rd, a.base, a.pos, (uint16_t*)a.q, a.kc, a.vc);

@@ -192,9 +192,10 @@ template int launch_gemv<float>(const GemvArgs&, Exec);
 // rows).  Each weight row is streamed once for all M rows.  The block layout
 // is gemv_kernel's: 4 waves split K in KSPLIT parts and the block's rows in
 // 4/KSPLIT groups; a wave keeps its K slice of all M activation rows in
-// registers (bf16, MR x CPL chunks of 8) and streams RB weight rows at a time,
-// issuing the next rows' loads before the current rows' reductions.
-template <int MR, int KSPLIT, int CPL, int RB, bool DUAL>
+// registers (bf16 or fp16 (XF16), MR x CPL chunks of 8) and streams RB bf16
+// weight rows at a time, issuing the next rows' loads before the current
+// rows' reductions.
+template <int MR, int KSPLIT, int CPL, int RB, bool DUAL, bool XF16>
 __global__ void __launch_bounds__(256)
 gemv_rows_kernel(GemvRowsArgs a) {
   constexpr int RSPLIT = 4 / KSPLIT;
@@ -253,7 +254,8 @@ gemv_rows_kernel(GemvRowsArgs a) {
 #pragma unroll
           for (int m = 0; m < MR; ++m) {
             float x[8];
-            unpack8(xr[m][i], x);
+            if constexpr (XF16) unpack8_f16(xr[m][i], x);
+            else unpack8(xr[m][i], x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               acc[r][m][0] += w[e] * x[e];
@@ -293,6 +295,7 @@ gemv_rows_kernel(GemvRowsArgs a) {
         const long o = (long)m * a.ldc + n;
         if (DUAL) static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(silu(g) * u);
         else if (a.epi == EPI_BF16) static_cast<uint16_t*>(a.C)[o] = f32_to_bf16(g);
+        else if (a.epi == EPI_F16) static_cast<uint16_t*>(a.C)[o] = f32_to_f16(g);
         else if (a.epi == EPI_RESID) static_cast<float*>(a.C)[o] += g;
         else static_cast<float*>(a.C)[o] = g;
       }
@@ -300,7 +303,7 @@ gemv_rows_kernel(GemvRowsArgs a) {
   }
 }
 
-template <int MR, bool DUAL>
+template <int MR, bool DUAL, bool XF16>
 int launch_gemv_rows_mr(const GemvRowsArgs& a, Exec st) {
   constexpr int RB = 2;
   auto go = [&](auto kern, int ksplit) {
@@ -310,8 +313,15 @@ int launch_gemv_rows_mr(const GemvRowsArgs& a, Exec st) {
     DS4G_LAUNCH(kern, dim3((unsigned)grid), dim3(256), 0, st, a);
     return 0;
   };
-  if (a.K <= 1024) return go(gemv_rows_kernel<MR, 1, 2, RB, DUAL>, 1);
-  return go(gemv_rows_kernel<MR, 4, 2, RB, DUAL>, 4);
+  if (a.K <= 1024) return go(gemv_rows_kernel<MR, 1, 2, RB, DUAL, XF16>, 1);
+  return go(gemv_rows_kernel<MR, 4, 2, RB, DUAL, XF16>, 4);
+}
+
+template <int MR>
+int launch_gemv_rows_m(const GemvRowsArgs& a, Exec st) {
+  if (a.epi == EPI_SWIGLU_BF16) return a.x_f16 ? -1 : launch_gemv_rows_mr<MR, true, false>(a, st);
+  return a.x_f16 ? launch_gemv_rows_mr<MR, false, true>(a, st)
+                 : launch_gemv_rows_mr<MR, false, false>(a, st);
 }
 
 int launch_gemv_rows(const GemvRowsArgs& a, Exec st) {
@@ -320,11 +330,12 @@ int launch_gemv_rows(const GemvRowsArgs& a, Exec st) {
   // ~330-390 VGPRs, one wave per SIMD, and streamed at half the split-K
   // GEMM's rate (47 against 20 us at B = 8)
   if (a.M < 1 || a.M > 8 || a.K % 8 || a.K > 4096 || a.N < 1 || (dual && !a.W2)) return -1;
-  if (!dual && a.epi != EPI_F32 && a.epi != EPI_BF16 && a.epi != EPI_RESID) return -1;
+  if (!dual && a.epi != EPI_F32 && a.epi != EPI_BF16 && a.epi != EPI_F16 && a.epi != EPI_RESID)
+    return -1;
   if (a.lda % 8) return -1;   // 16-byte activation chunks
-  if (a.M <= 2) return dual ? launch_gemv_rows_mr<2, true>(a, st) : launch_gemv_rows_mr<2, false>(a, st);
-  if (a.M <= 4) return dual ? launch_gemv_rows_mr<4, true>(a, st) : launch_gemv_rows_mr<4, false>(a, st);
-  return dual ? launch_gemv_rows_mr<8, true>(a, st) : launch_gemv_rows_mr<8, false>(a, st);
+  if (a.M <= 2) return launch_gemv_rows_m<2>(a, st);
+  if (a.M <= 4) return launch_gemv_rows_m<4>(a, st);
+  return launch_gemv_rows_m<8>(a, st);
 }
 
 // ---------------------------------------------------------------------------

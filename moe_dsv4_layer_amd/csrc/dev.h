@@ -29,6 +29,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(ds4g_f32x2{a, b}, ds4g_bf16x2));
 }
 
+// ----------------------------------------------------------- fp16 <-> fp32
+// The attention path of a prefill (normalised input, low-rank code, q, k, v,
+// probabilities, attention output) and the KV ring carry IEEE binary16: three
+// more significand bits than bf16 at the same MFMA rate.  Conversions round
+// to nearest even.
+typedef _Float16 ds4g_f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(ds4g_f32x2{a, b}, ds4g_f16x2));
+}
+// 8 fp16 values (16 bytes) widened to fp32
+__device__ __forceinline__ void unpack8_f16(const uint4& q, float* f) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const ds4g_f16x2 h = __builtin_bit_cast(ds4g_f16x2, w[i]);
+    f[2 * i] = (float)h.x;
+    f[2 * i + 1] = (float)h.y;
+  }
+}
+
 // Load a stored scalar of either weight type as float.
 __device__ __forceinline__ float ldw(const uint16_t* p, long i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ float ldw(const float* p, long i) { return p[i]; }

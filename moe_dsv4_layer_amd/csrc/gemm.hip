@@ -1,9 +1,12 @@
 // GEMMs of the layer-major prefill: C = A . B^T with A the activations
 // [rows, K] and B the weights [N, K] (both K-contiguous).
 //
-//   gemm_dma   bf16 x bf16 -> fp32 on the gfx950 matrix cores
-//              (v_mfma_f32_32x32x16_bf16), BM x BN x 64 tiles, 4 or 8 waves,
-//              an S-stage LDS ring filled by direct global -> LDS loads.
+//   gemm_dma   bf16 x bf16 or fp16 x fp16 -> fp32 on the gfx950 matrix cores
+//              (v_mfma_f32_32x32x16_bf16 / _f16), BM x BN x 64 tiles, 4 or 8
+//              waves, an S-stage LDS ring filled by direct global -> LDS
+//              loads.  fp16 runs the attention path of a prefill (its
+//              activations in fp16 against fp16 images of the bf16 weights,
+//              see f16_image_kernel).
 //   gemm_simt  fp32 activations x (fp32 | bf16) weights on the vector ALUs,
 //              64x64x16 tiles, 4x4 outputs per thread.  Used where the
 //              activations must stay fp32 (the router logits decide integer
@@ -158,12 +161,25 @@ gemm_simt_kernel(GemmArgs g) {
 // up rows of the same output columns, so a wave's fragment pair (fn, fn+1)
 // holds gate and up of the same (row, col) in the same lane.
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+// one 32x32x16 step on 16-byte operand fragments of either 16-bit type
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma16(u32x4_t a, u32x4_t b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 
 template <int EPI>
 __device__ __forceinline__ void epi_store_t(const GemmArgs& g, int row, int col, float v) {
   if (EPI == EPI_F32) static_cast<float*>(g.C)[(long)row * g.ldc + col] = v;
   if (EPI == EPI_BF16) static_cast<uint16_t*>(g.C)[(long)row * g.ldc + col] = f32_to_bf16(v);
+  if (EPI == EPI_F16) static_cast<uint16_t*>(g.C)[(long)row * g.ldc + col] = f32_to_f16(v);
   if (EPI == EPI_RESID) {
     float* c = static_cast<float*>(g.C) + (long)row * g.ldc + col;
     *c = *c + v;
@@ -174,12 +190,23 @@ __device__ __forceinline__ void epi_store_t(const GemmArgs& g, int row, int col,
 // col0 + 32 j + lane%32 (SwiGLU: fragment pairs (j, j+1) give one column
 // block).  For the residual add the 16 old values of a fragment are loaded
 // before any of them is stored, so the loads overlap instead of alternating
-// with the stores.
+// with the stores.  A column factor (colscale) multiplies the accumulator
+// first: a power of two, so it changes no bit of the significand.
 template <int EPI, int FM, int FN>
-__device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, const f32x16 (&acc)[FM][FN],
+__device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, f32x16 (&acc)[FM][FN],
                                               int row0, int row1, int col0, int lane) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32);
   const int lr = lane & 31, lg = lane >> 5;
+  if (!DUAL && g.colscale) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const float f = g.colscale[min(col0 + j * 32 + lr, g.N - 1)];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= f;
+    }
+  }
   if (EPI == EPI_ROPE_QKV) {
     // the partner of column n in its rotation pair (n ^ 1) is in lane ^ 1:
     // x0' = x0 c - x1 s (even column), x1' = x0 s + x1 c (odd column).
@@ -225,7 +252,7 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, const f32x16 (&
                 __builtin_amdgcn_mov_dpp(__float_as_int(own), 0xB1, 0xF, 0xF, false));
             const float v = rot ? own * cv[ii] + sgn * oth * sv[ii] : own;
             const int row = rb + ii;
-            if (col < g.N && row < row1) dst[(long)row * ld] = f32_to_bf16(v);
+            if (col < g.N && row < row1) dst[(long)row * ld] = f32_to_f16(v);
           }
         }
     }
@@ -316,7 +343,7 @@ __device__ __forceinline__ bool xcd_tile(int nb, int& bx, int& by) {
   return true;
 }
 
-template <int BM, int BN, int WM, int WN, int S, int EPI>
+template <int BM, int BN, int WM, int WN, int S, int EPI, bool F16>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_dma_kernel(GemmArgs g) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32);
@@ -413,18 +440,15 @@ gemm_dma_kernel(GemmArgs g) {
     const u32x4_t* Bs = &smem[st][BM * 8];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[FM], bfr[FN];
+      u32x4_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = As[swz1(wm * TM + i * 32 + lr, ks * 2 + lg)];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = Bs[swz1(wn * TN + j * 32 + lr, ks * 2 + lg)];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, As[swz1(wm * TM + i * 32 + lr, ks * 2 + lg)]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, Bs[swz1(wn * TN + j * 32 + lr, ks * 2 + lg)]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<F16>(af[i], bfr[j], acc[i][j]);
     }
   };
 
@@ -453,38 +477,86 @@ int launch_dma_cfg(const GemmArgs& g, Exec st) {
   const int mt = g.tiles ? g.max_tiles : (g.M + BM - 1) / BM;
   const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
   const dim3 grid((g.N + bn_out - 1) / bn_out, mt, nsplit), block(64 * WM * WN);
+#define DS4G_DMA(E, F) \
+  DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, E, F>), grid, block, 0, st, g)
+  if (g.f16) {   // the attention path: fp16 operands
+    if (g.tiles) return -1;
+    switch (g.epi) {
+      case EPI_F32: DS4G_DMA(EPI_F32, true); break;
+      case EPI_F16: DS4G_DMA(EPI_F16, true); break;
+      case EPI_RESID: DS4G_DMA(EPI_RESID, true); break;
+      case EPI_ROPE_QKV:
+        if (nsplit > 1) return -1;
+        DS4G_DMA(EPI_ROPE_QKV, true);
+        break;
+      default: return -1;
+    }
+    return 0;
+  }
   switch (g.epi) {
-    case EPI_F32:
-      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_F32>), grid, block, 0, st, g);
-      break;
-    case EPI_BF16:
-      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_BF16>), grid, block, 0, st, g);
-      break;
-    case EPI_RESID:
-      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_RESID>), grid, block, 0, st, g);
-      break;
-    case EPI_SWIGLU_BF16:
-      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_SWIGLU_BF16>), grid, block, 0, st,
-                         g);
-      break;
-    case EPI_ROPE_QKV:
-      if (g.tiles || nsplit > 1) return -1;
-      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, EPI_ROPE_QKV>), grid, block, 0, st, g);
-      break;
+    case EPI_F32: DS4G_DMA(EPI_F32, false); break;
+    case EPI_BF16: DS4G_DMA(EPI_BF16, false); break;
+    case EPI_RESID: DS4G_DMA(EPI_RESID, false); break;
+    case EPI_SWIGLU_BF16: DS4G_DMA(EPI_SWIGLU_BF16, false); break;
     default: return -1;
   }
+#undef DS4G_DMA
   return 0;
 }
 
-// Split-K partial sums part[s][m][n] (s < nsplit, stride pstride), then the
-// epilogue: F32, BF16, RESID (C += sum) or SWIGLU_BF16 (C = bf16(silu(sum
-// part) * sum part2)).  A block takes 32 consecutive elements; its 8 groups of
+// fp16 image of bf16 weights, one wave per row (see launch_f16_image): the
+// largest magnitude of the row (bf16 magnitudes order like their bit
+// patterns), then every element times 2^s rounded to fp16, s = 14 - e with
+// 2^e <= max < 2^(e+1).  The row is read twice; the second read hits L2.
+__global__ void __launch_bounds__(256)
+f16_image_kernel(const uint16_t* __restrict__ W, int N, int K, uint16_t* __restrict__ img,
+                 float* __restrict__ inv) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const uint16_t* row = W + (long)n * K;
+  uint16_t* out = img + (long)n * K;
+  const int nchunk = K >> 3;
+  uint32_t mb = 0;
+  for (int c = lane; c < nchunk; c += 64) {
+    const uint4 q = *reinterpret_cast<const uint4*>(row + c * 8);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mb = max(mb, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  }
+  mb = (uint32_t)wave_max((float)mb);              // exact: below 2^15
+  const int eb = (int)(mb >> 7);                   // biased bf16 exponent of the largest
+  const int sc = (mb == 0 || eb == 255) ? 0 : 141 - eb;   // 14 - (eb - 127)
+  for (int c = lane; c < nchunk; c += 64) {
+    const uint4 q = *reinterpret_cast<const uint4*>(row + c * 8);
+    float f[8];
+    unpack8(q, f);
+    uint4 o;
+    o.x = pack_f16x2(ldexpf(f[0], sc), ldexpf(f[1], sc));
+    o.y = pack_f16x2(ldexpf(f[2], sc), ldexpf(f[3], sc));
+    o.z = pack_f16x2(ldexpf(f[4], sc), ldexpf(f[5], sc));
+    o.w = pack_f16x2(ldexpf(f[6], sc), ldexpf(f[7], sc));
+    *reinterpret_cast<uint4*>(out + c * 8) = o;
+  }
+  if (lane == 0) inv[n] = ldexpf(1.f, -sc);
+}
+
+int launch_f16_image(const uint16_t* W, int N, int K, uint16_t* img, float* inv, Exec st) {
+  if (N <= 0 || K <= 0 || K % 8) return -1;
+  DS4G_LAUNCH(f16_image_kernel, dim3((N + 3) / 4), dim3(256), 0, st, W, N, K, img, inv);
+  return 0;
+}
+
+// Split-K partial sums part[s][m][n] (s < nsplit, stride pstride), times the
+// column factor (colscale, optional), then the epilogue: F32, BF16, F16,
+// RESID (C += sum) or SWIGLU_BF16 (C = bf16(silu(sum part) * sum part2)).  A block takes 32 consecutive elements; its 8 groups of
 // 32 threads add the splits g, g + 8, ... of their element, and the 8 group
 // sums are added in group order (a fixed order: results do not depend on
 // timing).  Spreading the splits over threads keeps many loads in flight.
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ part, const float* __restrict__ part2, int nsplit,
-                     long pstride, int M, int N, int epi, void* C, int ldc) {
+                     long pstride, int M, int N, int epi, void* C, int ldc,
+                     const float* __restrict__ colscale) {
   __shared__ float acc[2][8][32];
   const int e = threadIdx.x & 31, g = threadIdx.x >> 5;
   const long i = (long)blockIdx.x * 32 + e;
@@ -507,10 +579,13 @@ splitk_reduce_kernel(const float* __restrict__ part, const float* __restrict__ p
 #pragma unroll
   for (int q = 0; q < 8; ++q) { v += acc[0][q][e]; u += acc[1][q][e]; }
   const int m = (int)(i / N), n = (int)(i - (long)m * N);
+  if (colscale) v *= colscale[n];
   if (epi == EPI_SWIGLU_BF16) {
     static_cast<uint16_t*>(C)[(long)m * ldc + n] = f32_to_bf16(silu(v) * u);
   } else if (epi == EPI_BF16) {
     static_cast<uint16_t*>(C)[(long)m * ldc + n] = f32_to_bf16(v);
+  } else if (epi == EPI_F16) {
+    static_cast<uint16_t*>(C)[(long)m * ldc + n] = f32_to_f16(v);
   } else if (epi == EPI_RESID) {
     float* c = static_cast<float*>(C) + (long)m * ldc + n;
     *c = *c + v;
@@ -520,12 +595,14 @@ splitk_reduce_kernel(const float* __restrict__ part, const float* __restrict__ p
 }
 
 int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long pstride, int M,
-                         int N, int epi, void* C, int ldc, Exec st) {
-  if (epi != EPI_F32 && epi != EPI_BF16 && epi != EPI_RESID && epi != EPI_SWIGLU_BF16) return -1;
-  if (epi == EPI_SWIGLU_BF16 && !part2) return -1;
+                         int N, int epi, void* C, int ldc, const float* colscale, Exec st) {
+  if (epi != EPI_F32 && epi != EPI_BF16 && epi != EPI_F16 && epi != EPI_RESID &&
+      epi != EPI_SWIGLU_BF16)
+    return -1;
+  if (epi == EPI_SWIGLU_BF16 && (!part2 || colscale)) return -1;
   const long n = (long)M * N;
   DS4G_LAUNCH(splitk_reduce_kernel, dim3((unsigned)((n + 31) / 32)), dim3(256), 0, st,
-                     part, part2, nsplit, pstride, M, N, epi, C, ldc);
+                     part, part2, nsplit, pstride, M, N, epi, C, ldc, colscale);
   return 0;
 }
 
@@ -563,7 +640,8 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, Exec st) {
         lo.M = g.M - mb;
         if (g.gather) lo.gather = g.gather + mb;
         else lo.A = static_cast<const uint16_t*>(g.A) + (long)mb * g.lda;
-        const size_t es = (g.epi == EPI_BF16 || g.epi == EPI_SWIGLU_BF16) ? 2 : 4;
+        const size_t es =
+            (g.epi == EPI_BF16 || g.epi == EPI_F16 || g.epi == EPI_SWIGLU_BF16) ? 2 : 4;
         lo.C = static_cast<char*>(g.C) + (size_t)mb * g.ldc * es;
         const int r = launch_dma_cfg<256, 256, 2, 4, 2>(hi, st);
         if (r) return r;

@@ -25,14 +25,19 @@ enum Epi {
   EPI_RESID = 2,        // C[r, n] += acc                     (fp32)
   EPI_SWIGLU_BF16 = 3,  // C[r, n] = bf16(silu(A.G^T) * (A.U^T))
   EPI_SWIGLU_F32 = 4,   // same, fp32 out
-  // [q | k | v] = A.B^T with RoPE applied to q and k, all rounded to bf16:
+  // [q | k | v] = A.B^T with RoPE applied to q and k, all rounded to fp16:
   // q -> C [rows, ldc], k -> rope_kc [rows, dh], v -> rope_vc [rows, dh]
-  EPI_ROPE_QKV = 5
+  EPI_ROPE_QKV = 5,
+  EPI_F16 = 6           // C[r, n] = fp16(acc)
 };
 
 struct GemmArgs {
-  const void* A;        // activations [rows, K]: bf16 (MFMA) or fp32 (SIMT)
+  const void* A;        // activations [rows, K]: bf16 / fp16 (MFMA) or fp32 (SIMT)
   int lda;
+  int f16;              // MFMA: A and B are fp16 (else bf16)
+  // optional per-output-column factor applied to the accumulator before the
+  // epilogue (the inverse of a weight row's power-of-two scale)
+  const float* colscale;
   const int* gather;    // optional: A row of output row r is gather[r]
   const void* B;        // weights [N, K] (group g at B + g*b_stride)
   const void* B2;       // SwiGLU: up weights (B holds gate)
@@ -61,16 +66,22 @@ struct GemmArgs {
   uint16_t* rope_kc;
   uint16_t* rope_vc;
 };
+// fp16 image of a bf16 weight matrix W [N, K]: row n is scaled by a power of
+// two 2^s_n that puts its largest magnitude in [2^14, 2^15) (s_n = 0 for a
+// zero row), so every bf16 value of magnitude at least 2^-32 times the row's
+// largest converts exactly; inv[n] = 2^-s_n undoes it in an epilogue.
+int launch_f16_image(const uint16_t* W, int N, int K, uint16_t* img, float* inv, Exec st);
 // cos / sin of pair i for rows t < T at position *pos + t into c / s
 // [i * ld + t] (rows T..ld-1: 1 and 0), i < rd / 2
 int launch_rope_table(const int64_t* pos, int T, int ld, int rd, float base, float* c, float* s,
                       Exec st);
 int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, Exec st);
 // sum of nsplit fp32 partials part[s * pstride + m * N + n] in split order,
-// then the epilogue epi (F32, BF16, RESID: C += sum, SWIGLU_BF16: part2 holds
-// the up projection's partials) into C [M, ldc]
+// then the column factor (colscale, optional) and the epilogue epi (F32,
+// BF16, F16, RESID: C += sum, SWIGLU_BF16: part2 holds the up projection's
+// partials) into C [M, ldc]
 int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long pstride, int M,
-                         int N, int epi, void* C, int ldc, Exec st);
+                         int N, int epi, void* C, int ldc, const float* colscale, Exec st);
 
 // ---------------------------------------------------------------- GEMV
 // out[n] (= or +=) sum_k W[n, k] xs[k], xs = x or RMSNorm(x) * gamma.
@@ -88,15 +99,17 @@ template <typename WT>
 int launch_gemv(const GemvArgs& a, Exec st);
 
 // out[m, n] = sum_k W[n, k] X[m, k] for the M <= 8 rows of a batched decode
-// call: W [N, K] bf16 (row stride K), X [M, K] bf16 (row stride lda).  epi:
-// EPI_F32, EPI_BF16, EPI_RESID (C[m, n] += out) or EPI_SWIGLU_BF16 (W: gate,
-// W2: up, C = bf16(silu(gate) * up)); C [M, ldc].  -1 when the shape is not
-// covered (M > 8, K > 4096, K % 8), launching nothing.
+// call: W [N, K] bf16 (row stride K), X [M, K] bf16 or fp16 (x_f16; row
+// stride lda).  epi: EPI_F32, EPI_BF16, EPI_F16, EPI_RESID (C[m, n] += out) or
+// EPI_SWIGLU_BF16 (W: gate, W2: up, C = bf16(silu(gate) * up)); C [M, ldc].
+// -1 when the shape is not covered (M > 8, K > 4096, K % 8), launching
+// nothing.
 struct GemvRowsArgs {
   const uint16_t* W;
   const uint16_t* W2;
   int N, K;
   const uint16_t* X;
+  int x_f16;
   int lda, M;
   int epi;
   void* C;
@@ -110,14 +123,14 @@ struct AttnArgs {
   int T, H, dh, rd, W;
   float base;
   int64_t* pos;         // device
-  void* q;              // [T, H, dh] rotated (fp32)
-  int q_bf16;
-  uint16_t* kc;         // [T, dh] bf16 rotated keys
-  uint16_t* vc;         // [T, dh] bf16 values
-  uint16_t* ring_k;
+  void* q;              // [T, H, dh] rotated (fp32, or fp16 with q_f16)
+  int q_f16;
+  uint16_t* kc;         // [T, dh] fp16 rotated keys
+  uint16_t* vc;         // [T, dh] fp16 values
+  uint16_t* ring_k;     // fp16 [W, dh] (batched decode: [B, W, dh])
   uint16_t* ring_v;
-  void* o;              // [T, H*dh] attention output
-  int o_bf16;
+  void* o;              // [T, H*dh] attention output (fp32, or fp16 with o_f16)
+  int o_f16;
   int heads_per_block;
   int rope_done;        // MFMA prefill: q, kc, vc already rotated (QKV GEMM epilogue)
 };
@@ -126,10 +139,10 @@ int launch_attention(const AttnArgs& a, Exec st);
 // slot, attend over the window; o fp32 [H*dh].  Does not advance *pos.
 int launch_attention_decode(const AttnArgs& a, Exec st);
 // B independent sequences, one token each: row b of qkv at position pos[b],
-// ring b at ring_k / ring_v + b * W * dh; o [B, H*dh] fp32 or bf16 (o_bf16).
+// ring b at ring_k / ring_v + b * W * dh; o [B, H*dh] fp32 or fp16 (o_f16).
 // Does not advance pos (the layer's last kernel, the combine, does).
 int launch_attention_decode_batch(const AttnArgs& a, int B, Exec st);
-// prefill on the matrix cores: bf16 q (q_bf16 = 1) and o (o_bf16 = 1)
+// prefill on the matrix cores: fp16 q (q_f16 = 1) and o (o_f16 = 1)
 int launch_attention_prefill_mfma(const AttnArgs& a, Exec st);
 
 // ---------------------------------------------------------------- decode MoE
@@ -156,9 +169,12 @@ template <typename WT>
 int launch_moe_decode(const MoeDecodeArgs& a, float* x, int64_t* pos_inc, Exec st);
 
 // ---------------------------------------------------------------- prefill misc
+// RMSNorm(x) * gamma of T rows into any of: fp32, bf16, fp16, and the
+// three-term bf16 split y1 | y2 | y3 (y1 = bf16(y), y2 = bf16(y - y1), ...)
 template <typename WT>
 int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps,
-                        float* out_f32, uint16_t* out_bf16, uint16_t* out_split3, Exec st);
+                        float* out_f32, uint16_t* out_bf16, uint16_t* out_f16,
+                        uint16_t* out_split3, Exec st);
 
 struct RouteArgs {
   const float* logits;  // nsplit partial sums [nsplit][T][E], added in order

@@ -14,7 +14,7 @@ namespace ds4g {
 
 // ------------------------------------------------------------ RMSNorm rows
 // y = RMSNorm(x[t]) * gamma per row; outputs (each optional): fp32 of, bf16
-// ob, and os3 = the exact three-term bf16 split [y1 | y2 | y3] (row stride
+// ob, fp16 oh, and os3 = the exact three-term bf16 split [y1 | y2 | y3] (row stride
 // 3d): y1 = bf16(y), y2 = bf16(y - y1), y3 = bf16(y - y1 - y2).  Products of
 // the terms with bf16 weights are exact in fp32 and y - y1 - y2 - y3 is below
 // 2^-27 |y|, so a bf16 MFMA GEMM over the split gives fp32-quality results.
@@ -32,7 +32,8 @@ __device__ __forceinline__ void load_gain4(const float* g, int i, float* o) {
 template <typename WT>
 __global__ void __launch_bounds__(256)
 rmsnorm_rows_kernel(const float* __restrict__ x, int d, const WT* __restrict__ gamma, float eps,
-                    float* __restrict__ of, uint16_t* __restrict__ ob, uint16_t* __restrict__ os3) {
+                    float* __restrict__ of, uint16_t* __restrict__ ob, uint16_t* __restrict__ oh,
+                    uint16_t* __restrict__ os3) {
   // the row stays in registers between the sum of squares and the scaling
   // (d <= 256 * 4 * RMS_CHUNKS); all of a thread's loads go out together
   __shared__ float red[16];
@@ -74,6 +75,12 @@ rmsnorm_rows_kernel(const float* __restrict__ x, int d, const WT* __restrict__ g
       return p;
     };
     if (ob) *reinterpret_cast<uint2*>(ob + t * d + i) = pack(b1);
+    if (oh) {
+      uint2 p;
+      p.x = pack_f16x2(y[0], y[1]);
+      p.y = pack_f16x2(y[2], y[3]);
+      *reinterpret_cast<uint2*>(oh + t * d + i) = p;
+    }
     if (os3) {
       uint16_t* o = os3 + t * 3 * d + i;
       *reinterpret_cast<uint2*>(o) = pack(b1);
@@ -85,16 +92,16 @@ rmsnorm_rows_kernel(const float* __restrict__ x, int d, const WT* __restrict__ g
 
 template <typename WT>
 int launch_rmsnorm_rows(const float* x, int T, int d, const WT* gamma, float eps, float* of,
-                        uint16_t* ob, uint16_t* os3, Exec st) {
+                        uint16_t* ob, uint16_t* oh, uint16_t* os3, Exec st) {
   if (d % 4 || d > 1024 * RMS_CHUNKS) return -1;
   DS4G_LAUNCH((rmsnorm_rows_kernel<WT>), dim3(T), dim3(256), 0, st, x, d, gamma, eps, of,
-                     ob, os3);
+                     ob, oh, os3);
   return 0;
 }
 template int launch_rmsnorm_rows<uint16_t>(const float*, int, int, const uint16_t*, float,
-                                           float*, uint16_t*, uint16_t*, Exec);
+                                           float*, uint16_t*, uint16_t*, uint16_t*, Exec);
 template int launch_rmsnorm_rows<float>(const float*, int, int, const float*, float, float*,
-                                        uint16_t*, uint16_t*, Exec);
+                                        uint16_t*, uint16_t*, uint16_t*, Exec);
 
 // ------------------------------------------------------------ top-k per token
 // One wave per token: k rounds of a wave arg-max (lower index wins ties) over

@@ -30,8 +30,8 @@ class Stack:
         self.vocab = head["lm_head"].shape[0]
         self.device = device
         dh, W = shape.head_dim, shape.window
-        self.ring_k = [torch.zeros((W, dh), dtype=torch.bfloat16, device=device) for _ in layers]
-        self.ring_v = [torch.zeros((W, dh), dtype=torch.bfloat16, device=device) for _ in layers]
+        self.ring_k = [torch.zeros((W, dh), dtype=torch.float16, device=device) for _ in layers]
+        self.ring_v = [torch.zeros((W, dh), dtype=torch.float16, device=device) for _ in layers]
         self.pos = [torch.zeros(1, dtype=torch.int64, device=device) for _ in layers]
         self.rings = [make_ring(k, v, p) for k, v, p in zip(self.ring_k, self.ring_v, self.pos)]
         self.ws = alloc_workspace(workspace_bytes(self.cfg, max_tokens, self.vocab), device)

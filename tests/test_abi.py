@@ -102,8 +102,11 @@ def test_decode_and_sample_reject_before_launch():
     L = ds4g.lib
     assert L.ds4g_layer_decode(ctypes.byref(c), ctypes.byref(w), ctypes.byref(ring), None, None,
                                0x1000, n, None) == ds4g.ERR_INVALID_ARG
+    # ds4g_workspace_bytes is the largest need of any layer call (a prefill
+    # of that many tokens, with its fp16 weight images); the decode step
+    # needs far less, and refuses a workspace below its own need
     assert L.ds4g_layer_decode(ctypes.byref(c), ctypes.byref(w), ctypes.byref(ring), 0x1000,
-                               None, 0x1000, n - 1, None) == ds4g.ERR_WORKSPACE
+                               None, 0x1000, 4096, None) == ds4g.ERR_WORKSPACE
     ns = ds4g.workspace_bytes(None, 0, 129280)
     args = dict(hidden=4096, vocab=129280, wd=ds4g.BF16, norm=0x1000, eps=1e-6, w=0x1000, x=0x1000,
                 T=0.7, p=0.95, rng=0x1000, logits=0x1000, tok=0x1000, ws=0x1000, n=ns)

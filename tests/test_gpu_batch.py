@@ -40,7 +40,7 @@ class Batch:
         self.w = synth.layer_weights(shape, seed, layer=0, device="cuda")
         self.cfg, self.cw = ds4g.make_cfg(shape), ds4g.make_weights(self.w)
         dh, W = shape.head_dim, shape.window
-        self.rk = torch.zeros((self.B, W, dh), dtype=torch.bfloat16, device="cuda")
+        self.rk = torch.zeros((self.B, W, dh), dtype=torch.float16, device="cuda")
         self.rv = torch.zeros_like(self.rk)
         self.pos = torch.zeros(self.B, dtype=torch.int64, device="cuda")
         self.rings = ds4g.make_ring(self.rk, self.rv, self.pos)
@@ -131,7 +131,7 @@ def test_batch_matches_single_decode_full_size():
     w = synth.layer_weights(s, wl.seed, layer=0, device="cuda")
     cw = ds4g.make_weights(w)
     W, dh = s.window, s.head_dim
-    rk = torch.zeros((B, W, dh), dtype=torch.bfloat16, device="cuda")
+    rk = torch.zeros((B, W, dh), dtype=torch.float16, device="cuda")
     rv = torch.zeros_like(rk)
     pos = torch.zeros(B, dtype=torch.int64, device="cuda")
     ws = ds4g.alloc_workspace(ds4g.workspace_bytes(cfg, W))

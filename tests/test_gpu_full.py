@@ -6,10 +6,9 @@ window 128, 256 experts top-6 + 1 shared, inter 1024, bf16 weights).
 
 Inputs are drawn so every token's router margin (gap between the 6th and 7th
 largest logit, from the oracle) is at least 1e-3: rows below it are redrawn
-(a new candidate row from the seeded generator) until none is left.  The
-oracle evaluates the expert FFNs only for sampled rows (they are the costly
-part); routing, attention and everything before the experts are checked on
-every row.
+(a new candidate row from the seeded generator) until none is left.  Every
+row of the output is compared with the oracle, and every row's expert set
+must equal the oracle's.
 """
 import numpy as np
 import pytest
@@ -53,28 +52,39 @@ def full_layer():
 
 
 def test_full_prefill_2048(full_layer):
+    """Every one of the 2048 rows against the oracle, each under its own bound,
+    and the end-to-end expert sets equal on every row (all have oracle margin
+    >= 1e-3): the attention path's fp16 activations keep the router input
+    within ~1e-4 of the oracle's, far inside the margin."""
     shape, gl, wh = full_layer
     T = 2048
     gl.pos.zero_()
     h, attempts = _draw_with_margin(shape, wh, T, 1003)
     log(f"  redrawn rows: {int((attempts > 0).sum())}")
     x, bufs = gl.prefill(h)
-    rows = sorted({0, 1, 63, 127, 128, 129, 500, 1023, 1024, 1500, 2000, 2046, 2047})
     ring = oracle.Ring(shape.window, shape.head_dim)
-    orc = oracle.layer_forward(shape, wh, ring, h.cpu().numpy(), rows=rows)
+    orc = oracle.layer_forward(shape, wh, ring, h.cpu().numpy())
     c = orc["count"]
     log(f"  tokens per expert: min {c.min()} max {c.max()}")
     assert c.min() >= 20 and c.max() <= 80, "workload: every expert gets 20..80 tokens"
     g = to_np(bufs)
     out = x.cpu().numpy().astype(np.float64)
     hh = h.cpu().numpy().astype(np.float64)
-    e_out = rel_l2(out[rows], orc["out"][rows])
-    e_inc = rel_l2(out[rows] - hh[rows], orc["out"][rows] - hh[rows])
+    ref = orc["out"]
+    e_out = rel_l2(out, ref)
+    e_inc = rel_l2(out - hh, ref - hh)
+    row_out = np.linalg.norm(out - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    row_inc = np.linalg.norm(out - ref, axis=1) / np.linalg.norm(ref - hh, axis=1)
     e_y = rel_l2(g["router_in"], orc["y"])
     e_lg = rel_l2(g["router_logits"], orc["logits"])
-    st = check_routing(shape, wh, g, orc, label="full prefill")
-    log(f"full prefill: rel_l2 out={e_out:.2e} inc={e_inc:.2e} y={e_y:.2e} logits={e_lg:.2e} {st}")
+    lg_abs = float(np.abs(g["router_logits"] - orc["logits"]).max())
+    st = check_routing(shape, wh, g, orc, label="full prefill", margin_gate=MARGIN)
+    log(f"full prefill: rel_l2 out={e_out:.2e} inc={e_inc:.2e} y={e_y:.2e} logits={e_lg:.2e} "
+        f"(max abs {lg_abs:.2e}) per-row out max {row_out.max():.2e} inc max {row_inc.max():.2e} "
+        f"(row {int(row_inc.argmax())}) {st}")
+    assert st["flips"] == 0 and st["e2e_rows"] == T
     assert e_out < LAYER_TOL and e_inc < LAYER_TOL and e_y < LAYER_TOL
+    assert row_out.max() < LAYER_TOL and row_inc.max() < LAYER_TOL
     assert int(gl.pos.item()) == T
     rk = gl.ring_k.float().cpu().numpy()
     assert rel_l2(rk, ring.k) < 1e-2 and rel_l2(gl.ring_v.float().cpu().numpy(), ring.v) < 1e-2
@@ -98,7 +108,7 @@ def test_full_decode_at_128(full_layer):
     hh = h[128:129].cpu().numpy().astype(np.float64)
     e_out = rel_l2(out, orc["out"])
     e_inc = rel_l2(out - hh, orc["out"] - hh)
-    st = check_routing(shape, wh, g, orc, label="full decode")
+    st = check_routing(shape, wh, g, orc, label="full decode", margin_gate=MARGIN)
     log(f"full decode: rel_l2 out={e_out:.2e} inc={e_inc:.2e} {st}")
     assert e_out < LAYER_TOL and e_inc < LAYER_TOL
     assert int(gl.pos.item()) == 129
