@@ -10,7 +10,7 @@ prefix costs a near-full prefill).
 With a sliding-window ring the live state cannot be rewound: the slots of
 positions after the common prefix have overwritten the window before it.
 So the session keeps checkpoints, every layer's ring plus the position
-(2 x window x head_dim bf16 per layer), at chosen positions, and a prompt
+(2 x window x head_dim fp16 per layer), at chosen positions, and a prompt
 that leaves the live stream is served from the latest checkpoint at or
 before the common prefix, prefilling only the rest.  Layer-major prefill
 gives every token the same arithmetic whatever batch it arrives in (spans of

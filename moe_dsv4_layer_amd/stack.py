@@ -64,16 +64,20 @@ class Stack:
         return x
 
     def prefill(self, x: torch.Tensor, layer_inputs: Optional[list] = None,
-                routing: Optional[list] = None) -> torch.Tensor:
+                routing: Optional[list] = None,
+                capture: Optional[Dict[int, torch.Tensor]] = None) -> torch.Tensor:
         """Layer-major prefill of x [T, hidden] (updated in place) through
         every layer.  layer_inputs, if a list, receives a copy of each
-        layer's input; routing, if a list of dicts, gets each layer's
+        layer's input; capture, if a dict, a copy of the input of each layer
+        named by its keys; routing, if a list of dicts, gets each layer's
         routing buffers."""
         T = x.shape[0]
         assert T <= self.max_tokens
         for l in range(len(self.layers)):
             if layer_inputs is not None:
                 layer_inputs.append(x.clone())
+            if capture is not None and l in capture:
+                capture[l] = x.clone()
             r = make_routing(routing[l]) if routing is not None else None
             layer_prefill(self.cfg, self.cw[l], self.rings[l], x, T, self.ws, r)
         return x

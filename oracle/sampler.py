@@ -59,16 +59,18 @@ def min_p_mask(q: np.ndarray, min_p: float) -> np.ndarray:
 def sample(logits, temperature: float, top_p: float, u: float, min_p: float = 0.0) -> dict:
     """Sample one token id.  u in [0, 1) is the generator's draw.
 
-    Returns dict(token, n_kept, kept_sum, r, gap, min_p_gap) where gap is
-    the smallest distance, relative to kept_sum, between r and a running-sum
-    boundary of the roulette, and min_p_gap the smallest relative distance of
-    a weight from the min-p threshold (inf without min-p); a test uses them
-    to spot draws that sit on a boundary.
+    Returns dict(token, n_kept, kept_sum, r, gap, cut_gap, min_p_gap) where
+    gap is the smallest distance, relative to kept_sum, between r and a
+    running-sum boundary of the roulette; cut_gap the distance between top_p
+    and the nearer of the two descending cumulative shares around the top-p
+    cut (inf when top_p >= 1 keeps everything); min_p_gap the smallest
+    relative distance of a weight from the min-p threshold (inf without
+    min-p).  A test uses them to spot draws that sit on a boundary.
     """
     l = np.asarray(logits, dtype=np.float64)
     if temperature <= 0.0:
         return dict(token=argmax(l), n_kept=1, kept_sum=1.0, r=0.0, gap=np.inf,
-                    min_p_gap=np.inf)
+                    cut_gap=np.inf, min_p_gap=np.inf)
     q = np.exp((l - np.max(l)) / temperature)
     keep = nucleus(q, top_p) & min_p_mask(q, min_p)
     kept_idx = np.nonzero(keep)[0]                 # index order
@@ -83,4 +85,20 @@ def sample(logits, temperature: float, top_p: float, u: float, min_p: float = 0.
         thr = min(min_p, 1.0) * np.max(q)
         mgap = float(np.min(np.abs(q - thr)) / thr)
     return dict(token=tok, n_kept=int(kept_idx.size), kept_sum=float(S),
-                r=float(r), gap=gap, min_p_gap=mgap)
+                r=float(r), gap=gap, cut_gap=nucleus_cut_gap(q, top_p), min_p_gap=mgap)
+
+
+def nucleus_cut_gap(q: np.ndarray, top_p: float) -> float:
+    """Distance between top_p and the descending cumulative shares on either
+    side of the top-p cut: the cut keeps n tokens, so the shares after n - 1
+    and after n tokens straddle top_p; the smaller distance is how far the
+    weights may move before the cut moves.  inf when top_p >= 1."""
+    if top_p >= 1.0:
+        return float("inf")
+    n = q.shape[0]
+    order = np.lexsort((np.arange(n), -q))
+    cum = np.cumsum(q[order]) / np.sum(q)
+    n_keep = min(max(int(np.searchsorted(cum, top_p, side="left")) + 1, 1), n)
+    hi = cum[n_keep - 1]
+    lo = cum[n_keep - 2] if n_keep >= 2 else 0.0
+    return float(min(abs(hi - top_p), abs(top_p - lo)))

@@ -136,3 +136,33 @@ def check_routing(shape, w_host, gpu: dict, orc: dict, rows=None, margin_gate=1e
     np.testing.assert_array_equal(gpu["perm"], perm)
     return dict(tf_rows=int(ok_tf.sum()), e2e_rows=int(e2e.sum()), flips=flips,
                 below_tf=int((~ok_tf).sum()))
+
+
+def sampler_share_tol(logits, temperature: float) -> float:
+    """How far the GPU's kept-mass shares can sit from the oracle's.
+
+    The GPU takes each weight as expf of the fp32 argument (l - max) / T --
+    a rounded subtraction and a rounded division, each within 2^-24 of the
+    argument, then expf within one ulp (2^-23) -- and sums fixed-point
+    masses exactly, each truncated by at most 2^-45.  So a weight moves by
+    at most q (2 |x| 2^-24 + 2^-23) + 2^-45 and any running share C/S by at
+    most twice the sum of that over the vocabulary, divided by S."""
+    if temperature <= 0.0:
+        return 0.0
+    l = np.asarray(logits, dtype=np.float64)
+    x = (l - l.max()) / temperature
+    q = np.exp(x)
+    dq = q * (2.0 * np.abs(x) * 2.0 ** -24 + 2.0 ** -23) + 2.0 ** -45
+    return float(2.0 * dq.sum() / q.sum())
+
+
+def sampler_excused(ref: dict, logits, temperature: float) -> bool:
+    """A GPU/oracle token mismatch is excused only when the draw sits closer
+    to a roulette boundary, the top-p cut or the min-p threshold than the
+    GPU's fp32 weights can move it (sampler_share_tol)."""
+    tol = sampler_share_tol(logits, temperature)
+    x_max = float(np.abs((np.asarray(logits, np.float64) - np.max(logits)) / temperature).max()) \
+        if temperature > 0 else 0.0
+    q_rel = 2.0 * x_max * 2.0 ** -24 + 2.0 ** -23
+    return ref["gap"] < tol or ref.get("cut_gap", np.inf) < tol or \
+        ref.get("min_p_gap", np.inf) < 2.0 * q_rel

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from tests.harness import log, rel_l2
+from tests.harness import log, rel_l2, sampler_excused, sampler_share_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -82,10 +82,12 @@ def test_sampler_teacher_forced(temperature, top_p):
             agree += 1
             continue
         # different tokens are only acceptable on a boundary of the roulette
-        # or of the nucleus (fp32 weights on the GPU vs fp64 in the oracle)
-        assert ref["gap"] < 1e-5, (i, tok, ref)
+        # or of the nucleus, closer than the GPU's fp32 weights can move it
+        assert sampler_excused(ref, logits, temperature), (i, tok, ref,
+                                                           sampler_share_tol(logits, temperature))
         amb += 1
-    log(f"sampler T={temperature} p={top_p}: {agree} equal, {amb} on a boundary")
+    log(f"sampler T={temperature} p={top_p}: {agree} equal, {amb} on a boundary "
+        f"(share tolerance {sampler_share_tol(logits, temperature):.1e})")
     assert agree >= 22
 
 
@@ -100,7 +102,7 @@ def test_sampler_small_vocab_grid():
         _, tok, state = _run(hw, shape, 1024, x, 0.8, 0.9, st_in, ws)
         u = oracle.SplitMix64(st_in).next_f32()
         ref = oracle.sample(logits, 0.8, 0.9, u)
-        assert tok == ref["token"] or ref["gap"] < 1e-5, (i, tok, ref)
+        assert tok == ref["token"] or sampler_excused(ref, logits, 0.8), (i, tok, ref)
 
 
 def _run_ex(hw, shape, vocab, x, temperature, top_p, min_p, state, ws, tdev=None):
@@ -133,7 +135,7 @@ def test_sampler_min_p_teacher_forced(temperature, top_p, min_p):
         if tok == ref["token"]:
             agree += 1
             continue
-        assert ref["gap"] < 1e-5 or ref["min_p_gap"] < 1e-5, (i, tok, ref)
+        assert sampler_excused(ref, logits, temperature), (i, tok, ref)
         amb += 1
     log(f"sampler T={temperature} p={top_p} min_p={min_p}: {agree} equal, {amb} on a boundary")
     assert agree >= 18

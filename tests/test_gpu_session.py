@@ -3,12 +3,16 @@ checkpoint plus a suffix prefill must end in exactly the state (every ring,
 position, last hidden state, logits) of a session that prefills the whole
 prompt at once; the checkpointed chunks and the one-shot prefill tile the
 tokens differently, so this also pins that layer-major prefill does not
-depend on how a prompt is split."""
+depend on how a prompt is split.  The resumed state is also compared with
+the oracle's layer-major prefill of the new prompt (last hidden state,
+rings, logits and the greedy token)."""
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
-from tests.harness import log, small_shape
+from tests.harness import log, rel_l2, small_shape
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +62,27 @@ def test_session_reuse_is_bit_exact(wdtype):
     la, ta = _logits(live.stack, live.last_hidden)
     lb, tb = _logits(fresh.stack, fresh.last_hidden)
     assert torch.equal(la, lb) and ta == tb
+    # the resumed session against the oracle's prefill of prompt B
+    wh = [synth.weights_to_host(w) for w in layers]
+    hh = {k: synth.to_host(v) for k, v in head.items()}
+    rings = [oracle.Ring(shape.window, shape.head_dim) for _ in layers]
+    xo, _ = oracle.stack_prefill(shape, wh, rings, oracle.embed(B, hh["embed"]))
+    e_h = rel_l2(live.last_hidden.cpu().numpy(), xo[-1])
+    lo = oracle.lm_head(xo[-1], hh["final_norm"], hh["lm_head"], shape.rms_eps)
+    e_lg = rel_l2(la.cpu().numpy(), lo)
+    lt = oracle.lm_head(live.last_hidden.cpu().numpy(), hh["final_norm"], hh["lm_head"],
+                        shape.rms_eps)
+    e_tf = rel_l2(la.cpu().numpy(), lt)
+    e_r = max(max(rel_l2(live.stack.ring_k[l].float().cpu().numpy(), rings[l].k),
+                  rel_l2(live.stack.ring_v[l].float().cpu().numpy(), rings[l].v))
+              for l in range(n_layers))
+    srt = np.sort(lo)
+    log(f"session {wdtype} vs oracle: hidden {e_h:.2e}, logits {e_lg:.2e} (lm_head alone "
+        f"{e_tf:.2e}), rings {e_r:.2e}, top-2 gap {srt[-1] - srt[-2]:.2e}")
+    assert e_h < 1e-2 and e_r < 1e-2 and e_lg < 1e-2 and e_tf < 2e-3
+    assert all(int(live.stack.pos[l].item()) == rings[l].pos == len(B) for l in range(n_layers))
+    if srt[-1] - srt[-2] > 1e-2:
+        assert ta == oracle.argmax(lo)
     # the live stream grows by decoding; a prompt that extends it is served live
     x = live.stack.embed(torch.tensor([ta], dtype=torch.int32, device="cuda"))[0]
     live.decode_token(ta, x)

@@ -11,6 +11,10 @@ prefill, decode loop, lm_head + sampler, ring snapshot/resume).
                    tokens, a ring snapshot, restore, and the 148-token suffix
                    (the rebuild-vs-reuse case); the two runs must agree bit
                    for bit on the GPU.
+  stack43 16994  : the same prompt in one chunk per layer (256x256 dense
+                   tiles, 256-row expert tiles) and in 2048-token chunks
+                   (128x128 and 64-row tiles) must agree bit for bit; oracle
+                   windows across the whole prompt at layers 0, 21 and 42.
 
 A float64 oracle of 43 full-size layers over 16994 tokens is out of reach in
 a test; the 43-layer checks are: layer 0 against the oracle on the seeded
@@ -24,7 +28,7 @@ import torch
 
 import oracle
 import synth
-from tests.harness import log, rel_l2
+from tests.harness import log, rel_l2, sampler_excused, sampler_share_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -151,13 +155,15 @@ def test_stack43_prefill_and_sampled_decode(stack43):
         state = g.state
         ref = oracle.sample(logits, wl.temperature, wl.top_p, u)
         assert e < LOGIT_TOL, (step, e)
-        assert tok == ref["token"] or ref["gap"] < 1e-5, (step, tok, ref)
+        assert tok == ref["token"] or sampler_excused(ref, logits, wl.temperature), \
+            (step, tok, ref, sampler_share_tol(logits, wl.temperature))
         agree += tok == ref["token"]
         assert np.array_equal(xl.cpu().numpy().astype(np.float64),
                               oracle.embed([tok], hh["embed"])[0])
         st.decode(xl)
     assert int(rng.cpu().numpy().view(np.uint64)[0]) == state
     log(f"stack43 sampled decode: {agree}/8 tokens equal to the oracle sampler")
+    assert agree >= 7
     assert all(int(p.item()) == T + 8 for p in st.pos)
 
 
@@ -197,3 +203,106 @@ def test_stack43_resume_is_bit_exact(stack43):
     e = rel_l2(got[sel - (s.window - 1)], r["out"][sel])
     log(f"stack43 resume: suffix bit-exact; layer 0 vs oracle rel_l2 {e:.2e}")
     assert e < LAYER_TOL
+
+
+def _routing_bufs(T, k, device="cuda"):
+    return {"topk_idx": torch.full((T, k), -1, dtype=torch.int32, device=device)}
+
+
+def _window_rows(label, s, got_out, xin, r, gpu_topk, rows):
+    """Per-row parity of oracle window rows (survey protocol for the
+    43-layer stacks): a row whose expert set differs from the oracle's must
+    have an oracle router margin below 1e-3 (a near-tie; listed, and left
+    out of the error figures); every other row's layer increment must be
+    within the layer tolerance.  Returns (rel_l2 over the kept rows, flips)."""
+    rows = np.asarray(rows)
+    flips = [int(t) for t in rows
+             if set(gpu_topk[t].tolist()) != set(r["topk_idx"][t].tolist())]
+    for t in flips:
+        assert r["margin"][t] < 1e-3, (label, t, float(r["margin"][t]))
+    keep = np.asarray([t for t in rows if t not in flips])
+    inc_g = got_out[keep] - xin[keep]
+    inc_o = r["out"][keep] - xin[keep]
+    per_row = np.linalg.norm(inc_g - inc_o, axis=1) / np.linalg.norm(inc_o, axis=1)
+    assert per_row.max() < LAYER_TOL, (label, float(per_row.max()))
+    return rel_l2(inc_g, inc_o), flips
+
+
+def test_stack43_16994_chunked_and_oracle_windows(stack43):
+    """The 16994-token prefill's own tile shapes: the one-shot prefill runs
+    W_o and the shared expert on 256x256 tiles and the routed experts on
+    256-row tiles; 2048-token chunks run 128x128 and 64-row tiles.  Every
+    output element sums its K products in one order whatever the tiling, so
+    the two must agree bit for bit (final hidden state and every ring).
+
+    Oracle windows: a token's layer output depends on its layer input and
+    the 127 inputs before it, so the oracle fed a slice of 143 consecutive
+    inputs (empty ring at the slice start) reproduces the last 16 rows
+    exactly.  Slices across the whole prompt at layer 0 (embedding input),
+    21 and 42 (the GPU's own layer inputs, teacher-forced).  Rows 0..15 of
+    the prompt (1..16 keys) are reported apart from full-window rows.  The
+    prompt is random token ids, not redrawn for router margins: rows whose
+    expert set differs from the oracle's must be near-ties (margin < 1e-3)
+    and are listed."""
+    _, s, layers, head, st = stack43
+    wl = synth.WORKLOADS["stack43_resume"]
+    T = wl.prompt
+    ids = synth.token_ids(T, 129280, wl.seed)
+    ids_d = torch.as_tensor(ids, device="cuda")
+    check = (0, 21, 42)
+    keep = (0, 1, 21, 22, 42)
+    st.reset()
+    x_one = st.embed(ids_d)
+    cap = {l: None for l in keep}
+    routing = [_routing_bufs(T, s.top_k) if l in check else {} for l in range(len(layers))]
+    st.prefill(x_one, capture=cap, routing=routing)
+    one_snap = st.snapshot()
+    st.reset()
+    x_chunk = st.embed(ids_d)
+    C = 2048
+    for c0 in range(0, T, C):
+        part = x_chunk[c0:c0 + C]
+        st.prefill(part)
+    torch.cuda.synchronize()
+    assert torch.equal(x_one, x_chunk), "chunked prefill differs from the one-shot prefill"
+    for (k, v, p), (ok, ov, op) in zip(st.snapshot(), one_snap):
+        assert torch.equal(k, ok) and torch.equal(v, ov) and int(p.item()) == int(op.item()) == T
+    log("stack43 16994: one-shot and 2048-token chunks bit-identical (hidden and 43 rings)")
+
+    W, m = s.window, 16
+    starts = [0, 2000, 4100, 6150, 8190, 10240, 12300, 14336, 16200, T - (W - 1) - m]
+    outs = {0: cap[1], 21: cap[22], 42: x_one}
+    emb_host = synth.to_host(head["embed"])
+    worst, nflip = 0.0, 0
+    for l in check:
+        wh = _host(layers[l])
+        topk = routing[l]["topk_idx"].cpu().numpy()
+        errs = []
+        for a in starts:
+            sl = slice(a, a + W - 1 + m)
+            if l == 0:
+                xin = oracle.embed(ids[sl], emb_host)
+            else:
+                xin = cap[l][sl].cpu().numpy().astype(np.float64)
+            ring = oracle.Ring(s.window, s.head_dim)
+            ring.pos = a
+            rows = list(range(W - 1, W - 1 + m)) + (list(range(m)) if a == 0 else [])
+            r = oracle.layer_forward(s, wh, ring, xin, rows=rows)
+            got = outs[l][sl].cpu().numpy().astype(np.float64)
+            e_full, fl = _window_rows(f"layer {l} window {a}", s, got, xin, r, topk[sl],
+                                      range(W - 1, W - 1 + m))
+            errs.append((a + W - 1, e_full, [a + t for t in fl]))
+            worst = max(worst, e_full)
+            nflip += len(fl)
+            if a == 0:
+                e_few, fl0 = _window_rows(f"layer {l} rows 0..15", s, got, xin, r, topk[sl],
+                                          range(m))
+                nflip += len(fl0)
+                log(f"  layer {l}: positions 0..15 (1..16 keys) increment rel_l2 {e_few:.2e}"
+                    + (f", near-tie flips at {fl0}" if fl0 else ""))
+        log(f"  layer {l}: full-window increment rel_l2 by first position: " +
+            ", ".join(f"{p}: {e:.2e}" + (f" (near-tie flips at {f})" if f else "")
+                      for p, e, f in errs))
+    log(f"stack43 16994 oracle windows: worst increment rel_l2 {worst:.2e} over rows with the "
+        f"oracle's expert set; {nflip} near-tie rows with another set")
+    assert worst < LAYER_TOL

@@ -173,3 +173,32 @@ def test_min_p_brute_force_interval_lookup():
                 continue
             assert got["n_kept"] == int(kept.sum())
             assert got["token"] == _page_roulette(q.tolist(), kept.tolist(), u)
+
+
+def test_nucleus_cut_gap_closed_forms():
+    from oracle.sampler import nucleus_cut_gap
+    # weights 1, 2, 3, 4: descending shares 0.4, 0.7, 0.9, 1.0
+    q = np.array([1.0, 2.0, 3.0, 4.0])
+    assert nucleus_cut_gap(q, 0.69) == pytest.approx(0.01)      # cut after 0.7, 0.4 below
+    assert nucleus_cut_gap(q, 0.5) == pytest.approx(0.1)        # between 0.4 and 0.7
+    assert nucleus_cut_gap(q, 0.7) == pytest.approx(0.0)        # on a boundary
+    assert nucleus_cut_gap(q, 0.1) == pytest.approx(0.1)        # first share 0.4; 0 below
+    assert nucleus_cut_gap(q, 1.0) == float("inf")
+    # the dict carries it; temperature 1 on log weights reproduces q
+    r = sample(np.log(q), 1.0, 0.69, 0.3)
+    assert r["cut_gap"] == pytest.approx(0.01)
+    assert sample(np.log(q), 0.0, 0.69, 0.3)["cut_gap"] == float("inf")
+
+
+def test_nucleus_cut_gap_bounds_a_moved_cut():
+    # moving every weight by less than the cut gap (relative share) leaves the
+    # kept set alone; moving one weight across it changes the set
+    r = np.random.default_rng(5)
+    from oracle.sampler import nucleus_cut_gap
+    for _ in range(50):
+        q = r.exponential(size=40)
+        p = float(r.uniform(0.2, 0.95))
+        g = nucleus_cut_gap(q, p)
+        eps = 0.2 * g / 2
+        q2 = q * (1 + r.uniform(-eps, eps, size=q.size))
+        assert np.array_equal(nucleus(q, p), nucleus(q2, p))
