@@ -137,6 +137,23 @@ typedef struct {
   float *router_logits;    /* [T, E]  s                                       */
 } ds4g_routing;
 
+/* Optional copies of a prefill's intermediate activations, in the order the
+ * layer computes them (阶段四 4.2), for step-by-step parity checks: each
+ * step's output can be compared with that step applied to the previous
+ * step's copy.  Device memory; any member may be NULL.  "act" is the
+ * attention path's activation type: fp16 with bf16 weights, fp32 with fp32
+ * weights; k and v are always fp16 (the ring's type).
+ *   x_norm [T, hidden]    act   RMSNorm(h) * g1, as QKV-A read it
+ *   c      [T, qkv_rank]  act   A x_norm
+ *   q      [T, H*dh]      act   B c, query heads, after RoPE
+ *   k, v   [T, dh]        fp16  B c, key after RoPE, value (as cached)
+ *   o      [T, H*dh]      act   attention output, as W_o read it
+ *   h2     [T, hidden]    fp32  h + W_o o */
+typedef struct {
+  void *x_norm, *c, *q, *k, *v, *o;
+  float *h2;
+} ds4g_trace;
+
 /* Bytes of workspace that covers every layer call for up to max_tokens
  * tokens (the largest need is a prefill's: its activations plus the fp16
  * images of QKV-A, QKV-B and W_o), and ds4g_lmhead_sample for `vocab` (pass
@@ -166,6 +183,12 @@ int ds4g_layer_prefill(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
                        ds4g_kv_ring *ring, float *x, int32_t T,
                        ds4g_routing *routing, void *ws, size_t ws_bytes,
                        void *stream);
+
+/* ds4g_layer_prefill that also writes the intermediate activations named in
+ * `trace` (NULL: none).  Same arguments, results and errors otherwise. */
+int ds4g_layer_prefill_trace(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w,
+                             ds4g_kv_ring *ring, float *x, int32_t T, ds4g_routing *routing,
+                             const ds4g_trace *trace, void *ws, size_t ws_bytes, void *stream);
 
 /* One decode step (T = 1) of the layer at position *ring->pos (阶段四 4.2).
  * Same contract as ds4g_layer_prefill with T = 1; uses the bandwidth-bound

@@ -20,6 +20,7 @@ MODE_PREFILL, MODE_DECODE, MODE_DECODE_BATCH = 0, 1, 2
 
 # ds4g.h declares these functions; the ABI test checks the header agrees.
 EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_supported", "ds4g_layer_prefill",
+           "ds4g_layer_prefill_trace",
            "ds4g_layer_decode", "ds4g_layer_decode_noalloc", "ds4g_layer_decode_batch",
            "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_status_string")
 
@@ -59,6 +60,13 @@ class Routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ROUTING_NAMES]
 
 
+TRACE_NAMES = ("x_norm", "c", "q", "k", "v", "o", "h2")
+
+
+class Trace(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in TRACE_NAMES]
+
+
 class Ds4gError(RuntimeError):
     pass
 
@@ -95,6 +103,12 @@ def _load() -> ctypes.CDLL:
     lib.ds4g_layer_prefill.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
                                        ctypes.POINTER(KvRing), P, ctypes.c_int32,
                                        ctypes.POINTER(Routing), P, ctypes.c_size_t, P]
+    lib.ds4g_layer_prefill_trace.restype = ctypes.c_int
+    lib.ds4g_layer_prefill_trace.argtypes = [ctypes.POINTER(LayerCfg),
+                                             ctypes.POINTER(LayerWeights),
+                                             ctypes.POINTER(KvRing), P, ctypes.c_int32,
+                                             ctypes.POINTER(Routing), ctypes.POINTER(Trace), P,
+                                             ctypes.c_size_t, P]
     lib.ds4g_layer_decode.restype = ctypes.c_int
     lib.ds4g_layer_decode.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights),
                                       ctypes.POINTER(KvRing), P, ctypes.POINTER(Routing), P,
@@ -193,6 +207,20 @@ def layer_prefill(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x, T: int, ws,
                                 ctypes.byref(routing) if routing is not None else None,
                                 ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "ds4g_layer_prefill")
+
+
+def layer_prefill_trace(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x, T: int, ws,
+                        trace: Dict[str, "torch.Tensor"], routing: Optional[Routing] = None,
+                        stream=None) -> None:
+    """ds4g_layer_prefill_trace: the prefill, plus copies of its intermediate
+    activations into the tensors named in `trace` (keys of TRACE_NAMES)."""
+    tr = Trace(*[_ptr(trace.get(n)) for n in TRACE_NAMES])
+    rc = lib.ds4g_layer_prefill_trace(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(ring),
+                                      x.data_ptr(), T,
+                                      ctypes.byref(routing) if routing is not None else None,
+                                      ctypes.byref(tr), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "ds4g_layer_prefill_trace")
 
 
 def layer_decode(cfg: LayerCfg, w: LayerWeights, ring: KvRing, x, ws,

@@ -189,7 +189,7 @@ int dry_then_run(hipStream_t stream, F&& seq) {
 // experts over T rows; only the attention stage differs.
 int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ring& ring,
                  float* x, int T, ds4g_routing* routing, void* ws, Exec st,
-                 bool batch = false) {
+                 bool batch = false, const ds4g_trace* trace = nullptr) {
   const Layout L = layout(c, T, true);
   const bool bf = c.wdtype == DS4G_BF16;
   const int d = c.hidden, r = c.qkv_rank, H = c.n_heads, dh = c.head_dim, qd = H * dh,
@@ -301,6 +301,16 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
 
   // h2 = h + W_o o   (in place in x)
   gemm(at<void>(ws, L.o), qd, w.wo, T, d, qd, EPI_RESID, x, d, nullptr, 2);
+  if (trace) {   // the attention path's buffers are intact until the next call
+    const size_t ae = bf ? 2 : 4;   // activation element size
+    copy_out(trace->x_norm, at<void>(ws, L.xn), (size_t)T * d * ae, st);
+    copy_out(trace->c, at<void>(ws, L.c), (size_t)T * r * ae, st);
+    copy_out(trace->q, at<void>(ws, L.q), (size_t)T * qd * ae, st);
+    copy_out(trace->k, at<void>(ws, L.kc), (size_t)T * dh * 2, st);
+    copy_out(trace->v, at<void>(ws, L.vc), (size_t)T * dh * 2, st);
+    copy_out(trace->o, at<void>(ws, L.o), (size_t)T * qd * ae, st);
+    copy_out(trace->h2, x, (size_t)T * d * 4, st);
+  }
 
   // y = RMSNorm(h2) * g2: fp32, and (bf16 weights) its three-term bf16 split,
   // whose first term is bf16(y), the expert GEMMs' input
@@ -545,6 +555,16 @@ int ds4g_layer_prefill(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
   if (s != DS4G_OK) return s;
   return dry_then_run((hipStream_t)stream, [&](Exec ex) {
     return prefill_impl(*cfg, *w, *ring, x, T, routing, ws, ex);
+  });
+}
+
+int ds4g_layer_prefill_trace(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w,
+                             ds4g_kv_ring* ring, float* x, int32_t T, ds4g_routing* routing,
+                             const ds4g_trace* trace, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_call(cfg, w, ring, x, T, ws, ws_bytes, DS4G_MODE_PREFILL);
+  if (s != DS4G_OK) return s;
+  return dry_then_run((hipStream_t)stream, [&](Exec ex) {
+    return prefill_impl(*cfg, *w, *ring, x, T, routing, ws, ex, false, trace);
   });
 }
 
