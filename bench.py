@@ -114,6 +114,93 @@ def cpu_baseline(shape, w_dev, h_dev, n_tokens: int):
                       f"window pre-filled with {shape.window} positions), {dt:.1f} s"}
 
 
+def cpu_baseline_prefill(shape, w_dev, n_tokens: int, seed: int):
+    """The float64 oracle prefilling `n_tokens` fresh N(0, 1) rows through one
+    full-size layer from an empty ring (layer-major, every expert each token
+    routes to), timed on the host."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    wh = synth.weights_to_host(w_dev)
+    h = synth.hidden(n_tokens, shape.hidden, seed).numpy()
+    ring = oracle.Ring(shape.window, shape.head_dim)
+    t0 = time.perf_counter()
+    oracle.layer_forward(shape, wh, ring, h)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer-major prefill of {n_tokens} tokens through one full-size layer "
+                      f"(float64 numpy, empty ring), {dt:.1f} s"}
+
+
+def measured_peaks(dev) -> dict:
+    """What the chip sustains right now: a 1 GiB device copy (read + write)
+    and the bf16 MFMA loop of ds4g_probe_mfma (4 blocks per CU)."""
+    import torch
+    import moe_dsv4_layer_amd as ds4g
+    out = {}
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out["hbm_copy_gbs"] = round(5 * 2 * 4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    blocks, iters = 1024, 400
+    buf = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+    ds4g.probe_mfma(blocks, iters, buf)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    ds4g.probe_mfma(blocks, iters, buf)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fl = blocks * 4 * iters * 8 * 2.0 * 32 * 32 * 16
+    out["mfma_bf16_tflops"] = round(fl / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    return out
+
+
+def gpu_clocks() -> dict:
+    """Current clocks from rocm-smi (best effort; text as rocm-smi prints it)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                           timeout=20)
+        lines = [ln.strip() for ln in r.stdout.splitlines()
+                 if "clock level" in ln or "sclk" in ln or "mclk" in ln or "fclk" in ln]
+        return {"rocm_smi_showclocks": lines[:12]}
+    except Exception as e:   # rocm-smi missing or refused
+        return {"rocm_smi_showclocks": f"unavailable ({type(e).__name__})"}
+
+
+def expert_loads(counts) -> dict:
+    """Per-layer routing summary from each layer's expert_count: experts
+    that received a token, and the largest load."""
+    import numpy as np
+    touched = [int((c > 0).sum()) for c in counts]
+    mx = [int(c.max()) for c in counts]
+    return {"touched_experts_by_layer": touched, "max_load_by_layer": mx,
+            "touched_min": min(touched), "touched_mean": round(float(np.mean(touched)), 1)}
+
+
+def touched_weight_bytes(s, touched) -> int:
+    """Weight bytes a prefill must read when layer l's tokens reach only
+    touched[l] routed experts: every dense weight plus those experts."""
+    d, r, H, dh, I = s.hidden, s.qkv_rank, s.n_heads, s.head_dim, s.ffn_inter
+    dense = 2 * (r * d + (H * dh + 2 * dh) * r + d * H * dh + s.n_experts * d + 3 * I * d + 2 * d)
+    return int(sum(dense + 2 * 3 * I * d * t for t in touched))
+
+
 def stack_decode_bytes(s, n_layers: int, vocab: int) -> int:
     """Per token: every layer's decode bytes, then the final norm and lm_head
     rows, and the next token's embedding row."""
@@ -150,6 +237,27 @@ def bench_stack43(decode_steps: int) -> dict:
     ms_pre = e0.elapsed_time(e1)
     out["prefill_512_ms"] = round(ms_pre, 3)
     out["prefill_512_tok_s"] = round(wl.prompt / (ms_pre * 1e-3), 1)
+
+    def routed_counts(run):
+        """Each layer's expert_count from an untimed repeat of a prefill."""
+        bufs = [{"expert_count": torch.zeros(s.n_experts, dtype=torch.int32, device="cuda")}
+                for _ in range(wl.n_layers)]
+        run(bufs)
+        torch.cuda.synchronize()
+        return [b["expert_count"].cpu().numpy() for b in bufs]
+
+    def run512(bufs):
+        st.reset()
+        st.prefill(st.embed(ids), routing=bufs)
+    loads = expert_loads(routed_counts(run512))
+    tb = touched_weight_bytes(s, loads["touched_experts_by_layer"])
+    out["prefill_512_routing"] = loads
+    out["prefill_512_touched_weight_bytes"] = tb
+    out["prefill_512_hbm_frac_touched"] = round(tb / (ms_pre * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    st.reset()
+    x = st.embed(ids)
+    st.prefill(x)
+    torch.cuda.synchronize()
     rng = torch.tensor([synth.rng_seed(wl.seed) & 0x7FFFFFFFFFFFFFFF], dtype=torch.int64,
                        device="cuda")
     xl = x[-1].clone()
@@ -211,6 +319,22 @@ def bench_stack43(decode_steps: int) -> dict:
     out["prefill_16994_mfma_frac"] = round(fl / (ms_full * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     out["resume_suffix_148_ms"] = round(ms_suf, 3)
     out["resume_suffix_matches_full"] = bool(torch.equal(xs, x[P:]))
+
+    def run_full(bufs):
+        st.reset()
+        st.prefill(st.embed(ids), routing=bufs)
+
+    def run_suffix(bufs):
+        st.restore(snap)
+        st.prefill(st.embed(ids[P:]), routing=bufs)
+    loads = expert_loads(routed_counts(run_full))
+    out["prefill_16994_routing"] = loads
+    loads = expert_loads(routed_counts(run_suffix))
+    tb = touched_weight_bytes(s, loads["touched_experts_by_layer"])
+    out["resume_suffix_148_routing"] = loads
+    out["resume_suffix_148_touched_weight_bytes"] = tb
+    out["resume_suffix_148_hbm_frac_touched"] = round(tb / (ms_suf * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                                      4)
     del st, layers, head
     torch.cuda.empty_cache()
     return out
@@ -225,6 +349,7 @@ def main() -> int:
     ap.add_argument("--weight-sets", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--cpu-prefill-tokens", type=int, default=256)
     ap.add_argument("--no-graph", action="store_true", help="launch decode eagerly")
     ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer workloads")
     ap.add_argument("--stack-decode-steps", type=int, default=256)
@@ -339,19 +464,33 @@ def main() -> int:
     dec_gbs = dec_bytes / (ms_decode * 1e-3) / 1e9
 
     # ------------------------------------------------------------ prefill timing
+    # every call: fresh N(0, 1) rows at positions 0..2047 from an empty ring
+    # (the input copy and position reset sit outside the timed events)
     hp = synth.hidden(T_pre, s.hidden, synth.WORKLOADS["layer_prefill_2048"].seed, device=dev)
-    xp = hp.clone()
+    xp = torch.empty_like(hp)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.prefill_steps)]
+
+    def prefill_call(i, evs=None, routing=None):
+        L = layers[i % nl]
+        L["pos"].zero_()
+        xp.copy_(hp)
+        if evs:
+            evs[0].record(stream)
+        ds4g.layer_prefill(cfg, L["cw"], L["ring"], xp, T_pre, ws, routing, stream=stream)
+        if evs:
+            evs[1].record(stream)
     for i in range(2):
-        L = layers[i % nl]
-        ds4g.layer_prefill(cfg, L["cw"], L["ring"], xp, T_pre, ws, stream=stream)
+        prefill_call(i)
     torch.cuda.synchronize()
-    e0.record(stream)
     for i in range(args.prefill_steps):
-        L = layers[i % nl]
-        ds4g.layer_prefill(cfg, L["cw"], L["ring"], xp, T_pre, ws, stream=stream)
-    e1.record(stream)
+        prefill_call(i, ev[i])
     torch.cuda.synchronize()
-    ms_prefill = e0.elapsed_time(e1) / args.prefill_steps
+    ms_prefill = sum(a.elapsed_time(b) for a, b in ev) / args.prefill_steps
+    cnt = torch.zeros(s.n_experts, dtype=torch.int32, device=dev)
+    prefill_call(0, routing=ds4g.make_routing({"expert_count": cnt}))
+    torch.cuda.synchronize()
+    pre_load = (int(cnt.min().item()), int(cnt.max().item()))
     pre_tflops = layer_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
     pre_dense_tflops = dense_gemm_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
 
@@ -426,7 +565,9 @@ def main() -> int:
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
                      "algorithmic_bytes": dec_bytes},
-        "prefill": {"workload": "same layer, layer-major prefill of 2048 tokens",
+        "prefill": {"workload": "same layer, layer-major prefill of 2048 fresh N(0,1) rows at "
+                                "positions 0..2047 (empty ring)",
+                    "expert_load_min_max": list(pre_load),
                     "tok_s": round(T_pre / (ms_prefill * 1e-3), 1),
                     "ms": round(ms_prefill, 4),
                     "tflops_all": round(pre_tflops, 1),
@@ -448,6 +589,12 @@ def main() -> int:
         rec["stack43"] = bench_stack43(args.stack_decode_steps)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(s, w_cpu, h_all, args.cpu_tokens)
+        rec["cpu_baseline_prefill"] = cpu_baseline_prefill(
+            s, w_cpu, args.cpu_prefill_tokens, synth.WORKLOADS["layer_prefill_2048"].seed)
+    rec["measured_peaks"] = measured_peaks(dev)
+    rec["measured_peaks"]["roofline_frac_vs_copy"] = round(
+        rec["roofline"]["achieved"] / rec["measured_peaks"]["hbm_copy_gbs"], 4)
+    rec["clocks"] = gpu_clocks()
     print(json.dumps(rec))
     return 0
 

@@ -294,6 +294,14 @@ int ds4g_lmhead_sample_ex(int32_t hidden, int32_t vocab, int32_t wdtype,
 int ds4g_embed(int32_t vocab, int32_t hidden, int32_t wdtype, const void *table,
                const int32_t *ids, int32_t T, float *x, void *stream);
 
+/* Calibration of the matrix-core roofline: `blocks` blocks of 4 waves each
+ * issue iters x 8 independent bf16 v_mfma_f32_32x32x16 steps on register
+ * operands (2*32*32*16 flops each), with no memory traffic but one float per
+ * wave written to out (device, blocks*4 floats).  Time it with events on
+ * `stream`: flops / time is the rate the chip sustains at its current clocks.
+ * DS4G_ERR_INVALID_ARG for a non-positive size or NULL out. */
+int ds4g_probe_mfma(int32_t blocks, int32_t iters, float *out, void *stream);
+
 /* Static text for a ds4g_status value. */
 const char *ds4g_status_string(int status);
 

@@ -22,7 +22,8 @@ MODE_PREFILL, MODE_DECODE, MODE_DECODE_BATCH = 0, 1, 2
 EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_supported", "ds4g_layer_prefill",
            "ds4g_layer_prefill_trace",
            "ds4g_layer_decode", "ds4g_layer_decode_noalloc", "ds4g_layer_decode_batch",
-           "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_status_string")
+           "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_probe_mfma",
+           "ds4g_status_string")
 
 
 class LayerCfg(ctypes.Structure):
@@ -133,6 +134,8 @@ def _load() -> ctypes.CDLL:
     lib.ds4g_embed.restype = ctypes.c_int
     lib.ds4g_embed.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
                                ctypes.c_int32, P, P]
+    lib.ds4g_probe_mfma.restype = ctypes.c_int
+    lib.ds4g_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
     lib.ds4g_status_string.restype = ctypes.c_char_p
     lib.ds4g_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -284,6 +287,12 @@ def embed(vocab: int, hidden: int, wdtype: int, table, ids, x, stream=None) -> N
     rc = lib.ds4g_embed(vocab, hidden, wdtype, table.data_ptr(), ids.data_ptr(), ids.numel(),
                         x.data_ptr(), _stream(stream))
     _check(rc, "ds4g_embed")
+
+
+def probe_mfma(blocks: int, iters: int, out, stream=None) -> None:
+    """ds4g_probe_mfma: blocks x 4 waves of iters x 8 bf16 32x32x16 MFMAs."""
+    _check(lib.ds4g_probe_mfma(blocks, iters, out.data_ptr(), _stream(stream)),
+           "ds4g_probe_mfma")
 
 
 def alloc_workspace(nbytes: int, device="cuda"):

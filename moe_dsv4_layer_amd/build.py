@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libds4g.so")
-SOURCES = ["api.hip", "decode.hip", "attn.hip", "gemm.hip", "route.hip", "sample.hip"]
+SOURCES = ["api.hip", "decode.hip", "attn.hip", "gemm.hip", "route.hip", "sample.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
