@@ -353,10 +353,18 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch decode eagerly")
     ap.add_argument("--no-stack", action="store_true", help="skip the 43-layer workloads")
     ap.add_argument("--stack-decode-steps", type=int, default=256)
+    ap.add_argument("--sections", default="decode,prefill,batch,lmhead,stack,cpu,peaks",
+                    help="comma list of what to run (profiling runs pick one); the JSON line "
+                         "carries only what ran")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB on the device 5 times (calibrates the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE against a known size) and exit")
     args = ap.parse_args()
+    want = set(args.sections.split(","))
+    if args.no_stack:
+        want.discard("stack")
+    if args.no_cpu_baseline:
+        want.discard("cpu")
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
@@ -441,116 +449,124 @@ def main() -> int:
             print(f"graph capture failed ({e}); timing eager launches", file=sys.stderr)
             graph = None
 
-    # ------------------------------------------------------------ decode timing
     nl = len(layers)
-    steps = args.steps
-    if graph is not None:
-        steps = max(nl, (steps // nl) * nl)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    if graph is not None:
-        for _ in range(steps // nl):
-            graph.replay()
-    else:
-        for i in range(steps):
-            decode_step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_decode = e0.elapsed_time(e1) / steps
+    ms_decode = steps = t_wall = dec_gbs = None
     dec_bytes = layer_decode_bytes(s)
-    dec_gbs = dec_bytes / (ms_decode * 1e-3) / 1e9
-
-    # ------------------------------------------------------------ prefill timing
-    # every call: fresh N(0, 1) rows at positions 0..2047 from an empty ring
-    # (the input copy and position reset sit outside the timed events)
-    hp = synth.hidden(T_pre, s.hidden, synth.WORKLOADS["layer_prefill_2048"].seed, device=dev)
-    xp = torch.empty_like(hp)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.prefill_steps)]
-
-    def prefill_call(i, evs=None, routing=None):
-        L = layers[i % nl]
-        L["pos"].zero_()
-        xp.copy_(hp)
-        if evs:
-            evs[0].record(stream)
-        ds4g.layer_prefill(cfg, L["cw"], L["ring"], xp, T_pre, ws, routing, stream=stream)
-        if evs:
-            evs[1].record(stream)
-    for i in range(2):
-        prefill_call(i)
-    torch.cuda.synchronize()
-    for i in range(args.prefill_steps):
-        prefill_call(i, ev[i])
-    torch.cuda.synchronize()
-    ms_prefill = sum(a.elapsed_time(b) for a, b in ev) / args.prefill_steps
-    cnt = torch.zeros(s.n_experts, dtype=torch.int32, device=dev)
-    prefill_call(0, routing=ds4g.make_routing({"expert_count": cnt}))
-    torch.cuda.synchronize()
-    pre_load = (int(cnt.min().item()), int(cnt.max().item()))
-    pre_tflops = layer_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
-    pre_dense_tflops = dense_gemm_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
-
-    # ------------------------------------------------------------ batched decode
-    # one token of each of B sequences per call (rings at position 128; the
-    # projections, router and experts run over the B rows, weights read once)
-    batch = {}
-    for B in (8, 32, 128):
-        rkb = torch.zeros((B, s.window, s.head_dim), dtype=torch.float16, device=dev)
-        rvb = torch.zeros_like(rkb)
-        posb = torch.full((B,), s.window, dtype=torch.int64, device=dev)
-        ringb = ds4g.make_ring(rkb, rvb, posb)
-        xb0 = synth.hidden(B, s.hidden, 7000 + B, device=dev)
-        xb = xb0.clone()
-        for i in range(2):
-            xb.copy_(xb0)
-            ds4g.layer_decode_batch(cfg, layers[i % nl]["cw"], ringb, xb, B, ws, stream=stream)
+    # ------------------------------------------------------------ decode timing
+    if "decode" in want:
+        nl = len(layers)
+        steps = args.steps
+        if graph is not None:
+            steps = max(nl, (steps // nl) * nl)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        nb_steps = 8
+        t_wall = time.perf_counter()
         e0.record(stream)
-        for i in range(nb_steps):
-            ds4g.layer_decode_batch(cfg, layers[i % nl]["cw"], ringb, xb, B, ws, stream=stream)
+        if graph is not None:
+            for _ in range(steps // nl):
+                graph.replay()
+        else:
+            for i in range(steps):
+                decode_step(i)
         e1.record(stream)
         torch.cuda.synchronize()
-        ms_b = e0.elapsed_time(e1) / nb_steps
-        batch[str(B)] = {"ms_per_step": round(ms_b, 4), "tok_s": round(B / (ms_b * 1e-3), 1)}
-        del rkb, rvb, posb, xb, xb0
+        t_wall = time.perf_counter() - t_wall
+        ms_decode = e0.elapsed_time(e1) / steps
+        dec_bytes = layer_decode_bytes(s)
+        dec_gbs = dec_bytes / (ms_decode * 1e-3) / 1e9
+
+    # ------------------------------------------------------------ prefill timing
+    if "prefill" in want:
+        # every call: fresh N(0, 1) rows at positions 0..2047 from an empty ring
+        # (the input copy and position reset sit outside the timed events)
+        hp = synth.hidden(T_pre, s.hidden, synth.WORKLOADS["layer_prefill_2048"].seed, device=dev)
+        xp = torch.empty_like(hp)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.prefill_steps)]
+
+        def prefill_call(i, evs=None, routing=None):
+            L = layers[i % nl]
+            L["pos"].zero_()
+            xp.copy_(hp)
+            if evs:
+                evs[0].record(stream)
+            ds4g.layer_prefill(cfg, L["cw"], L["ring"], xp, T_pre, ws, routing, stream=stream)
+            if evs:
+                evs[1].record(stream)
+        for i in range(2):
+            prefill_call(i)
+        torch.cuda.synchronize()
+        for i in range(args.prefill_steps):
+            prefill_call(i, ev[i])
+        torch.cuda.synchronize()
+        ms_prefill = sum(a.elapsed_time(b) for a, b in ev) / args.prefill_steps
+        cnt = torch.zeros(s.n_experts, dtype=torch.int32, device=dev)
+        prefill_call(0, routing=ds4g.make_routing({"expert_count": cnt}))
+        torch.cuda.synchronize()
+        pre_load = (int(cnt.min().item()), int(cnt.max().item()))
+        pre_tflops = layer_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
+        pre_dense_tflops = dense_gemm_flops(s, T_pre) / (ms_prefill * 1e-3) / 1e12
+
+    # ------------------------------------------------------------ batched decode
+    batch = {}
+    if "batch" in want:
+        # one token of each of B sequences per call (rings at position 128; the
+        # projections, router and experts run over the B rows, weights read once)
+        for B in (8, 32, 128):
+            rkb = torch.zeros((B, s.window, s.head_dim), dtype=torch.float16, device=dev)
+            rvb = torch.zeros_like(rkb)
+            posb = torch.full((B,), s.window, dtype=torch.int64, device=dev)
+            ringb = ds4g.make_ring(rkb, rvb, posb)
+            xb0 = synth.hidden(B, s.hidden, 7000 + B, device=dev)
+            xb = xb0.clone()
+            for i in range(2):
+                xb.copy_(xb0)
+                ds4g.layer_decode_batch(cfg, layers[i % nl]["cw"], ringb, xb, B, ws, stream=stream)
+            torch.cuda.synchronize()
+            nb_steps = 8
+            e0.record(stream)
+            for i in range(nb_steps):
+                ds4g.layer_decode_batch(cfg, layers[i % nl]["cw"], ringb, xb, B, ws, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_b = e0.elapsed_time(e1) / nb_steps
+            batch[str(B)] = {"ms_per_step": round(ms_b, 4), "tok_s": round(B / (ms_b * 1e-3), 1)}
+            del rkb, rvb, posb, xb, xb0
 
     # ------------------------------------------------------------ lm_head + sampler
-    V = 129280
-    hw = synth.head_weights(s, V, 1004, device=dev)
-    logits = torch.empty(V, dtype=torch.float32, device=dev)
-    tok = torch.zeros(1, dtype=torch.int32, device=dev)
-    rng = torch.tensor([synth.rng_seed(1004) & 0x7FFFFFFFFFFFFFFF], dtype=torch.int64,
-                       device=dev)
-    xl = xs[0].clone()
+    if "lmhead" in want:
+        V = 129280
+        hw = synth.head_weights(s, V, 1004, device=dev)
+        logits = torch.empty(V, dtype=torch.float32, device=dev)
+        tok = torch.zeros(1, dtype=torch.int32, device=dev)
+        rng = torch.tensor([synth.rng_seed(1004) & 0x7FFFFFFFFFFFFFFF], dtype=torch.int64,
+                           device=dev)
+        xl = xs[0].clone()
 
-    def lm_step():
-        ds4g.lmhead_sample(s.hidden, V, ds4g.BF16, hw["final_norm"], s.rms_eps, hw["lm_head"],
-                           xl, 0.7, 0.95, rng, logits, tok, ws, stream=stream)
-    for _ in range(5):
-        lm_step()
-    torch.cuda.synchronize()
-    n_lm = 50
-    e0.record(stream)
-    for _ in range(n_lm):
-        lm_step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us_lm = e0.elapsed_time(e1) / n_lm * 1e3
-    lm_bytes = 2 * V * s.hidden + 2 * s.hidden + 4 * V
+        def lm_step():
+            ds4g.lmhead_sample(s.hidden, V, ds4g.BF16, hw["final_norm"], s.rms_eps, hw["lm_head"],
+                               xl, 0.7, 0.95, rng, logits, tok, ws, stream=stream)
+        for _ in range(5):
+            lm_step()
+        torch.cuda.synchronize()
+        n_lm = 50
+        e0.record(stream)
+        for _ in range(n_lm):
+            lm_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_lm = e0.elapsed_time(e1) / n_lm * 1e3
+        lm_bytes = 2 * V * s.hidden + 2 * s.hidden + 4 * V
 
     rec = {
         "metric": "decode tok/s + layer-major prefill tok/s; % HBM BW (decode), % MFMA (prefill)",
-        "value": round(1e3 / ms_decode, 2),
+        "value": round(1e3 / ms_decode, 2) if ms_decode else None,
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_decode, 5),
+        "ms_per_step": round(ms_decode, 5) if ms_decode else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -560,41 +576,49 @@ def main() -> int:
                                "(hidden 4096, 64-head MQA dh 128, QKV rank 1024, window 128, "
                                "256 experts top-6 + 1 shared, SwiGLU inter 1024, bf16 weights)",
                    "weight_sets_rotated": nl, "graph": graph is not None,
-                   "global_batch": 1, "seq_len": 1, "parallelism": "none"},
-        "roofline": {"bound": "hbm", "kernel": "ds4g_layer_decode (whole layer step)",
-                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
-                     "algorithmic_bytes": dec_bytes},
-        "prefill": {"workload": "same layer, layer-major prefill of 2048 fresh N(0,1) rows at "
-                                "positions 0..2047 (empty ring)",
-                    "expert_load_min_max": list(pre_load),
-                    "tok_s": round(T_pre / (ms_prefill * 1e-3), 1),
-                    "ms": round(ms_prefill, 4),
-                    "tflops_all": round(pre_tflops, 1),
-                    "mfma_frac_all": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "weight_bytes": prefill_weight_bytes(s),
-                    "hbm_frac_weights": round(prefill_weight_bytes(s) / (ms_prefill * 1e-3)
-                                              / 1e9 / HBM_PEAK_GBS, 4)},
-        "decode_batch": {"workload": "same layer, one decode token of each of B sequences per "
-                                     "call (ds4g_layer_decode_batch), weight sets rotated",
-                         "by_B": batch},
-        "lmhead_sample": {"workload": "RMSNorm + lm_head 129280x4096 bf16 + T=0.7 top-p 0.95",
-                          "us": round(us_lm, 2),
-                          "hbm_frac": round(lm_bytes / (us_lm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
-        "wall_s_decode": round(t_wall, 3),
+                   "global_batch": 1, "seq_len": 1, "parallelism": "none",
+                   "sections": sorted(want)},
     }
-    if not args.no_stack:
+    if ms_decode:
+        rec["roofline"] = {"bound": "hbm", "kernel": "ds4g_layer_decode (whole layer step)",
+                           "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
+                           "algorithmic_bytes": dec_bytes}
+        rec["wall_s_decode"] = round(t_wall, 3)
+    if "prefill" in want:
+        rec["prefill"] = {"workload": "same layer, layer-major prefill of 2048 fresh N(0,1) rows "
+                                      "at positions 0..2047 (empty ring)",
+                          "expert_load_min_max": list(pre_load),
+                          "tok_s": round(T_pre / (ms_prefill * 1e-3), 1),
+                          "ms": round(ms_prefill, 4),
+                          "tflops_all": round(pre_tflops, 1),
+                          "mfma_frac_all": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "weight_bytes": prefill_weight_bytes(s),
+                          "hbm_frac_weights": round(prefill_weight_bytes(s) / (ms_prefill * 1e-3)
+                                                    / 1e9 / HBM_PEAK_GBS, 4)}
+    if "batch" in want:
+        rec["decode_batch"] = {"workload": "same layer, one decode token of each of B sequences "
+                                           "per call (ds4g_layer_decode_batch), weight sets "
+                                           "rotated", "by_B": batch}
+    if "lmhead" in want:
+        rec["lmhead_sample"] = {"workload": "RMSNorm + lm_head 129280x4096 bf16 + T=0.7 top-p 0.95",
+                                "us": round(us_lm, 2),
+                                "hbm_frac": round(lm_bytes / (us_lm * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                                  4)}
+    if "stack" in want:
         del layers, xs, ws
         torch.cuda.empty_cache()
         rec["stack43"] = bench_stack43(args.stack_decode_steps)
-    if not args.no_cpu_baseline:
+    if "cpu" in want:
         rec["cpu_baseline"] = cpu_baseline(s, w_cpu, h_all, args.cpu_tokens)
         rec["cpu_baseline_prefill"] = cpu_baseline_prefill(
             s, w_cpu, args.cpu_prefill_tokens, synth.WORKLOADS["layer_prefill_2048"].seed)
-    rec["measured_peaks"] = measured_peaks(dev)
-    rec["measured_peaks"]["roofline_frac_vs_copy"] = round(
-        rec["roofline"]["achieved"] / rec["measured_peaks"]["hbm_copy_gbs"], 4)
-    rec["clocks"] = gpu_clocks()
+    if "peaks" in want:
+        rec["measured_peaks"] = measured_peaks(dev)
+        if "roofline" in rec:
+            rec["measured_peaks"]["roofline_frac_vs_copy"] = round(
+                rec["roofline"]["achieved"] / rec["measured_peaks"]["hbm_copy_gbs"], 4)
+        rec["clocks"] = gpu_clocks()
     print(json.dumps(rec))
     return 0
 

@@ -23,6 +23,16 @@
 #include "dev.h"
 #include "kernels.h"
 
+#include <type_traits>
+
+// Wave grid of the 256x256 tiles (rows x columns of waves); measured choice.
+#ifndef DS4G_BIG_WM
+#define DS4G_BIG_WM 2
+#endif
+#ifndef DS4G_BIG_WN
+#define DS4G_BIG_WN 4
+#endif
+
 namespace ds4g {
 
 // ------------------------------------------------------------------ epilogue
@@ -435,34 +445,50 @@ gemm_dma_kernel(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int lr = lane & 31, lg = lane >> 5;
-  auto compute = [&](int st) {
-    const u32x4_t* As = &smem[st][0];
-    const u32x4_t* Bs = &smem[st][BM * 8];
+  // Row fragments of this wave that hold a row of the tile.  A partly filled
+  // tile (the last tile of an expert, or of M) neither reads nor multiplies
+  // the fragments past its last row; the rows it holds sum the same products
+  // in the same order.  The main loop is instantiated per count of live
+  // fragments, so every accumulator index stays a constant.
+  const int vrows = __builtin_amdgcn_readfirstlane(ti.row1 - ti.row0);
+  const int live = __builtin_amdgcn_readfirstlane(min(FM, max(0, (vrows - wm * TM + 31) >> 5)));
+  auto run = [&](auto live_c) {
+    constexpr int LIVE = decltype(live_c)::value;
+    auto compute = [&](int st) {
+      const u32x4_t* As = &smem[st][0];
+      const u32x4_t* Bs = &smem[st][BM * 8];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4_t af[FM], bfr[FN];
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4_t af[LIVE > 0 ? LIVE : 1], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = As[swz1(wm * TM + i * 32 + lr, ks * 2 + lg)];
+        for (int i = 0; i < LIVE; ++i) af[i] = As[swz1(wm * TM + i * 32 + lr, ks * 2 + lg)];
+        if (LIVE > 0) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = Bs[swz1(wn * TN + j * 32 + lr, ks * 2 + lg)];
+          for (int j = 0; j < FN; ++j) bfr[j] = Bs[swz1(wn * TN + j * 32 + lr, ks * 2 + lg)];
+        }
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < LIVE; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<F16>(af[i], bfr[j], acc[i][j]);
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<F16>(af[i], bfr[j], acc[i][j]);
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t)
+      if (t < nk) issue(t, t);
+    for (int kt = 0; kt < nk; ++kt) {
+      // tile kt has landed once at most min(S-2, nk-1-kt) later tiles are pending
+      if (kt + S - 2 < nk) wait_vm<(S - 2) * NDMA>();
+      else wait_vm<0>();
+      barrier_lds();   // every wave: tile kt visible, and done reading the stage refilled next
+      if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+      compute(kt % S);
     }
   };
-
-#pragma unroll
-  for (int t = 0; t < S - 1; ++t)
-    if (t < nk) issue(t, t);
-  for (int kt = 0; kt < nk; ++kt) {
-    // tile kt has landed once at most min(S-2, nk-1-kt) later tiles are pending
-    if (kt + S - 2 < nk) wait_vm<(S - 2) * NDMA>();
-    else wait_vm<0>();
-    barrier_lds();   // every wave: tile kt visible, and done reading the stage refilled next
-    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
-    compute(kt % S);
-  }
+  if (live == FM) run(std::integral_constant<int, FM>{});
+  else if (FM >= 4 && live == 3) run(std::integral_constant<int, (FM >= 4 ? 3 : 0)>{});
+  else if (FM >= 3 && live == 2) run(std::integral_constant<int, (FM >= 3 ? 2 : 0)>{});
+  else if (FM >= 2 && live == 1) run(std::integral_constant<int, (FM >= 2 ? 1 : 0)>{});
+  else run(std::integral_constant<int, 0>{});
 
   GemmArgs ge = g;
   if (nsplit > 1) ge.C = static_cast<float*>(g.C) + (long)blockIdx.z * g.part_stride;
@@ -621,7 +647,7 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, Exec st) {
       // spread over the CUs and two blocks fit a CU's LDS
       if (g.rows_hint == 64) return launch_dma_cfg<64, 128, 2, 2, 3>(g, st);
       if (g.rows_hint == 128) return launch_dma_cfg<128, 256, 2, 4, 3>(g, st);
-      if (g.rows_hint == 256) return launch_dma_cfg<256, 256, 2, 4, 2>(g, st);
+      if (g.rows_hint == 256) return launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, 2>(g, st);
       return -1;
     }
     const long nout = dual ? g.N * 2L : g.N;           // B rows per output row
@@ -643,13 +669,13 @@ int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, Exec st) {
         const size_t es =
             (g.epi == EPI_BF16 || g.epi == EPI_F16 || g.epi == EPI_SWIGLU_BF16) ? 2 : 4;
         lo.C = static_cast<char*>(g.C) + (size_t)mb * g.ldc * es;
-        const int r = launch_dma_cfg<256, 256, 2, 4, 2>(hi, st);
+        const int r = launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, 2>(hi, st);
         if (r) return r;
         const long lblocks = ((lo.M + 127) / 128) * ((nout + 127) / 128);
         if (lblocks <= 256) return launch_dma_cfg<128, 128, 2, 2, 3>(lo, st);
         return launch_dma_cfg<128, 128, 2, 2, 2>(lo, st);
       }
-      return launch_dma_cfg<256, 256, 2, 4, 2>(g, st);
+      return launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, 2>(g, st);
     }
     if (g.M <= 64) return launch_dma_cfg<64, 256, 1, 4, 3>(g, st);
     const long blocks = ((g.M + 127) / 128) * ((nout + 127) / 128) * nsplit;
