@@ -345,7 +345,11 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   }
   // tile height of the grouped expert GEMMs: follow the mean rows per expert
   const int mean_rows = (T * k + E - 1) / E;
-  const int tile_m = (!bf || mean_rows <= 64) ? 64 : mean_rows < 160 ? 128 : 256;
+#ifndef DS4G_TILE_M_MAX   // cap on the expert tile height (128: measured 3% slower at 16994)
+#define DS4G_TILE_M_MAX 256
+#endif
+  const int tile_m = std::min((!bf || mean_rows <= 64) ? 64 : mean_rows < 160 ? 128 : 256,
+                              DS4G_TILE_M_MAX);
   RouteArgs ra{};
   ra.logits = at<float>(ws, L.lpart); ra.nsplit = rsplit;
   ra.logits_sum = at<float>(ws, L.logits); ra.T = T; ra.E = E; ra.k = k;

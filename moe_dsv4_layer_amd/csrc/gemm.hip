@@ -32,6 +32,12 @@
 #ifndef DS4G_BIG_WN
 #define DS4G_BIG_WN 4
 #endif
+// Dense GEMMs with at least this many 128x128 tiles run in the XCD-contiguous
+// tile order of the grouped GEMMs (0: never; measured no faster at 2048 or
+// 16994 rows).
+#ifndef DS4G_DENSE_REMAP_TILES
+#define DS4G_DENSE_REMAP_TILES 0
+#endif
 
 namespace ds4g {
 
@@ -632,8 +638,13 @@ int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long
   return 0;
 }
 
-int launch_gemm(const GemmArgs& g, bool mfma, int wdtype_bf16, Exec st) {
-  const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
+int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
+  const bool dual = (g0.epi == EPI_SWIGLU_BF16 || g0.epi == EPI_SWIGLU_F32);
+  GemmArgs g = g0;
+  if (mfma && !g.tiles && DS4G_DENSE_REMAP_TILES > 0) {
+    const long nt = ((g.M + 127) / 128) * (((dual ? 2L * g.N : g.N) + 127) / 128);
+    if (nt >= DS4G_DENSE_REMAP_TILES) g.xcd_remap = 1;
+  }
   if (mfma) {
     const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
     if (g.K % (64 * nsplit)) return -1;
