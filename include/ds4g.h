@@ -116,6 +116,11 @@ typedef struct {
   const void *sh_gate;    /* [Is, d]                                         */
   const void *sh_up;      /* [Is, d]                                         */
   const void *sh_down;    /* [d, Is]                                         */
+  /* Optional (bf16 weights): the layer's fp16 attention-path images made once
+   * by ds4g_make_f16_images, device memory, 256-byte aligned.  NULL: every
+   * prefill and batched decode makes them in its workspace (a read and a
+   * write of QKV-A, QKV-B and W_o per call). */
+  const void *f16_images;
 } ds4g_layer_weights;
 
 /* One layer's KV ring (device memory). */
@@ -136,6 +141,21 @@ typedef struct {
   float *router_in;        /* [T, d]  y = RMSNorm(h2)*g2 as the router saw it */
   float *router_logits;    /* [T, E]  s                                       */
 } ds4g_routing;
+
+/* Bytes of the fp16 image buffer of ds4g_make_f16_images for this layer
+ * shape: fp16 copies of QKV-A, QKV-B and W_o, each row scaled by a power of
+ * two, and the rows' inverse factors.  0 for fp32 weights (they have none)
+ * or invalid dimensions. */
+size_t ds4g_f16_images_bytes(const ds4g_layer_cfg *cfg);
+
+/* Make the fp16 images of a layer's attention-path weights once, so that its
+ * prefills and batched decodes read them (set w->f16_images) instead of
+ * making them per call.  images: device, >= ds4g_f16_images_bytes(cfg)
+ * bytes, 256-byte aligned; owned by the caller and valid while the weights
+ * are unchanged.  Asynchronous on `stream`.  Returns DS4G_OK or a negative
+ * ds4g_status (DS4G_ERR_UNSUPPORTED for fp32 weights). */
+int ds4g_make_f16_images(const ds4g_layer_cfg *cfg, const ds4g_layer_weights *w, void *images,
+                         size_t images_bytes, void *stream);
 
 /* Optional copies of a prefill's intermediate activations, in the order the
  * layer computes them (阶段四 4.2), for step-by-step parity checks: each

@@ -19,7 +19,8 @@ F32, BF16 = 0, 1
 MODE_PREFILL, MODE_DECODE, MODE_DECODE_BATCH = 0, 1, 2
 
 # ds4g.h declares these functions; the ABI test checks the header agrees.
-EXPORTS = ("ds4g_workspace_bytes", "ds4g_layer_supported", "ds4g_layer_prefill",
+EXPORTS = ("ds4g_workspace_bytes", "ds4g_f16_images_bytes", "ds4g_make_f16_images",
+           "ds4g_layer_supported", "ds4g_layer_prefill",
            "ds4g_layer_prefill_trace",
            "ds4g_layer_decode", "ds4g_layer_decode_noalloc", "ds4g_layer_decode_batch",
            "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_probe_mfma",
@@ -41,7 +42,7 @@ WEIGHT_NAMES = ("attn_norm", "qkv_a", "qkv_b", "wo", "ffn_norm", "router", "gate
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES] + [("f16_images", ctypes.c_void_p)]
 
 
 class SampleParams(ctypes.Structure):
@@ -98,6 +99,11 @@ def _load() -> ctypes.CDLL:
     P = ctypes.c_void_p
     lib.ds4g_workspace_bytes.restype = ctypes.c_size_t
     lib.ds4g_workspace_bytes.argtypes = [ctypes.POINTER(LayerCfg), ctypes.c_int32, ctypes.c_int32]
+    lib.ds4g_f16_images_bytes.restype = ctypes.c_size_t
+    lib.ds4g_f16_images_bytes.argtypes = [ctypes.POINTER(LayerCfg)]
+    lib.ds4g_make_f16_images.restype = ctypes.c_int
+    lib.ds4g_make_f16_images.argtypes = [ctypes.POINTER(LayerCfg), ctypes.POINTER(LayerWeights), P,
+                                         ctypes.c_size_t, P]
     lib.ds4g_layer_supported.restype = ctypes.c_int
     lib.ds4g_layer_supported.argtypes = [ctypes.POINTER(LayerCfg), ctypes.c_int32, ctypes.c_int32]
     lib.ds4g_layer_prefill.restype = ctypes.c_int
@@ -174,12 +180,31 @@ def make_cfg(shape) -> LayerCfg:
                     float(shape.rms_eps), BF16 if wd in ("bf16", BF16) else F32)
 
 
-def make_weights(w: Dict[str, "torch.Tensor"]) -> LayerWeights:
+def make_weights(w: Dict[str, "torch.Tensor"], f16_images=None) -> LayerWeights:
+    """ds4g_layer_weights of a dict of contiguous weight tensors; f16_images:
+    an optional buffer filled by make_f16_images (kept alive by the caller)."""
     for n in WEIGHT_NAMES:
         t = w[n]
         if not t.is_contiguous():
             raise ValueError(f"weight {n} must be contiguous")
-    return LayerWeights(*[w[n].data_ptr() for n in WEIGHT_NAMES])
+    return LayerWeights(*[w[n].data_ptr() for n in WEIGHT_NAMES], _ptr(f16_images))
+
+
+def f16_images_bytes(cfg: LayerCfg) -> int:
+    return int(lib.ds4g_f16_images_bytes(ctypes.byref(cfg)))
+
+
+def make_f16_images(cfg: LayerCfg, w: LayerWeights, device="cuda", stream=None):
+    """A device buffer holding the layer's fp16 attention-path images
+    (ds4g_make_f16_images); set it as f16_images of the layer's weights."""
+    import torch
+    n = f16_images_bytes(cfg)
+    if n == 0:
+        raise Ds4gError("this layer has no fp16 images (fp32 weights)")
+    buf = torch.empty(n, dtype=torch.uint8, device=device)
+    _check(lib.ds4g_make_f16_images(ctypes.byref(cfg), ctypes.byref(w), buf.data_ptr(), n,
+                                    _stream(stream)), "ds4g_make_f16_images")
+    return buf
 
 
 def make_ring(k, v, pos) -> KvRing:

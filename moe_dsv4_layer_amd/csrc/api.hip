@@ -47,6 +47,25 @@ inline int router_split(int hidden, bool mfma) {
   return s;
 }
 
+// The fp16 image buffer: QKV-A, QKV-B and W_o in fp16, then each one's row
+// factors; the same carve inside a workspace and in a caller's image buffer.
+struct ImageLayout {
+  size_t img[3], inv[3], total;
+};
+ImageLayout image_layout(const ds4g_layer_cfg& c, size_t base) {
+  const size_t d = c.hidden, r = c.qkv_rank, qd = (size_t)c.n_heads * c.head_dim,
+               qkvd = qd + 2 * (size_t)c.head_dim;
+  const size_t n[3] = {r, qkvd, d}, k[3] = {d, r, qd};
+  ImageLayout L;
+  size_t o = base;
+  for (int m = 0; m < 3; ++m) {
+    L.img[m] = o; o = a256(o + n[m] * k[m] * 2);
+    L.inv[m] = o; o = a256(o + n[m] * 4);
+  }
+  L.total = o - base;
+  return L;
+}
+
 struct Layout {
   size_t xn, c, qkv, q, kc, vc, o, yf, ys, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
       count, offset, tiles, ntiles, z, zs, part, psh, skp, rope, img[3], inv[3], total;
@@ -100,13 +119,12 @@ Layout layout(const ds4g_layer_cfg& c, int T, bool images) {
     L.skp = take(T <= 256 ? m : 0);
   }
   L.rope = take((size_t)dh * (((size_t)T + 3) & ~(size_t)3) * 4);   // cos, sin [rd/2][T pad 4]
-  {
-    const bool on = images && c.wdtype == DS4G_BF16;
-    const size_t n[3] = {r, qkvd, d}, k[3] = {d, r, qd};
-    for (int m = 0; m < 3; ++m) {
-      L.img[m] = take(on ? n[m] * k[m] * 2 : 0);
-      L.inv[m] = take(on ? n[m] * 4 : 0);
-    }
+  if (images && c.wdtype == DS4G_BF16) {
+    const ImageLayout IL = image_layout(c, o);
+    for (int m = 0; m < 3; ++m) { L.img[m] = IL.img[m]; L.inv[m] = IL.inv[m]; }
+    o += IL.total;
+  } else {
+    for (int m = 0; m < 3; ++m) L.img[m] = L.inv[m] = o;
   }
   L.total = o;
   return L;
@@ -212,13 +230,21 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   // made right before the first GEMM that reads it
   const void* const wsrc[3] = {w.qkv_a, w.qkv_b, w.wo};
   const int wN[3] = {r, qkvd, d}, wK[3] = {d, r, qd};
+  // (or read from the caller's prepared images, w.f16_images)
   bool made[3] = {false, false, false};
+  void* ibase = w.f16_images ? const_cast<void*>(w.f16_images) : ws;
+  size_t img_off[3], inv_off[3];
+  if (w.f16_images) {
+    const ImageLayout IL = image_layout(c, 0);
+    for (int m = 0; m < 3; ++m) { img_off[m] = IL.img[m]; inv_off[m] = IL.inv[m]; }
+  } else {
+    for (int m = 0; m < 3; ++m) { img_off[m] = L.img[m]; inv_off[m] = L.inv[m]; }
+  }
   auto image = [&](int m) {
-    if (!made[m]) {
+    if (!made[m] && !w.f16_images)
       rc |= launch_f16_image(static_cast<const uint16_t*>(wsrc[m]), wN[m], wK[m],
                              at<uint16_t>(ws, L.img[m]), at<float>(ws, L.inv[m]), st);
-      made[m] = true;
-    }
+    made[m] = true;
   };
 
   // dense GEMM; batched decode splits K (fp32 partials, then a reduce that
@@ -237,8 +263,8 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     const float* cs = nullptr;
     if (bf && img >= 0) {
       image(img);
-      B = at<void>(ws, L.img[img]);
-      cs = at<float>(ws, L.inv[img]);
+      B = at<void>(ibase, img_off[img]);
+      cs = at<float>(ibase, inv_off[img]);
     }
     const int s = batch ? batch_split(M, N, K, bf) : 1;
     if (s > 1) {
@@ -274,8 +300,8 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
                             st);
     image(1);
     GemmArgs g{};
-    g.A = at<void>(ws, L.c); g.lda = r; g.B = at<void>(ws, L.img[1]); g.M = T; g.N = qkvd; g.K = r;
-    g.f16 = 1; g.colscale = at<float>(ws, L.inv[1]);
+    g.A = at<void>(ws, L.c); g.lda = r; g.B = at<void>(ibase, img_off[1]); g.M = T; g.N = qkvd;
+    g.K = r; g.f16 = 1; g.colscale = at<float>(ibase, inv_off[1]);
     g.epi = EPI_ROPE_QKV; g.C = at<void>(ws, L.q); g.ldc = qd;
     g.rope_c = rc_tab; g.rope_s = rc_tab + (size_t)(rd / 2) * tpad; g.rope_ld = tpad;
     g.rope_dh = dh; g.rope_rd = rd;
@@ -487,8 +513,11 @@ int check_call(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, const ds4
   if ((s = check_ring(ring)) != DS4G_OK) return s;
   if (!x || !ws || T <= 0) return DS4G_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return DS4G_ERR_INVALID_ARG;
+  if (w->f16_images && (reinterpret_cast<uintptr_t>(w->f16_images) & 255) != 0)
+    return DS4G_ERR_INVALID_ARG;
   if ((s = check_rows(*cfg, T, mode)) != DS4G_OK) return s;
-  if (ws_bytes < layout(*cfg, T, mode != DS4G_MODE_DECODE).total) return DS4G_ERR_WORKSPACE;
+  const bool images = mode != DS4G_MODE_DECODE && !w->f16_images;
+  if (ws_bytes < layout(*cfg, T, images).total) return DS4G_ERR_WORKSPACE;
   return DS4G_OK;
 }
 
@@ -612,6 +641,33 @@ int ds4g_layer_decode_noalloc(const ds4g_layer_cfg* cfg, const ds4g_layer_weight
                               Exec{(hipStream_t)stream, false}, DS4G_MODE_DECODE));
 }
 
+size_t ds4g_f16_images_bytes(const ds4g_layer_cfg* cfg) {
+  if (check_cfg(cfg) != DS4G_OK || cfg->wdtype != DS4G_BF16) return 0;
+  return image_layout(*cfg, 0).total;
+}
+
+int ds4g_make_f16_images(const ds4g_layer_cfg* cfg, const ds4g_layer_weights* w, void* images,
+                         size_t images_bytes, void* stream) {
+  int s = check_cfg(cfg);
+  if (s != DS4G_OK) return s;
+  if ((s = check_weights(w)) != DS4G_OK) return s;
+  if (cfg->wdtype != DS4G_BF16) return DS4G_ERR_UNSUPPORTED;
+  if (!images || (reinterpret_cast<uintptr_t>(images) & 255) != 0) return DS4G_ERR_INVALID_ARG;
+  const ImageLayout IL = image_layout(*cfg, 0);
+  if (images_bytes < IL.total) return DS4G_ERR_WORKSPACE;
+  const int d = cfg->hidden, r = cfg->qkv_rank, qd = cfg->n_heads * cfg->head_dim,
+            qkvd = qd + 2 * cfg->head_dim;
+  const void* const src[3] = {w->qkv_a, w->qkv_b, w->wo};
+  const int N[3] = {r, qkvd, d}, K[3] = {d, r, qd};
+  return dry_then_run((hipStream_t)stream, [&](Exec ex) {
+    int rc = 0;
+    for (int m = 0; m < 3; ++m)
+      rc |= launch_f16_image(static_cast<const uint16_t*>(src[m]), N[m], K[m],
+                             at<uint16_t>(images, IL.img[m]), at<float>(images, IL.inv[m]), ex);
+    return rc;
+  });
+}
+
 int ds4g_layer_supported(const ds4g_layer_cfg* cfg, int32_t T, int32_t mode) {
   int s = check_cfg(cfg);
   if (s != DS4G_OK) return s;
@@ -621,7 +677,7 @@ int ds4g_layer_supported(const ds4g_layer_cfg* cfg, int32_t T, int32_t mode) {
   if ((s = check_rows(*cfg, T, mode)) != DS4G_OK) return s;
   // the launch sequence, dry, over placeholder addresses (never dereferenced)
   void* const p = reinterpret_cast<void*>(uintptr_t(1) << 40);
-  ds4g_layer_weights w{p, p, p, p, p, p, p, p, p, p, p, p};
+  ds4g_layer_weights w{p, p, p, p, p, p, p, p, p, p, p, p, nullptr};
   ds4g_kv_ring ring{p, p, static_cast<int64_t*>(p)};
   return layer_seq(*cfg, w, ring, static_cast<float*>(p), T, nullptr, p, Exec{nullptr, true}, mode)
              ? DS4G_ERR_UNSUPPORTED

@@ -15,17 +15,26 @@ from typing import Dict, List, Optional, Sequence
 import torch
 
 from . import (BF16, F32, alloc_workspace, embed, layer_decode, layer_prefill, lmhead_sample,
-               make_cfg, make_ring, make_routing, make_weights, workspace_bytes)
+               make_cfg, make_f16_images, make_ring, make_routing, make_weights,
+               workspace_bytes)
 
 
 class Stack:
     def __init__(self, shape, layers: Sequence[Dict[str, torch.Tensor]],
-                 head: Dict[str, torch.Tensor], max_tokens: int, device="cuda"):
+                 head: Dict[str, torch.Tensor], max_tokens: int, device="cuda",
+                 prepare_images: bool = True):
+        """prepare_images (bf16 weights): make every layer's fp16
+        attention-path images once (ds4g_make_f16_images), as an engine does
+        when it loads weights, instead of in every prefill."""
         self.shape = shape
         self.cfg = make_cfg(shape)
         self.wdtype = BF16 if self.cfg.wdtype == BF16 else F32
         self.layers = list(layers)
-        self.cw = [make_weights(w) for w in self.layers]
+        self.images = [None] * len(self.layers)
+        if prepare_images and self.wdtype == BF16:
+            self.images = [make_f16_images(self.cfg, make_weights(w), device)
+                           for w in self.layers]
+        self.cw = [make_weights(w, img) for w, img in zip(self.layers, self.images)]
         self.head = head
         self.vocab = head["lm_head"].shape[0]
         self.device = device
