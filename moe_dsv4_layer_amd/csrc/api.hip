@@ -68,7 +68,7 @@ ImageLayout image_layout(const ds4g_layer_cfg& c, size_t base) {
 
 struct Layout {
   size_t xn, c, qkv, q, kc, vc, o, yf, ys, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
-      count, offset, tiles, ntiles, z, zs, part, psh, skp, rope, img[3], inv[3], total;
+      count, offset, tiles, ntiles, z, zs, part, skp, rope, img[3], inv[3], total;
 };
 
 // Byte offsets of every workspace buffer for T tokens.  fp32-sized slots are
@@ -108,7 +108,6 @@ Layout layout(const ds4g_layer_cfg& c, int T, bool images) {
   L.z = take(((size_t)T * k * I + I + Is) * 4);
   L.zs = take((size_t)T * Is * 4);
   L.part = take((size_t)T * k * d * 4);
-  L.psh = take(d * 4);
   {   // split-K partial sums of the batched decode's dense GEMMs
     const bool mfma = c.wdtype == DS4G_BF16;
     size_t m = 0;
@@ -475,7 +474,7 @@ int decode_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_ri
   m.logits_out = logits; m.logits = logits; m.E = E;
   m.k = c.top_k; m.d = d; m.I = c.ffn_inter; m.Is = c.shared_inter; m.gate = w.gate;
   m.up = w.up; m.down = w.down; m.sh_gate = w.sh_gate; m.sh_up = w.sh_up;
-  m.sh_down = w.sh_down; m.z = at<float>(ws, L.z); m.part_sh = at<float>(ws, L.psh);
+  m.sh_down = w.sh_down; m.z = at<float>(ws, L.z);
   m.sel = at<int>(ws, L.tidx); m.wsel = at<float>(ws, L.tw);
   if (routing) {
     m.topk_idx = routing->topk_idx; m.topk_w = routing->topk_w;

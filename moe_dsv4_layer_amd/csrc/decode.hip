@@ -11,6 +11,8 @@
 #include "dev.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 // Launch shapes (rows in flight per block, grid caps); measured choices.
 #ifndef DS4G_GEMV_GRID_MAX
 #define DS4G_GEMV_GRID_MAX 2048
@@ -25,16 +27,13 @@
 #define DS4G_GATEUP_GRID_MAX 896
 #endif
 #ifndef DS4G_DOWN_RB
-#define DS4G_DOWN_RB 8
+#define DS4G_DOWN_RB 16
 #endif
 #ifndef DS4G_ROUTER_SHARED_RB
 #define DS4G_ROUTER_SHARED_RB 2
 #endif
-#ifndef DS4G_SHDOWN_GRID_MAX
-#define DS4G_SHDOWN_GRID_MAX 128
-#endif
-#ifndef DS4G_SHDOWN_RB
-#define DS4G_SHDOWN_RB 8
+#ifndef DS4G_SHGU_GRID_MAX   // blocks of the gate/up launch that compute the shared gate/up
+#define DS4G_SHGU_GRID_MAX 256
 #endif
 
 namespace ds4g {
@@ -340,16 +339,16 @@ int launch_gemv_rows(const GemvRowsArgs& a, Exec st) {
 
 // ---------------------------------------------------------------------------
 // MoE decode for one token, three kernels:
-//   router_shared_decode  logits = W_r y and the shared expert's
-//                         z_sh = silu(G_sh y) * (U_sh y), y = RMSNorm(h2) * g2
-//   moe_gateup_decode     every wave picks the top-k from the logits; routed
-//                         z_s = silu(G_s y) * (U_s y); its first blocks do the
-//                         shared expert's down rows part_sh = D_sh z_sh, whose
-//                         loads need no routing and fill HBM while the routed
-//                         blocks route
-//   moe_down_decode       x = h2 + sum_s w_s D_s z_s + part_sh
-// The shared expert needs only y, so it runs beside the router (itself a
-// small read); the routed kernels carry only the routed weights.
+//   router_shared_decode  logits = W_r y, y = RMSNorm(h2) * g2
+//   moe_gateup_decode     its first blocks compute the shared expert's
+//                         z_sh = silu(G_sh y) * (U_sh y), whose loads need no
+//                         routing and fill HBM while the other blocks route;
+//                         those pick the top-k from the logits (every wave for
+//                         itself) and compute z_s = silu(G_s y) * (U_s y)
+//   moe_down_decode       x = h2 + sum_s w_s D_s z_s + D_sh z_sh, one wave per
+//                         routed slot and one for the shared expert
+// The router launch reads only W_r, so the routing the gate/up blocks wait
+// for is ready early.
 
 // y = RMSNorm(h2) * g2 over the K slice of wave w (chunks [w*CPL*64,
 // (w+1)*CPL*64)); h2 is read by every block (L2-resident).
@@ -393,14 +392,16 @@ struct NormSlice {
 // ceil(E/RB) are RB router rows each (one weight row -> one logit), the rest
 // RB shared (gate, up) row pairs each.  Blocks (4 waves splitting K = hidden)
 // stride over groups; the next group's loads go out before the reductions.
+// Groups [g0, g1) of that list, taken by block blk of nblk; every thread of
+// the block calls it.
 template <typename WT, int CPL, int RB>
-__global__ void __launch_bounds__(256)
-router_shared_decode(MoeDecodeArgs a) {
+__device__ __forceinline__ void router_shared_groups(const MoeDecodeArgs& a, int g0, int g1,
+                                                     int blk, int nblk) {
   __shared__ float ssq[4];
   __shared__ float red[4][RB][2];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nchunk = a.d >> 3;
-  const int ngr = (a.E + RB - 1) / RB, ng = ngr + (a.Is + RB - 1) / RB;
+  const int ngr = (a.E + RB - 1) / RB, ng = g1;
   Chunk8<WT> cg[RB][CPL], cu[RB][CPL];
   auto load_group = [&](int g) {
 #pragma unroll
@@ -426,12 +427,12 @@ router_shared_decode(MoeDecodeArgs a) {
       }
     }
   };
-  int g = blockIdx.x;
+  int g = g0 + blk;
   if (g < ng) load_group(g);
   NormSlice<WT, CPL> y;
   y.load(a.h2, nchunk);
   y.normalize(a.ffn_norm, a.eps, a.d, ssq);
-  if (blockIdx.x == 0 && a.router_in) {
+  if (g0 == 0 && blk == 0 && a.router_in) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = (wid * CPL + i) * 64 + lane;
@@ -440,7 +441,7 @@ router_shared_decode(MoeDecodeArgs a) {
         for (int e = 0; e < 8; ++e) a.router_in[c * 8 + e] = y.v[i][e];
     }
   }
-  for (; g < ng; g += gridDim.x) {
+  for (; g < ng; g += nblk) {
     const bool router = g < ngr;
     float ag[RB], au[RB];
 #pragma unroll
@@ -465,7 +466,7 @@ router_shared_decode(MoeDecodeArgs a) {
         }
       }
     }
-    if (g + (int)gridDim.x < ng) load_group(g + gridDim.x);
+    if (g + nblk < ng) load_group(g + nblk);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       ag[r] = wave_sum(ag[r]);
@@ -492,62 +493,31 @@ router_shared_decode(MoeDecodeArgs a) {
   }
 }
 
-// Shared expert's down rows: part_sh[n] = D_sh[n, :] . z_sh, RBS whole rows
-// (K = Is <= 512 * CPL2) per wave, every wave of blocks [0, nblk).
-template <typename WT, int CPL2, int RBS>
-__device__ void shared_down_rows(const MoeDecodeArgs& a, int blk, int nblk) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int Ks = a.Is;
-  const WT* D = static_cast<const WT*>(a.sh_down);
-  const float* zz = a.z + a.k * a.I;
-  for (int n0 = (blk * 4 + wid) * RBS; n0 < a.d; n0 += nblk * 4 * RBS) {
-    Chunk8<WT> ch[RBS][CPL2];
-#pragma unroll
-    for (int r = 0; r < RBS; ++r)
-#pragma unroll
-      for (int i = 0; i < CPL2; ++i) {
-        const int c = i * 64 + lane;
-        if (n0 + r < a.d && c * 8 < Ks) ch[r][i].load(D + (long)(n0 + r) * Ks + c * 8);
-      }
-    float zv[CPL2][8];
-#pragma unroll
-    for (int i = 0; i < CPL2; ++i) {
-      const int c = i * 64 + lane;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) zv[i][e] = (c * 8 < Ks) ? zz[c * 8 + e] : 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < RBS; ++r) {
-      float p = 0.f;
-#pragma unroll
-      for (int i = 0; i < CPL2; ++i) {
-        const int c = i * 64 + lane;
-        if (n0 + r < a.d && c * 8 < Ks) {
-          float f[8];
-          ch[r][i].widen(f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p += f[e] * zv[i][e];
-        }
-      }
-      p = wave_sum(p);
-      if (lane == 0 && n0 + r < a.d) a.part_sh[n0 + r] = p;
-    }
-  }
+// The router logits alone (the shared expert's gate/up runs in the first
+// blocks of the routed gate/up launch, which need no routing).
+template <typename WT, int CPL, int RB>
+__global__ void __launch_bounds__(256)
+router_shared_decode(MoeDecodeArgs a) {
+  router_shared_groups<WT, CPL, RB>(a, 0, (a.E + RB - 1) / RB, blockIdx.x, gridDim.x);
 }
 
-// Routed gate/up: blocks [0, a.nsd) are shared-down blocks; the rest stride
+// Routed gate/up: blocks [0, a.nsd) compute the shared expert's gate/up rows
+// (they need only y, so their loads fill HBM while the routed blocks route);
+// the rest stride
 // over RB routed (gate, up) row pairs.  Every wave routes for itself from the
 // logits in its registers (no block barrier before its routed loads); the
 // first routed block publishes the routing for the down kernel and the caller.
-template <typename WT, int CPL, int RB, int CPL2>
+template <typename WT, int CPL, int RB>
 __global__ void __launch_bounds__(256)
 moe_gateup_decode(MoeDecodeArgs a) {
   __shared__ float ssq[4];
   __shared__ float red[4][RB][2];
   __shared__ int wsel_idx[4][8];
   __shared__ float wsel_w[4][8];
-  if ((int)blockIdx.x < a.nsd) {
-    shared_down_rows<WT, CPL2, DS4G_SHDOWN_RB>(a, blockIdx.x, a.nsd);
+  if ((int)blockIdx.x < a.nsd) {   // the shared expert's gate/up rows
+    constexpr int RBR = DS4G_ROUTER_SHARED_RB;
+    const int ngr = (a.E + RBR - 1) / RBR;
+    router_shared_groups<WT, CPL, RBR>(a, ngr, ngr + (a.Is + RBR - 1) / RBR, blockIdx.x, a.nsd);
     return;
   }
   const int bid = blockIdx.x - a.nsd, nblk = gridDim.x - a.nsd;
@@ -650,26 +620,29 @@ moe_gateup_decode(MoeDecodeArgs a) {
 }
 
 // MoE down + combine + residual for one token:
-//   x[n] = h2[n] + sum_s w_s (D_{e_s} z_s)[n] + part_sh[n]
-// A block is 8 waves and owns RB output rows; wave w handles routed slot w
-// (k <= 8), so the weight rows of every slot are in flight together.  The sum
-// runs in slot order, then the shared expert, then the residual.  Block 0
-// advances the ring position (the attention kernel has read it already).
+//   x[n] = h2[n] + sum_s w_s (D_{e_s} z_s)[n] + (D_sh z_sh)[n]
+// A block is k + 1 waves and owns RB output rows; wave s < k handles routed
+// slot s and wave k the shared expert, so the weight rows of every slot are
+// in flight together.  The sum runs in slot order, then the shared expert,
+// then the residual.  Block 0 advances the ring position (the attention
+// kernel has read it already).
 template <typename WT, int CPL, int RB>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(576)
 moe_down_decode(MoeDecodeArgs a, float* x, int64_t* pos_inc) {
   __shared__ int sel[8];
   __shared__ float wsel[8];
-  __shared__ float part[8][RB];
+  __shared__ float part[9][RB];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (threadIdx.x < a.k) { sel[threadIdx.x] = a.sel[threadIdx.x]; wsel[threadIdx.x] = a.wsel[threadIdx.x]; }
   if (pos_inc && blockIdx.x == 0 && threadIdx.x == 0) *pos_inc += 1;
   __syncthreads();
   const int n0 = blockIdx.x * RB;
-  const int Ks = a.I;
-  if (wid < a.k) {
+  if (wid <= a.k) {
     const int s = wid;
-    const WT* D = static_cast<const WT*>(a.down) + (long)sel[s] * a.d * a.I;
+    const bool shared = s == a.k;
+    const int Ks = shared ? a.Is : a.I;
+    const WT* D = shared ? static_cast<const WT*>(a.sh_down)
+                         : static_cast<const WT*>(a.down) + (long)sel[s] * a.d * a.I;
     Chunk8<WT> ch[RB][CPL];
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -678,7 +651,7 @@ moe_down_decode(MoeDecodeArgs a, float* x, int64_t* pos_inc) {
         const int c = i * 64 + lane;
         if (n0 + r < a.d && c * 8 < Ks) ch[r][i].load(D + (long)(n0 + r) * Ks + c * 8);
       }
-    const float* zz = a.z + s * a.I;
+    const float* zz = a.z + s * a.I;   // the shared slot follows the k routed ones
     float zv[CPL][8];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
@@ -707,7 +680,7 @@ moe_down_decode(MoeDecodeArgs a, float* x, int64_t* pos_inc) {
   if (wid == 0 && lane < RB && n0 + lane < a.d) {
     float v = 0.f;
     for (int s = 0; s < a.k; ++s) v += wsel[s] * part[s][lane];
-    v += a.part_sh[n0 + lane];
+    v += part[a.k][lane];
     x[n0 + lane] = a.h2[n0 + lane] + v;
   }
 }
@@ -717,39 +690,47 @@ int launch_moe_decode(const MoeDecodeArgs& a0, float* x, int64_t* pos_inc, Exec 
   if (a0.k > 8 || a0.E > 512 || a0.d % 8 || a0.I % 8 || a0.Is % 8) return -1;
   const int nchunk = a0.d / 8;
   const int cpl = (nchunk + 255) / 256;      // K = d over 4 waves
-  const int cpls = (a0.Is / 8 + 63) / 64;    // K = Is per wave (shared down)
-  const int cpld = (a0.I / 8 + 63) / 64;     // K = I per wave (routed down)
-  if (cpl > 4 || cpls > 4 || cpld > 4) return -1;
+  // K = I (routed) or Is (shared) per wave of the down kernel
+  const int cpld = (std::max(a0.I, a0.Is) / 8 + 63) / 64;
+  if (cpl > 4 || cpld > 4) return -1;
   MoeDecodeArgs a = a0;
-  // router logits + shared gate/up
+  // router logits
   {
     constexpr int RB = DS4G_ROUTER_SHARED_RB;
-    const int ng = (a.E + RB - 1) / RB + (a.Is + RB - 1) / RB;
+    const int ng = (a.E + RB - 1) / RB;
 #define DS4G_RS(C) DS4G_LAUNCH((router_shared_decode<WT, C, RB>), dim3(ng), dim3(256), 0, st, a)
     if (cpl == 1) DS4G_RS(1); else if (cpl == 2) DS4G_RS(2); else DS4G_RS(4);
 #undef DS4G_RS
   }
-  // shared down rows + routed gate/up
+  // shared gate/up rows + routed gate/up
   {
     constexpr int RB = DS4G_GATEUP_RB;
-    a.nsd = (a.d + 4 * DS4G_SHDOWN_RB - 1) / (4 * DS4G_SHDOWN_RB);   // 4 waves x RB rows
-    if (a.nsd > DS4G_SHDOWN_GRID_MAX) a.nsd = DS4G_SHDOWN_GRID_MAX;
+    a.nsd = (a.Is + DS4G_ROUTER_SHARED_RB - 1) / DS4G_ROUTER_SHARED_RB;   // groups of shared rows
+    if (a.nsd > DS4G_SHGU_GRID_MAX) a.nsd = DS4G_SHGU_GRID_MAX;
     const int ntask = a.k * a.I;
     int grid = (ntask + RB - 1) / RB;
     if (grid > DS4G_GATEUP_GRID_MAX) grid = DS4G_GATEUP_GRID_MAX;
     grid += a.nsd;
-#define DS4G_GU(C, C2) DS4G_LAUNCH((moe_gateup_decode<WT, C, RB, C2>), dim3(grid), dim3(256), 0, st, a)
-#define DS4G_GU2(C) { if (cpls == 1) DS4G_GU(C, 1); else if (cpls == 2) DS4G_GU(C, 2); else DS4G_GU(C, 4); }
-    if (cpl == 1) DS4G_GU2(1) else if (cpl == 2) DS4G_GU2(2) else DS4G_GU2(4)
-#undef DS4G_GU2
+#define DS4G_GU(C) DS4G_LAUNCH((moe_gateup_decode<WT, C, RB>), dim3(grid), dim3(256), 0, st, a)
+    if (cpl == 1) DS4G_GU(1); else if (cpl == 2) DS4G_GU(2); else DS4G_GU(4);
 #undef DS4G_GU
   }
-  // routed down + combine + residual
+  // routed down + shared down + combine + residual: k + 1 waves per block,
+  // DS4G_DOWN_RB rows per block where a wave's rows fit its registers
+  // (bf16, K <= 1024), else 8
   {
-    constexpr int RB2 = DS4G_DOWN_RB;
-    const int grid2 = (a.d + RB2 - 1) / RB2;
-#define DS4G_DN(C) DS4G_LAUNCH((moe_down_decode<WT, C, RB2>), dim3(grid2), dim3(512), 0, st, a, x, pos_inc)
-    if (cpld == 1) DS4G_DN(1); else if (cpld == 2) DS4G_DN(2); else DS4G_DN(4);
+    const int dthreads = 64 * (a.k + 1);
+#define DS4G_DN(C, R) DS4G_LAUNCH((moe_down_decode<WT, C, R>), dim3((a.d + R - 1) / R), dim3(dthreads), 0, st, a, x, pos_inc)
+    bool done = false;
+    if constexpr (sizeof(WT) == 2) {
+      if (cpld == 1) { DS4G_DN(1, DS4G_DOWN_RB); done = true; }
+      else if (cpld == 2) { DS4G_DN(2, DS4G_DOWN_RB); done = true; }
+    }
+    if (!done) {
+      if (cpld == 1) DS4G_DN(1, 8);
+      else if (cpld == 2) DS4G_DN(2, 8);
+      else DS4G_DN(4, 8);
+    }
 #undef DS4G_DN
   }
   return 0;

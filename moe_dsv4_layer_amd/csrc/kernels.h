@@ -155,16 +155,15 @@ struct MoeDecodeArgs {
   const float* logits;    // [E] read by the gate/up kernel (same buffer)
   int E, k, d, I, Is;
   const void *gate, *up, *down, *sh_gate, *sh_up, *sh_down;
-  float* z;               // [k*I + Is]
-  float* part_sh;         // [d] shared expert's down output
-  int nsd;                // shared-down blocks of the gate/up launch (set by the launcher)
+  float* z;               // [k*I + Is]: routed slots, then the shared expert
+  int nsd;                // shared gate/up blocks of the gate/up launch (set by the launcher)
   int* sel;               // [k] workspace
   float* wsel;            // [k] workspace
   // optional routing outputs
   int* topk_idx; float* topk_w; int* count; int* offset; int* perm; float* router_in;
 };
-// router logits + shared expert, routed gate/up (+ shared down), routed down
-// + combine + residual: three launches
+// router logits, shared + routed gate/up, routed + shared down with the
+// combine and residual: three launches
 template <typename WT>
 int launch_moe_decode(const MoeDecodeArgs& a, float* x, int64_t* pos_inc, Exec st);
 
