@@ -18,7 +18,7 @@
 #define DS4G_GEMV_GRID_MAX 2048
 #endif
 #ifndef DS4G_GEMV_RB_K8K
-#define DS4G_GEMV_RB_K8K 2
+#define DS4G_GEMV_RB_K8K 4
 #endif
 #ifndef DS4G_GATEUP_RB
 #define DS4G_GATEUP_RB 4

@@ -32,6 +32,14 @@
 #ifndef DS4G_BIG_WN
 #define DS4G_BIG_WN 4
 #endif
+// LDS stages and k-step width of the 256x256 tiles (2 x 64 or 4 x 32: the
+// same 128 KB of LDS)
+#ifndef DS4G_BIG_S
+#define DS4G_BIG_S 2
+#endif
+#ifndef DS4G_BIG_BK
+#define DS4G_BIG_BK 64
+#endif
 // Dense GEMMs with at least this many 128x128 tiles run in the XCD-contiguous
 // tile order of the grouped GEMMs (0: never; measured no faster at 2048 or
 // 16994 rows).
@@ -338,9 +346,14 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 
-// row swizzle of the 8 16-byte chunks of a 128-byte LDS row: conflict-free
-// for the fragment reads (32 rows x 2 chunks per instruction)
-__device__ __forceinline__ int swz1(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+// LDS slot of chunk c of row r, rows of CPR 16-byte chunks: the chunk index
+// is XORed with bits of the row so that the 16 rows one fragment read takes
+// at a time land on distinct banks (128-byte rows: bits 1..3; 64-byte rows:
+// bits 2..3)
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * CPR + (c ^ (CPR == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3)));
+}
 
 // Workgroups go to the 8 XCDs round-robin (linear id % 8), each XCD with its
 // own L2.  Renumbering the nb tiles that have work so that XCD k runs a
@@ -359,19 +372,23 @@ __device__ __forceinline__ bool xcd_tile(int nb, int& bx, int& by) {
   return true;
 }
 
-template <int BM, int BN, int WM, int WN, int S, int EPI, bool F16>
+template <int BM, int BN, int WM, int WN, int S, int EPI, bool F16, int BK>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_dma_kernel(GemmArgs g) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32);
-  constexpr int NW = WM * WN, BK = 64;
+  constexpr int NW = WM * WN;
+  constexpr int CPR = BK / 8;                // 16-byte chunks per LDS row
+  constexpr int RPL = 64 / CPR;              // LDS rows per 1 KB wave load
+  constexpr int KS = BK / 16;                // MFMA k steps per stage
+  static_assert(BK == 64 || BK == 32, "64- or 32-wide k steps");
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int ROWS = BM + BN;              // LDS rows per stage (A rows, then B rows)
-  constexpr int NDMA = ROWS / (8 * NW);      // 1 KB loads per wave per stage
+  constexpr int NDMA = ROWS / (RPL * NW);    // 1 KB loads per wave per stage
   static_assert(FM >= 1 && FN >= 1 && TM * WM == BM && TN * WN == BN, "32x32 fragments");
-  static_assert(NDMA * 8 * NW == ROWS && BM % 8 == 0, "whole 8-row loads per wave");
+  static_assert(NDMA * RPL * NW == ROWS && BM % RPL == 0, "whole loads per wave");
   static_assert(!DUAL || FN % 2 == 0, "SwiGLU pairs gate/up fragments");
   static_assert(S >= 2 && (S - 2) * NDMA <= 63, "vmcnt range");
-  __shared__ u32x4_t smem[S][ROWS * 8];
+  __shared__ u32x4_t smem[S][ROWS * CPR];
   TileInfo ti;
   int bx = blockIdx.x, by = blockIdx.y;
   if (g.xcd_remap && gridDim.z == 1 &&
@@ -393,7 +410,7 @@ gemm_dma_kernel(GemmArgs g) {
   int arow[NDMA];
 #pragma unroll
   for (int j = 0; j < NDMA; ++j)
-    arow[j] = min(ti.row0 + (wid * NDMA + j) * 8 + (lane >> 3), ti.row1 - 1);
+    arow[j] = min(ti.row0 + (wid * NDMA + j) * RPL + lane / CPR, ti.row1 - 1);
   if (g.gather) {   // all gather loads issued together
     int src[NDMA];
 #pragma unroll
@@ -403,10 +420,10 @@ gemm_dma_kernel(GemmArgs g) {
   }
 #pragma unroll
   for (int j = 0; j < NDMA; ++j) {
-    const int I = wid * NDMA + j;            // stage rows 8I .. 8I+7
-    const int row = I * 8 + (lane >> 3), slot = lane & 7;
-    const int c = slot ^ ((row >> 1) & 7);   // logical chunk stored in this slot
-    if (I * 8 < BM) {
+    const int I = wid * NDMA + j;            // stage rows RPL*I .. RPL*I + RPL-1
+    const int row = I * RPL + lane / CPR, slot = lane % CPR;
+    const int c = swz<CPR>(row, slot) - row * CPR;   // logical chunk stored in this slot
+    if (I * RPL < BM) {
       voff[j] = (uint32_t)(((long)arow[j] * g.lda + c * 8) * 2);
       which[j] = 0;
     } else {
@@ -435,7 +452,7 @@ gemm_dma_kernel(GemmArgs g) {
     const int kb = g.brep ? k % g.brep : k;
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const uint32_t dst = lds0 + (uint32_t)(st * ROWS * 128 + (wid * NDMA + j) * 1024);
+      const uint32_t dst = lds0 + (uint32_t)(st * ROWS * CPR * 16 + (wid * NDMA + j) * 1024);
       const i32x4_t rs = which[j] == 0 ? rsA : (which[j] == 1 ? rsB : rsB2);
       dma16(rs, __builtin_amdgcn_readfirstlane(dst),
             voff[j] + (uint32_t)((which[j] == 0 ? k : kb) * 2));
@@ -462,15 +479,15 @@ gemm_dma_kernel(GemmArgs g) {
     constexpr int LIVE = decltype(live_c)::value;
     auto compute = [&](int st) {
       const u32x4_t* As = &smem[st][0];
-      const u32x4_t* Bs = &smem[st][BM * 8];
+      const u32x4_t* Bs = &smem[st][BM * CPR];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         u32x4_t af[LIVE > 0 ? LIVE : 1], bfr[FN];
 #pragma unroll
-        for (int i = 0; i < LIVE; ++i) af[i] = As[swz1(wm * TM + i * 32 + lr, ks * 2 + lg)];
+        for (int i = 0; i < LIVE; ++i) af[i] = As[swz<CPR>(wm * TM + i * 32 + lr, ks * 2 + lg)];
         if (LIVE > 0) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) bfr[j] = Bs[swz1(wn * TN + j * 32 + lr, ks * 2 + lg)];
+          for (int j = 0; j < FN; ++j) bfr[j] = Bs[swz<CPR>(wn * TN + j * 32 + lr, ks * 2 + lg)];
         }
 #pragma unroll
         for (int i = 0; i < LIVE; ++i)
@@ -502,7 +519,7 @@ gemm_dma_kernel(GemmArgs g) {
                              ncol0 + wn * (DUAL ? TN / 2 : TN), lane);
 }
 
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int WM, int WN, int S, int BK = 64>
 int launch_dma_cfg(const GemmArgs& g, Exec st) {
   const bool dual = (g.epi == EPI_SWIGLU_BF16 || g.epi == EPI_SWIGLU_F32);
   const int bn_out = dual ? BN / 2 : BN;
@@ -510,7 +527,7 @@ int launch_dma_cfg(const GemmArgs& g, Exec st) {
   const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
   const dim3 grid((g.N + bn_out - 1) / bn_out, mt, nsplit), block(64 * WM * WN);
 #define DS4G_DMA(E, F) \
-  DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, E, F>), grid, block, 0, st, g)
+  DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, E, F, BK>), grid, block, 0, st, g)
   if (g.f16) {   // the attention path: fp16 operands
     if (g.tiles) return -1;
     switch (g.epi) {
@@ -658,7 +675,7 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
       // spread over the CUs and two blocks fit a CU's LDS
       if (g.rows_hint == 64) return launch_dma_cfg<64, 128, 2, 2, 3>(g, st);
       if (g.rows_hint == 128) return launch_dma_cfg<128, 256, 2, 4, 3>(g, st);
-      if (g.rows_hint == 256) return launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, 2>(g, st);
+      if (g.rows_hint == 256) return launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, DS4G_BIG_S, DS4G_BIG_BK>(g, st);
       return -1;
     }
     const long nout = dual ? g.N * 2L : g.N;           // B rows per output row
@@ -680,13 +697,13 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
         const size_t es =
             (g.epi == EPI_BF16 || g.epi == EPI_F16 || g.epi == EPI_SWIGLU_BF16) ? 2 : 4;
         lo.C = static_cast<char*>(g.C) + (size_t)mb * g.ldc * es;
-        const int r = launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, 2>(hi, st);
+        const int r = launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, DS4G_BIG_S, DS4G_BIG_BK>(hi, st);
         if (r) return r;
         const long lblocks = ((lo.M + 127) / 128) * ((nout + 127) / 128);
         if (lblocks <= 256) return launch_dma_cfg<128, 128, 2, 2, 3>(lo, st);
         return launch_dma_cfg<128, 128, 2, 2, 2>(lo, st);
       }
-      return launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, 2>(g, st);
+      return launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, DS4G_BIG_S, DS4G_BIG_BK>(g, st);
     }
     if (g.M <= 64) return launch_dma_cfg<64, 256, 1, 4, 3>(g, st);
     const long blocks = ((g.M + 127) / 128) * ((nout + 127) / 128) * nsplit;
