@@ -40,12 +40,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 
 # HBM bytes of one decode step as read by the hardware counters (rocprofv3
 # --pmc FETCH_SIZE, then WRITE_SIZE, summed over the step's 7 kernels, mean of
-# 8 steps; FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0, the factors that make a
+# 12 steps; FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0, the factors that make a
 # 1 GiB device copy read 1 GiB and write 1 GiB).  Valid only for the decode
 # sources it was measured on: any change to them reports traffic as null.
-DECODE_TRAFFIC_BYTES = 274063385
+DECODE_TRAFFIC_BYTES = 273973964
 DECODE_TRAFFIC_SOURCES = ("api.hip", "attn.hip", "decode.hip", "dev.h", "kernels.h")
-DECODE_TRAFFIC_SHA1 = "b5cb6045aa4e934094b068d55473b824794638f8"
+DECODE_TRAFFIC_SHA1 = "b1fae9d59b70889bd77aefe9c3f28ecaf3aaeba1"
 
 
 def decode_traffic():
