@@ -33,7 +33,7 @@
 #define DS4G_ROUTER_SHARED_RB 2
 #endif
 #ifndef DS4G_SHGU_GRID_MAX   // blocks of the gate/up launch that compute the shared gate/up
-#define DS4G_SHGU_GRID_MAX 256
+#define DS4G_SHGU_GRID_MAX 128
 #endif
 
 namespace ds4g {

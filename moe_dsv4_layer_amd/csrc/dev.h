@@ -203,53 +203,86 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ----------------------------------------------------------- routing
-// Router selection: top-k of the E <= 512 logits (descending, ties to the
+// Order-preserving map of a float to an unsigned key (larger float, larger
+// key; -0 < +0) and back.
+__device__ __forceinline__ unsigned order_key(float x) {
+  const unsigned u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_val(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+#define DS4G_DPP_MAXU(ctrl, rm) v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, rm, 0xF, false))
+  DS4G_DPP_MAXU(0x111, 0xF); DS4G_DPP_MAXU(0x112, 0xF); DS4G_DPP_MAXU(0x114, 0xF);
+  DS4G_DPP_MAXU(0x118, 0xF); DS4G_DPP_MAXU(0x142, 0xA); DS4G_DPP_MAXU(0x143, 0xC);
+#undef DS4G_DPP_MAXU
+  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Router selection: top-k of the E <= 64 NV logits (descending, ties to the
 // lower index) and the softmax probabilities of the chosen ones, by one wave
-// with the logits in registers (element lane + 64 i).  Each lane keeps its
-// best remaining element (first maximum in i order, so the lowest index among
-// its equal values); a round takes the wave max of those, then the lowest
-// index among the lanes that hold it, and only the winning lane rescans.
-// This runs before the first routed weight load, so it is kept short: a
-// rolled loop over the k rounds, two DPP reductions each.  Lane 0 writes the
-// choices to sel / wsel (this wave's own LDS slots).
-__device__ __forceinline__ void route_wave(const float (&lg)[8], int E, int k, int* sel,
+// with the logits in registers (element lane + 64 i, i < NV).  Each lane
+// sorts its NV elements by (key descending, index ascending); a round takes
+// the wave max of the lanes' heads, then the lowest index among the heads
+// that hold it, and the lane that owns it drops its head: two DPP reductions
+// and a register shift per round.  A NaN logit ranks as -inf.  Lane r < k
+// keeps the r-th choice and writes it to sel[r] / wsel[r] (LDS or global).
+template <int NV>
+__device__ __forceinline__ void route_topk(const float (&lg)[8], int E, int k, int* sel,
                                            float* wsel) {
   const int lane = threadIdx.x & 63;
-  // a NaN score ranks below every number; a chosen expert becomes NaN, which
-  // neither > nor == selects again.  k < E leaves a candidate every round.
-  float v[8];
+  unsigned key[NV];
+  int idx[NV];
+  float v[NV];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
     const float x = lg[i];
-    v[i] = (lane + 64 * i < E) ? (x == x ? x : -INFINITY) : __builtin_nanf("");
+    v[i] = x == x ? x : -INFINITY;
+    key[i] = e < E ? order_key(v[i]) : 0u;   // every valid key is above 0
+    idx[i] = e;
   }
-  auto best = [&](float& bv, int& bi) {
-    bv = -INFINITY;
-    bi = 0x7fffffff;
+  // odd-even transposition sort of the lane's NV entries
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (v[i] > bv || (v[i] == bv && lane + 64 * i < bi)) { bv = v[i]; bi = lane + 64 * i; }
-  };
-  float bv;
-  int bi;
-  best(bv, bi);
-  const float m = wave_max(bv);
+  for (int pass = 0; pass < NV; ++pass)
+#pragma unroll
+    for (int a = pass & 1; a + 1 < NV; a += 2) {
+      const bool sw = key[a + 1] > key[a] || (key[a + 1] == key[a] && idx[a + 1] < idx[a]);
+      const unsigned tk = sw ? key[a + 1] : key[a];
+      const int ti = sw ? idx[a + 1] : idx[a];
+      key[a + 1] = sw ? key[a] : key[a + 1];
+      idx[a + 1] = sw ? idx[a] : idx[a + 1];
+      key[a] = tk;
+      idx[a] = ti;
+    }
+  const unsigned m0 = wave_max_u32(key[0]);
+  const float m = order_val(m0);
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
+  for (int i = 0; i < NV; ++i) s += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
   s = wave_sum(s);
+  float mytop = 0.f;
+  int myidx = 0;
 #pragma unroll 1
   for (int r = 0; r < k; ++r) {
-    const float top = (r == 0) ? m : wave_max(bv);
-    const int idx = min(wave_min(bv == top ? bi : 0x7fffffff), E - 1);
-    if (lane == 0) { sel[r] = idx; wsel[r] = expf(top - m) / s; }
-    if (lane == (idx & 63)) {
+    const unsigned top = (r == 0) ? m0 : wave_max_u32(key[0]);
+    const int w = min(wave_min(key[0] == top ? idx[0] : 0x7fffffff), E - 1);
+    if (lane == r) { mytop = order_val(top); myidx = w; }
+    if (idx[0] == w) {   // the owner drops its head
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (lane + 64 * i == idx) v[i] = __builtin_nanf("");
-      best(bv, bi);
+      for (int i = 0; i + 1 < NV; ++i) { key[i] = key[i + 1]; idx[i] = idx[i + 1]; }
+      key[NV - 1] = 0u;
     }
   }
+  if (lane < k) { sel[lane] = myidx; wsel[lane] = expf(mytop - m) / s; }
+}
+__device__ __forceinline__ void route_wave(const float (&lg)[8], int E, int k, int* sel,
+                                           float* wsel) {
+  if (E <= 64) route_topk<1>(lg, E, k, sel, wsel);
+  else if (E <= 128) route_topk<2>(lg, E, k, sel, wsel);
+  else if (E <= 256) route_topk<4>(lg, E, k, sel, wsel);
+  else route_topk<8>(lg, E, k, sel, wsel);
   wave_lds_sync();
 }
 
