@@ -202,15 +202,17 @@ int launch_attention(const AttnArgs& a, Exec st) {
 //
 // One block (256 threads) per head.  The work per head is tiny (2 x 128 x dh
 // multiply-adds), so the kernel is latency-bound: every thread issues all of
-// its K and V loads (straight from the ring into registers) right after
-// reading *pos, and the math needs only a few block barriers.
-//   scores: thread t owns half of key j = t/2 (dh/2 dims), halves meet by
+// its K and V loads (straight from the ring into registers) at once, by ring
+// slot, without waiting for *pos, and the RoPE frequencies are formed while
+// *pos is in flight; the position only masks slots and picks the angle.
+//   scores: thread t owns half of slot s = t/2 (dh/2 dims), halves meet by
 //           a lane shuffle;
-//   p.v:    thread t owns 8 dims (group t % DG) of KPG keys (group t / DG),
-//           key groups meet in LDS.
-// Slot p % W holds position p - W, outside the window, so block 0 may
-// overwrite it while the other blocks read.  *pos is advanced by a later
-// kernel.  Batched decode: blockIdx.y is the sequence b, with its own qkv row
+//   p.v:    thread t owns 8 dims (group t % DG) of KPG slots (group t / DG),
+//           slot groups meet in LDS.
+// Slot s holds key j = (s - lo) mod W of the window [lo, p]; slot p % W
+// holds position p - W, outside the window: its load is replaced by the
+// token's own k, v, and block 0 may overwrite it while the other blocks read.
+// *pos is advanced by a later kernel.  Batched decode: blockIdx.y is the sequence b, with its own qkv row
 // (stride qkv_stride), ring (b * W * DH), position pos[b] and o row (H * DH);
 // o is fp32 or fp16 (OT).
 template <int DH, typename OT>
@@ -253,16 +255,11 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
     ta = qkv[qd + DH + (tid - DH)];
   }
   const long p = *pos;
-  const long lo = p - W + 1 > 0 ? p - W + 1 : 0;
-  const int n = (int)(p - lo + 1);                 // window keys; the token is key n-1
-  const int s0 = (int)(lo % W);
-  // ---- issue every ring load now
+  // ---- issue every ring load now, by slot (slots past W read slot 0)
   const int jk = tid >> 1, hk = tid & 1;
   uint4 kreg[KC];
   {
-    int slot = s0 + jk;
-    slot = slot >= W ? slot - W : slot;
-    const long at = (jk < n - 1) ? (long)slot * DH + hk * (DH / 2) : 0;
+    const long at = (jk < W) ? (long)jk * DH + hk * (DH / 2) : 0;
 #pragma unroll
     for (int c = 0; c < KC; ++c) kreg[c] = *reinterpret_cast<const uint4*>(ring_k + at + c * 8);
   }
@@ -270,15 +267,21 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
   uint4 vreg[KPG];
 #pragma unroll
   for (int u = 0; u < KPG; ++u) {
-    const int j = kg * KPG + u;
-    int slot = s0 + j;
-    slot = slot >= W ? slot - W : slot;
-    const long at = (j < n - 1) ? (long)slot * DH + dg * 8 : 0;
+    const int sl = kg * KPG + u;
+    const long at = (sl < W) ? (long)sl * DH + dg * 8 : 0;
     vreg[u] = *reinterpret_cast<const uint4*>(ring_v + at);
   }
+  // RoPE frequencies need no position
+  double rinv = 0.0;
+  if (tid < rd / 2) rinv = rope_inv(tid, rd, base);
+  // the window [lo, p]: slot s holds key (s - lo) mod W, the token is key n-1
+  const long lo = p - W + 1 > 0 ? p - W + 1 : 0;
+  const int n = (int)(p - lo + 1);
+  const int s0 = (int)(lo % W);
+  auto key_of = [&](int sl) { const int j = sl - s0; return j < 0 ? j + W : j; };
   // ---- RoPE of q (this head) and k; the token's k, v in fp16 like the ring
   const int off = DH - rd;
-  for (int i = tid; i < rd / 2; i += 256) rope_cs(p, i, rd, base, &cs[i], &sn[i]);
+  if (tid < rd / 2) rope_cs_inv(p, rinv, &cs[tid], &sn[tid]);
   __syncthreads();
   if (tid < DH) {   // pairs: tid < DH/2 -> q, else -> k
     const bool isq = tid < DH / 2;
@@ -301,10 +304,11 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
     if (tid < DH) ring_k[slot * DH + tid] = kself[tid];
     else if (tid < 2 * DH) ring_v[slot * DH + tid - DH] = vself[tid - DH];
   }
-  // ---- scores
+  // ---- scores (slot jk, key kj)
+  const int kj = jk < W ? key_of(jk) : W;
   float sj;
   {
-    if (jk == n - 1) {
+    if (kj == n - 1) {
 #pragma unroll
       for (int c = 0; c < KC; ++c)
         kreg[c] = *reinterpret_cast<const uint4*>(kself + hk * (DH / 2) + c * 8);
@@ -320,14 +324,14 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
              q1.x * f[4] + q1.y * f[5] + q1.z * f[6] + q1.w * f[7];
     }
     acc += __shfl_xor(acc, 1, 64);
-    sj = (jk < n) ? acc * rsqrtf((float)DH) : -INFINITY;
+    sj = (kj < n) ? acc * rsqrtf((float)DH) : -INFINITY;
   }
   // softmax over the window: block max and sum (each key counted by its even lane)
   const float m = wave_max(sj);
   if (lane == 0) wred[wid] = m;
   __syncthreads();
   const float mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-  const float ej = (jk < n) ? expf(sj - mx) : 0.f;
+  const float ej = (kj < n) ? expf(sj - mx) : 0.f;
   const float es = wave_sum(hk == 0 ? ej : 0.f);
   __syncthreads();
   if (lane == 0) wred[wid] = es;
@@ -339,13 +343,14 @@ attn_decode_kernel(const float* __restrict__ qkv, long qkv_stride, int H, int W,
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < KPG; ++u) {
-      const int j = kg * KPG + u;
+      const int sl = kg * KPG + u;
+      const int j = sl < W ? key_of(sl) : W;
       if (j < n) {
         uint4 v4 = vreg[u];
         if (j == n - 1) v4 = *reinterpret_cast<const uint4*>(vself + dg * 8);
         float f[8];
         unpack8_f16(v4, f);
-        const float pj = pr[j];
+        const float pj = pr[sl];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += pj * f[e];
       }

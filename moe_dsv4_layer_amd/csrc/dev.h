@@ -290,12 +290,17 @@ __device__ __forceinline__ void route_wave(const float (&lg)[8], int E, int k, i
 // p * base^(-2i/rd).  The angle is formed and reduced modulo 2*pi in fp64
 // (positions reach 1e4..1e6), then sin/cos are taken in fp32 of the reduced
 // angle.  Shared by the prefill and decode kernels so both rotate alike.
-__device__ __forceinline__ void rope_cs(long p, int i, int rd, float base, float* c, float* s) {
-  const double inv = exp2(-(2.0 * (double)i / (double)rd) * log2((double)base));
+__device__ __forceinline__ double rope_inv(int i, int rd, float base) {
+  return exp2(-(2.0 * (double)i / (double)rd) * log2((double)base));
+}
+__device__ __forceinline__ void rope_cs_inv(long p, double inv, float* c, float* s) {
   const double th = (double)p * inv;
   const double two_pi = 6.283185307179586476925286766559;
   const double red = th - two_pi * rint(th / two_pi);
   sincosf((float)red, s, c);
+}
+__device__ __forceinline__ void rope_cs(long p, int i, int rd, float base, float* c, float* s) {
+  rope_cs_inv(p, rope_inv(i, rd, base), c, s);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
