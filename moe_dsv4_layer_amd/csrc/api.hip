@@ -201,6 +201,46 @@ int dry_then_run(hipStream_t stream, F&& seq) {
 }
 
 // ------------------------------------------------------------------ prefill
+// A second stream per device, for the shared expert: it needs only y, so it
+// runs beside the router, the routing and the routed experts, and the
+// combine waits for it.  Created on the first prefill on each device (never
+// while the caller's stream is being captured into a graph); nullptr if HIP
+// refuses, and then the shared expert runs on the caller's stream.  Default
+// priority, non-blocking; the fork and join events are reused by every call,
+// so enqueueing from the fork to the join holds side_mutex().
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
+std::mutex& side_mutex() {
+  static std::mutex mu;
+  return mu;
+}
+SideStream* side_stream(hipStream_t main) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static SideStream ss[kMaxDevices] = {};
+  static bool tried[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!tried[dev]) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(main, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+      return nullptr;
+    tried[dev] = true;
+    SideStream t{};
+    if (hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&t.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&t.join, hipEventDisableTiming) != hipSuccess) {
+      fprintf(stderr, "ds4g: no events for the shared-expert stream; it runs inline\n");
+      return nullptr;
+    }
+    ss[dev] = t;
+  }
+  return ss[dev].s ? &ss[dev] : nullptr;
+}
+
 // Layer-major prefill of T tokens of one sequence, or (batch) one decode
 // token of each of T independent sequences: the same GEMMs, router and
 // experts over T rows; only the attention stage differs.
@@ -214,6 +254,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
             Is = c.shared_inter;
   const int rd = c.rope_dim ? c.rope_dim : dh;
   int rc = 0;
+  Exec cur = st;   // the stream the dense GEMMs below go to
 
   // x_norm = RMSNorm(h) * g1.  bf16 weights: the attention path (x_norm, c,
   // q, k, v, probabilities, o) runs in fp16 on the matrix cores; fp32
@@ -257,7 +298,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
       v.W = static_cast<const uint16_t*>(B); v.W2 = static_cast<const uint16_t*>(B2);
       v.N = N; v.K = K; v.X = static_cast<const uint16_t*>(A); v.x_f16 = img >= 0 ? 1 : 0;
       v.lda = lda; v.M = M; v.epi = epi; v.C = C; v.ldc = ldc;
-      if (launch_gemv_rows(v, st) == 0) return;
+      if (launch_gemv_rows(v, cur) == 0) return;
     }
     const float* cs = nullptr;
     if (bf && img >= 0) {
@@ -273,19 +314,19 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
       g.A = A; g.lda = lda; g.M = M; g.N = N; g.K = K; g.epi = EPI_F32; g.ldc = N;
       g.ksplit = s; g.part_stride = ps; g.f16 = img >= 0 ? 1 : 0;
       g.B = B; g.C = part;
-      rc |= launch_gemm(g, bf, 1, st);
+      rc |= launch_gemm(g, bf, 1, cur);
       if (B2) {
         g.B = B2; g.C = part + (size_t)s * ps;
-        rc |= launch_gemm(g, bf, 1, st);
+        rc |= launch_gemm(g, bf, 1, cur);
       }
       rc |= launch_splitk_reduce(part, B2 ? part + (size_t)s * ps : nullptr, s, ps, M, N, epi, C,
-                                 ldc, cs, st);
+                                 ldc, cs, cur);
       return;
     }
     GemmArgs g{};
     g.A = A; g.lda = lda; g.B = B; g.B2 = B2; g.M = M; g.N = N; g.K = K; g.epi = epi; g.C = C;
     g.ldc = ldc; g.f16 = (bf && img >= 0) ? 1 : 0; g.colscale = cs;
-    rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
+    rc |= launch_gemm(g, bf, bf ? 1 : 0, cur);
   };
   // c = A x ; qkv = B c (prefill on the matrix cores: RoPE in the epilogue,
   // q / k / v written rotated in fp16, as attention reads them)
@@ -348,6 +389,27 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     rc |= launch_rmsnorm_rows<float>(x, T, d, (const float*)w.ffn_norm, c.rms_eps,
                                      at<float>(ws, L.yf), nullptr, nullptr, nullptr, st);
 
+  // the shared expert, x = h2 + D_sh(silu(G_sh y) * (U_sh y)), on the side
+  // stream when there is one (nothing on this stream touches x until the
+  // combine, which waits for it)
+  const void* yA = bf ? at<void>(ws, L.ys) : at<void>(ws, L.yf);
+  const int ylda = bf ? 3 * d : d;
+  // (a few rows: the fork and join cost more than the overlap gives)
+  SideStream* side = (st.dry || T < 32) ? nullptr : side_stream(st.stream);
+  std::unique_lock<std::mutex> side_lock(side_mutex(), std::defer_lock);
+  if (side) {
+    side_lock.lock();
+    if (hipEventRecord(side->fork, st.stream) != hipSuccess ||
+        hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+      rc |= -1;
+    cur = Exec{side->s, false};
+  }
+  gemm(yA, ylda, w.sh_gate, T, Is, d, bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32, at<void>(ws, L.zs),
+       Is, w.sh_up);
+  gemm(at<void>(ws, L.zs), Is, w.sh_down, T, d, Is, EPI_RESID, x, d);
+  if (side && hipEventRecord(side->join, side->s) != hipSuccess) rc |= -1;
+  cur = st;
+
   // router logits at fp32 quality (they decide integer expert choices):
   // bf16 weights: y1|y2|y3 against [W_r|W_r|W_r] on the matrix cores; fp32
   // weights: fp32 y on the vector ALUs.  Split-K partial sums, added in split
@@ -391,8 +453,6 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   rc |= launch_route(ra, st);
   const int max_tiles = E + (T * k + tile_m - 1) / tile_m;
 
-  const void* yA = bf ? at<void>(ws, L.ys) : at<void>(ws, L.yf);
-  const int ylda = bf ? 3 * d : d;
   // routed gate/up + SwiGLU over the permuted rows
   {
     GemmArgs g{};
@@ -403,9 +463,6 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.xcd_remap = 1;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
-  // shared gate/up + SwiGLU over every token
-  gemm(yA, ylda, w.sh_gate, T, Is, d, bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32, at<void>(ws, L.zs),
-       Is, w.sh_up);
   // routed down projections -> part (permuted rows; bf16 on the MFMA path,
   // fp32 on the fp32-weight path), combined in fp32 below
   {
@@ -418,8 +475,11 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.xcd_remap = tile_m >= DS4G_DOWN_XCD_REMAP_MIN;   // 1.1% at 16994 tokens, 0.5% slower at 2048
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
-  // shared down (x = h2 + shared), then combine: x += sum_j w_j part_j
-  gemm(at<void>(ws, L.zs), Is, w.sh_down, T, d, Is, EPI_RESID, x, d);
+  // combine, x += sum_j w_j part_j, once the shared expert is in x
+  if (side) {
+    if (hipStreamWaitEvent(st.stream, side->join, 0) != hipSuccess) rc |= -1;
+    side_lock.unlock();
+  }
   // batched decode: the combine also advances each sequence's position (the
   // attention kernel read it; nothing after the combine does)
   rc |= launch_moe_combine(x, at<void>(ws, L.part), bf ? 1 : 0, ra.pos_of, ra.topk_w, T, d, k,
