@@ -42,7 +42,12 @@
  *     inputs.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream).  They never synchronise and never call the allocator, so a
- *     decode step can be captured in a HIP graph and replayed.
+ *     decode step can be captured in a HIP graph and replayed.  A prefill or
+ *     batched decode of 32 or more rows runs the shared expert on a second
+ *     stream that the library creates once per device (default priority,
+ *     never while `stream` is being captured; without it the work stays on
+ *     `stream`), forked from and joined back into `stream` with events, so
+ *     the call's work is still ordered on `stream`.
  *   - Every argument check runs on the host before anything is enqueued; on
  *     an error nothing is written and a negative ds4g_status is returned.
  *     A call first walks its whole launch sequence without enqueuing (each

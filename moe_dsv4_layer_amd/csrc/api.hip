@@ -399,15 +399,23 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   std::unique_lock<std::mutex> side_lock(side_mutex(), std::defer_lock);
   if (side) {
     side_lock.lock();
-    if (hipEventRecord(side->fork, st.stream) != hipSuccess ||
-        hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
-      rc |= -1;
-    cur = Exec{side->s, false};
+    if (hipEventRecord(side->fork, st.stream) == hipSuccess &&
+        hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess) {
+      cur = Exec{side->s, false};
+    } else {   // no fork: the shared expert runs on the caller's stream
+      side = nullptr;
+      side_lock.unlock();
+    }
   }
   gemm(yA, ylda, w.sh_gate, T, Is, d, bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32, at<void>(ws, L.zs),
        Is, w.sh_up);
   gemm(at<void>(ws, L.zs), Is, w.sh_down, T, d, Is, EPI_RESID, x, d);
-  if (side && hipEventRecord(side->join, side->s) != hipSuccess) rc |= -1;
+  if (side && hipEventRecord(side->join, side->s) != hipSuccess) {
+    // no join event: wait for the side stream here instead
+    if (hipStreamSynchronize(side->s) != hipSuccess) rc |= -1;
+    side_lock.unlock();
+    side = nullptr;
+  }
   cur = st;
 
   // router logits at fp32 quality (they decide integer expert choices):
@@ -477,7 +485,9 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   }
   // combine, x += sum_j w_j part_j, once the shared expert is in x
   if (side) {
-    if (hipStreamWaitEvent(st.stream, side->join, 0) != hipSuccess) rc |= -1;
+    if (hipStreamWaitEvent(st.stream, side->join, 0) != hipSuccess &&
+        hipStreamSynchronize(side->s) != hipSuccess)
+      rc |= -1;
     side_lock.unlock();
   }
   // batched decode: the combine also advances each sequence's position (the
