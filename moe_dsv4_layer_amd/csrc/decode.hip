@@ -119,6 +119,10 @@ gemv_kernel(GemvArgs a) {
 
   for (; r0 < N; r0 += stride) {
     const int rbase = r0 + rgroup * RB;
+    // the residual of the rows this thread writes goes out with the weights,
+    // not after the reductions
+    const bool writer = (KSPLIT == 1 || kpart == 0) && lane < RB && rbase + lane < N;
+    const float res = (a.accumulate && writer) ? a.out[rbase + lane] : 0.f;
     float acc[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -142,7 +146,7 @@ gemv_kernel(GemvArgs a) {
         float v = acc[0];
 #pragma unroll
         for (int r = 1; r < RB; ++r) if (lane == r) v = acc[r];
-        a.out[rbase + lane] = a.accumulate ? a.out[rbase + lane] + v : v;
+        a.out[rbase + lane] = a.accumulate ? res + v : v;
       }
     } else {
       __syncthreads();
@@ -155,7 +159,7 @@ gemv_kernel(GemvArgs a) {
         float v = 0.f;
 #pragma unroll
         for (int p = 0; p < KSPLIT; ++p) v += red[rgroup * KSPLIT + p][lane];
-        a.out[rbase + lane] = a.accumulate ? a.out[rbase + lane] + v : v;
+        a.out[rbase + lane] = a.accumulate ? res + v : v;
       }
     }
   }
@@ -635,8 +639,10 @@ moe_down_decode(MoeDecodeArgs a, float* x, int64_t* pos_inc) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (threadIdx.x < a.k) { sel[threadIdx.x] = a.sel[threadIdx.x]; wsel[threadIdx.x] = a.wsel[threadIdx.x]; }
   if (pos_inc && blockIdx.x == 0 && threadIdx.x == 0) *pos_inc += 1;
-  __syncthreads();
   const int n0 = blockIdx.x * RB;
+  // the residual rows go out before the weights
+  const float h2v = (threadIdx.x < RB && n0 + (int)threadIdx.x < a.d) ? a.h2[n0 + threadIdx.x] : 0.f;
+  __syncthreads();
   if (wid <= a.k) {
     const int s = wid;
     const bool shared = s == a.k;
@@ -681,7 +687,7 @@ moe_down_decode(MoeDecodeArgs a, float* x, int64_t* pos_inc) {
     float v = 0.f;
     for (int s = 0; s < a.k; ++s) v += wsel[s] * part[s][lane];
     v += part[a.k][lane];
-    x[n0 + lane] = a.h2[n0 + lane] + v;
+    x[n0 + lane] = h2v + v;
   }
 }
 
