@@ -21,6 +21,12 @@ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kRouterSplit = 24;
 constexpr int kBatchRouterSplit = 12;   // batched decode (<= kRouterSplit)
 
+// GEMMs with 16-bit outputs store them through LDS in 16-byte row chunks
+// (GemmArgs::stage16) when their tiles are mostly full: dense GEMMs of at
+// least this many rows, grouped expert GEMMs of at least half as many rows
+// per expert on average.  A tile with a few rows stores less the direct way.
+constexpr int kStageRows = 64;
+
 // Batched decode (a few rows per GEMM): split K so that a dense GEMM runs
 // ~256 blocks instead of one per N tile.  A power of two dividing K / 64, at
 // most 64; 1 beyond 256 rows or on the fp32-weight path.  The tile shapes
@@ -326,6 +332,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     GemmArgs g{};
     g.A = A; g.lda = lda; g.B = B; g.B2 = B2; g.M = M; g.N = N; g.K = K; g.epi = epi; g.C = C;
     g.ldc = ldc; g.f16 = (bf && img >= 0) ? 1 : 0; g.colscale = cs;
+    g.stage16 = M >= kStageRows;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, cur);
   };
   // c = A x ; qkv = B c (prefill on the matrix cores: RoPE in the epilogue,
@@ -346,6 +353,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.rope_c = rc_tab; g.rope_s = rc_tab + (size_t)(rd / 2) * tpad; g.rope_ld = tpad;
     g.rope_dh = dh; g.rope_rd = rd;
     g.rope_kc = at<uint16_t>(ws, L.kc); g.rope_vc = at<uint16_t>(ws, L.vc);
+    g.stage16 = T >= kStageRows;
     rc |= launch_gemm(g, true, 1, st);
   } else {
     gemm(at<void>(ws, L.c), r, w.qkv_b, T, qkvd, r, EPI_F32, at<void>(ws, L.qkv), qkvd, nullptr,
@@ -469,6 +477,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.row_off = ra.offset; g.max_tiles = max_tiles; g.rows_hint = tile_m;
     g.epi = bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_F32; g.C = at<void>(ws, L.z); g.ldc = I;
     g.xcd_remap = 1;
+    g.stage16 = mean_rows >= kStageRows / 2;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
   // routed down projections -> part (permuted rows; bf16 on the MFMA path,
@@ -481,6 +490,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     g.C = at<void>(ws, L.part);
     g.ldc = d;
     g.xcd_remap = tile_m >= DS4G_DOWN_XCD_REMAP_MIN;   // 1.1% at 16994 tokens, 0.5% slower at 2048
+    g.stage16 = mean_rows >= kStageRows / 2;
     rc |= launch_gemm(g, bf, bf ? 1 : 0, st);
   }
   // combine, x += sum_j w_j part_j, once the shared expert is in x

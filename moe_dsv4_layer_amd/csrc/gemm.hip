@@ -327,6 +327,109 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, f32x16 (&acc)[F
     }
 }
 
+// 16-bit outputs (EPI_BF16, EPI_F16, EPI_SWIGLU_BF16, EPI_ROPE_QKV) through
+// LDS: each wave writes its fragments' final values into a row-major tile
+// [BM][OUTC] (row stride OUTC * 2 + 16 bytes, so the two row groups of a
+// fragment write land on different banks), then the block stores 16-byte
+// chunks: 8 lanes cover 128 bytes of a row, where the fragment layout stores
+// two 64-byte runs of 2-byte values per instruction.  Same values, same
+// rounding as mfma_epilogue.  stg: LDS bytes, free (every wave is past its
+// last read of the ring).  Returns with the block synchronised.
+template <int EPI, int BM, int OUTC, int NT, int FM, int FN>
+__device__ __forceinline__ void staged_epilogue(const GemmArgs& g, f32x16 (&acc)[FM][FN],
+                                                unsigned char* stg, int trow0, int row1,
+                                                int tcol0, int wrow0, int wcol0, int lane) {
+  constexpr bool DUAL = EPI == EPI_SWIGLU_BF16;
+  constexpr int RS = OUTC * 2 + 16;
+  const int lr = lane & 31, lg = lane >> 5;
+  if (!DUAL && g.colscale) {   // as mfma_epilogue: the column factor first
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const float f = g.colscale[min(tcol0 + wcol0 + j * 32 + lr, g.N - 1)];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= f;
+    }
+  }
+  auto put = [&](int lrow, int lcol, uint16_t v) {
+    *reinterpret_cast<uint16_t*>(stg + lrow * RS + lcol * 2) = v;
+  };
+  if constexpr (EPI == EPI_ROPE_QKV) {
+#pragma clang fp contract(off)
+    const int dh = g.rope_dh, qd = g.N - 2 * dh, off = dh - g.rope_rd;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int lcol = wcol0 + j * 32 + lr, col = tcol0 + lcol;
+      const int e = col < qd ? col % dh : (col < qd + dh ? col - qd : col - qd - dh);
+      const bool rot = col < qd + dh && e >= off;
+      const long tab = (long)(rot ? (e - off) >> 1 : 0) * g.rope_ld;
+      const float sgn = (col & 1) ? 1.f : -1.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int lrow = wrow0 + i * 32 + 8 * q4 + 4 * lg;
+          const int rt = min(trow0 + lrow, g.rope_ld - 4);   // rows past the table are not stored
+          const float4 mine = *reinterpret_cast<const float4*>(
+              ((col & 1) ? g.rope_s : g.rope_c) + tab + rt);
+          const float m4[4] = {mine.x, mine.y, mine.z, mine.w};
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const float other = __int_as_float(
+                __builtin_amdgcn_mov_dpp(__float_as_int(m4[ii]), 0xB1, 0xF, 0xF, false));
+            const float cv = (col & 1) ? other : m4[ii];
+            const float sv = (col & 1) ? m4[ii] : other;
+            const float own = acc[i][j][4 * q4 + ii];
+            const float oth = __int_as_float(
+                __builtin_amdgcn_mov_dpp(__float_as_int(own), 0xB1, 0xF, 0xF, false));
+            const float v = rot ? own * cv + sgn * oth * sv : own;
+            put(lrow + ii, lcol, f32_to_f16(v));
+          }
+        }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int lrow = wrow0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+        if constexpr (DUAL) {
+#pragma unroll
+          for (int j = 0; j < FN; j += 2)
+            put(lrow, wcol0 + (j >> 1) * 32 + lr,
+                f32_to_bf16(silu(acc[i][j][e]) * acc[i][j + 1][e]));
+        } else {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const float v = acc[i][j][e];
+            put(lrow, wcol0 + j * 32 + lr, EPI == EPI_F16 ? f32_to_f16(v) : f32_to_bf16(v));
+          }
+        }
+      }
+  }
+  __syncthreads();
+  constexpr int CPRW = OUTC / 8;   // 16-byte chunks per row
+  const int nrows = min(BM, row1 - trow0);
+  const int qd = EPI == EPI_ROPE_QKV ? g.N - 2 * g.rope_dh : 0;
+  for (int c = threadIdx.x; c < nrows * CPRW; c += NT) {
+    const int lrow = c / CPRW, cc = c - lrow * CPRW;
+    const int col = tcol0 + cc * 8, row = trow0 + lrow;
+    if (col >= g.N) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(stg + lrow * RS + cc * 16);
+    uint16_t* dst;
+    if constexpr (EPI == EPI_ROPE_QKV) {
+      const int dh = g.rope_dh;
+      if (col < qd) dst = static_cast<uint16_t*>(g.C) + (long)row * g.ldc + col;
+      else if (col < qd + dh) dst = g.rope_kc + (long)row * dh + (col - qd);
+      else dst = g.rope_vc + (long)row * dh + (col - qd - dh);
+    } else {
+      dst = static_cast<uint16_t*>(g.C) + (long)row * g.ldc + col;
+    }
+    *reinterpret_cast<uint4*>(dst) = v;
+  }
+}
+
 // =========================================================================
 // MFMA GEMM with an S-stage LDS ring filled by direct global -> LDS loads
 // (buffer_load_dwordx4 ... lds): each lane's 16 bytes land in a fixed LDS
@@ -372,7 +475,7 @@ __device__ __forceinline__ bool xcd_tile(int nb, int& bx, int& by) {
   return true;
 }
 
-template <int BM, int BN, int WM, int WN, int S, int EPI, bool F16, int BK>
+template <int BM, int BN, int WM, int WN, int S, int EPI, bool F16, int BK, bool STG>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_dma_kernel(GemmArgs g) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32);
@@ -388,7 +491,13 @@ gemm_dma_kernel(GemmArgs g) {
   static_assert(NDMA * RPL * NW == ROWS && BM % RPL == 0, "whole loads per wave");
   static_assert(!DUAL || FN % 2 == 0, "SwiGLU pairs gate/up fragments");
   static_assert(S >= 2 && (S - 2) * NDMA <= 63, "vmcnt range");
-  __shared__ u32x4_t smem[S][ROWS * CPR];
+  constexpr int OUTC = DUAL ? BN / 2 : BN;
+  constexpr bool STAGE = STG && (EPI == EPI_BF16 || EPI == EPI_F16 ||
+                                EPI == EPI_SWIGLU_BF16 || EPI == EPI_ROPE_QKV);
+  constexpr int RING = S * ROWS * CPR;                              // 16-byte entries
+  constexpr int STGN = STAGE ? (BM * (OUTC * 2 + 16) + 15) / 16 : 0;   // staging entries
+  __shared__ u32x4_t smem_all[RING > STGN ? RING : STGN];
+  auto smem = reinterpret_cast<u32x4_t(*)[ROWS * CPR]>(smem_all);
   TileInfo ti;
   int bx = blockIdx.x, by = blockIdx.y;
   if (g.xcd_remap && gridDim.z == 1 &&
@@ -515,8 +624,15 @@ gemm_dma_kernel(GemmArgs g) {
 
   GemmArgs ge = g;
   if (nsplit > 1) ge.C = static_cast<float*>(g.C) + (long)blockIdx.z * g.part_stride;
-  mfma_epilogue<EPI, FM, FN>(ge, acc, ti.row0 + wm * TM, ti.row1,
-                             ncol0 + wn * (DUAL ? TN / 2 : TN), lane);
+  if constexpr (STAGE) {   // g.stage16: launch_gemm checked the 16-byte alignment
+    barrier_lds();        // every wave is done reading the ring
+    staged_epilogue<EPI, BM, OUTC, 64 * NW, FM, FN>(
+        ge, acc, reinterpret_cast<unsigned char*>(smem_all), ti.row0, ti.row1, ncol0, wm * TM,
+        wn * (DUAL ? TN / 2 : TN), lane);
+  } else {
+    mfma_epilogue<EPI, FM, FN>(ge, acc, ti.row0 + wm * TM, ti.row1,
+                               ncol0 + wn * (DUAL ? TN / 2 : TN), lane);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int S, int BK = 64>
@@ -526,8 +642,13 @@ int launch_dma_cfg(const GemmArgs& g, Exec st) {
   const int mt = g.tiles ? g.max_tiles : (g.M + BM - 1) / BM;
   const int nsplit = g.ksplit > 1 ? g.ksplit : 1;
   const dim3 grid((g.N + bn_out - 1) / bn_out, mt, nsplit), block(64 * WM * WN);
-#define DS4G_DMA(E, F) \
-  DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, E, F, BK>), grid, block, 0, st, g)
+#define DS4G_DMA(E, F)                                                                     \
+  {                                                                                        \
+    if (g.stage16)                                                                         \
+      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, E, F, BK, true>), grid, block, 0, st, g); \
+    else                                                                                   \
+      DS4G_LAUNCH((gemm_dma_kernel<BM, BN, WM, WN, S, E, F, BK, false>), grid, block, 0, st, g); \
+  }
   if (g.f16) {   // the attention path: fp16 operands
     if (g.tiles) return -1;
     switch (g.epi) {
@@ -669,6 +790,15 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
     // byte offsets of the direct loads are 32-bit
     if ((double)g.N * (g.brep ? g.brep : g.K) * 2 >= 4294967296.0) return -1;
     if (g.brep && (g.brep % 64 || g.K % g.brep)) return -1;
+    // 16-bit outputs are stored 16 bytes at a time (staged_epilogue)
+    const bool out16 = g.epi == EPI_BF16 || g.epi == EPI_F16 || g.epi == EPI_SWIGLU_BF16 ||
+                       g.epi == EPI_ROPE_QKV;
+    auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    if (!out16) g.stage16 = 0;
+    if (g.stage16 && (g.N % 8 || g.ldc % 8 || !a16(g.C))) return -1;
+    if (g.stage16 && g.epi == EPI_ROPE_QKV &&
+        (g.rope_dh % 8 || !a16(g.rope_kc) || !a16(g.rope_vc)))
+      return -1;
     if (g.tiles) {   // the tile list was built for exactly rows_hint rows per tile
       // 64-row tiles (few rows per expert: a 2048-token prefill, batched
       // decode): 128 columns per tile, so small calls have more blocks to

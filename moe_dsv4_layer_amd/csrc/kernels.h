@@ -57,6 +57,8 @@ struct GemmArgs {
   int ksplit;
   long part_stride;
   int xcd_remap;        // MFMA: renumber tiles so each XCD runs a contiguous run
+  int stage16;          // MFMA, 16-bit outputs: store 16-byte row chunks through LDS (for
+                        // tiles that are mostly full; 16-byte aligned C, N and ldc % 8 == 0)
   // EPI_ROPE_QKV: cos / sin of pair i at row r in rope_c / rope_s [i * rope_ld + r]
   // (rope_ld a multiple of 4, >= rows); q columns [0, qd) are heads of dh,
   // then k, then v; pairs (e, e+1) with e >= dh - rd rotate
