@@ -43,9 +43,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 # 12 steps; FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0, the factors that make a
 # 1 GiB device copy read 1 GiB and write 1 GiB).  Valid only for the decode
 # sources it was measured on: any change to them reports traffic as null.
-DECODE_TRAFFIC_BYTES = 273973964
+DECODE_TRAFFIC_BYTES = 274017134
 DECODE_TRAFFIC_SOURCES = ("api.hip", "attn.hip", "decode.hip", "dev.h", "kernels.h")
-DECODE_TRAFFIC_SHA1 = "b1fae9d59b70889bd77aefe9c3f28ecaf3aaeba1"
+DECODE_TRAFFIC_SHA1 = "72dc84a50bd64bd2bb599b36c3c5665116a4a335"
 
 
 def decode_traffic():
