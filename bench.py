@@ -170,6 +170,129 @@ def measured_peaks(dev) -> dict:
     return out
 
 
+def calibration_probes(dev) -> dict:
+    """What the chip does with launches and access shapes, from the library's
+    calibration kernels (ds4g_probe_chain, ds4g_probe_read) and, for
+    comparison, the vendor GEMM behind torch.matmul.  Times are HIP events on
+    the launch stream; graph figures replay a captured graph."""
+    import numpy as np
+    import torch
+    import moe_dsv4_layer_amd as ds4g
+    st = torch.cuda.current_stream()
+
+    def timed_us(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def graph_of(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    res = {}
+    # launch cost: 64 launches per call, eager and graph-replayed
+    buf = torch.zeros(2, dtype=torch.int32, device=dev)
+    n = 64
+    launch = {}
+    for chained in (False, True):
+        for blocks in (256, 2048):
+            def call(b=blocks, c=chained):
+                ds4g.probe_chain(b, n, c, buf)
+            call()
+            eager = timed_us(call, 10) / n
+            g = graph_of(call)
+            graph = timed_us(g.replay, 20) / n
+            launch[f"{'chained' if chained else 'independent'}_{blocks}_blocks"] = {
+                "eager_us": round(eager, 2), "graph_us": round(graph, 2)}
+    res["launch_cost_per_kernel"] = launch
+
+    # HBM read rate by access shape over 1 GiB (512 blocks, 96 KB in flight each)
+    GiB = 1 << 30
+    rows = GiB // 8192
+    src = torch.ones((rows - 1) * 8320 + 8192, dtype=torch.uint8, device=dev)
+    out = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+    shapes = {}
+    for name, step_rows, stride in (("contiguous, 32 KB per step", 4, 8192),
+                                    ("128 rows x 256 B per step", 128, 8192),
+                                    ("256 rows x 128 B per step", 256, 8192),
+                                    ("256 rows x 128 B per step, row stride 8 KB + 128 B", 256,
+                                     8320)):
+        def rd(sr=step_rows, sd=stride):
+            ds4g.probe_read(src, sr, sd, GiB, 512, out)
+        rd()
+        us = timed_us(rd, 5)
+        shapes[name] = round(GiB / (us * 1e-6) / 1e12, 2)
+    res["read_tbs_by_shape_1GiB"] = shapes
+
+    # one contiguous read per launch, graph-replayed, four regions 256 MB
+    # apart rotated so the 256 MB Infinity Cache does not hold the next one
+    sizes = [8_388_608, 17_301_504, 67_108_864, 117_440_512]
+    region = 256 << 20
+    per_launch = []
+    for nbytes in sizes:
+        def four(nb=nbytes):
+            for r in range(4):
+                ds4g.probe_read(src[r * region: r * region + nb], 4, 8192, nb, 1024, out)
+        g = graph_of(lambda: [four() for _ in range(10)])
+        per_launch.append(timed_us(g.replay, 5) / 40)
+    slope, icpt = np.polyfit(np.array(sizes, dtype=np.float64), np.array(per_launch), 1)
+    res["contiguous_read_per_launch"] = {
+        "bytes": sizes, "us": [round(u, 2) for u in per_launch],
+        "fit_fixed_us": round(float(icpt), 2),
+        "fit_marginal_tbs": round(1e-6 / float(slope), 2)}
+
+    # does a read leave its bytes in the Infinity Cache for the next launch?
+    def read_at(off, nb):
+        v = src[off: off + nb]
+        return timed_us(lambda: ds4g.probe_read(v, 4, 8192, nb, 512, out), 1)
+
+    def flush():
+        ds4g.probe_read(src, 4, 8192, GiB, 512, out)
+
+    MB = 1 << 20
+    trials = []
+    for _ in range(3):
+        flush()
+        cold = read_at(0, 64 * MB)
+        again = read_at(0, 64 * MB)
+        read_at(128 * MB, 64 * MB)
+        after_other = read_at(0, 64 * MB)
+        flush()
+        cold32 = read_at(256 * MB, 32 * MB)
+        again32 = read_at(256 * MB, 32 * MB)
+        trials.append((cold, again, after_other, cold32, again32))
+    med = np.median(np.array(trials), axis=0)
+    res["reread_us"] = {"64MB_cold": round(float(med[0]), 2),
+                        "64MB_again": round(float(med[1]), 2),
+                        "64MB_after_another_64MB": round(float(med[2]), 2),
+                        "32MB_cold": round(float(med[3]), 2),
+                        "32MB_again": round(float(med[4]), 2)}
+    del src
+
+    # the vendor GEMM on two shapes (bf16, fp32 accumulate), random operands
+    vendor = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    for name, (M, N, K) in (("8192^3", (8192, 8192, 8192)),
+                            ("W_o of a 16994-token prefill", (16994, 4096, 8192))):
+        a = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+        b = torch.randn((K, N), generator=gen, device=dev).to(torch.bfloat16).contiguous()
+        torch.matmul(a, b)
+        us = timed_us(lambda: torch.matmul(a, b), 10)
+        vendor[name] = {"us": round(us, 1), "pflops": round(2.0 * M * N * K / (us * 1e-6) / 1e15, 3)}
+        del a, b
+    res["vendor_matmul_bf16"] = vendor
+    return res
+
+
 def gpu_clocks() -> dict:
     """Current clocks from rocm-smi (best effort; text as rocm-smi prints it)."""
     import subprocess
@@ -359,6 +482,9 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB on the device 5 times (calibrates the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE against a known size) and exit")
+    ap.add_argument("--probes", action="store_true",
+                    help="only run the calibration probes (launch cost, read rate by access "
+                         "shape, Infinity Cache reuse, the vendor GEMM) and print their JSON line")
     args = ap.parse_args()
     want = set(args.sections.split(","))
     if args.no_stack:
@@ -385,6 +511,10 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
                           "copies": 5}))
+        return 0
+    if args.probes:
+        print(json.dumps({"probes": calibration_probes(dev),
+                          "device": torch.cuda.get_device_name(dev)}))
         return 0
     wl = synth.WORKLOADS["layer_decode"]
     s = wl.layer

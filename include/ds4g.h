@@ -327,6 +327,31 @@ int ds4g_embed(int32_t vocab, int32_t hidden, int32_t wdtype, const void *table,
  * DS4G_ERR_INVALID_ARG for a non-positive size or NULL out. */
 int ds4g_probe_mfma(int32_t blocks, int32_t iters, float *out, void *stream);
 
+/* Calibration of the HBM read rate of an access shape.  src: device buffer
+ * of src_bytes (16-byte aligned), read as rows of row_stride bytes (>= 8192,
+ * a multiple of 16) of which the first 8192 are read.  read_bytes (a
+ * multiple of step_rows * 8192) are read as units of step_rows rows
+ * (a power of two in [4, 2048]); each unit in steps of 32 KB that take
+ * 32768 / step_rows bytes of every row of the unit, left to right (the walk
+ * of an MFMA GEMM over a weight panel; step_rows = 4 with row_stride = 8192
+ * is a contiguous stream).  `blocks` blocks of 256 threads split the units
+ * into contiguous ranges; out (device, blocks * 256 words) receives an xor of
+ * what each thread read.  Time it with events on `stream`.
+ * DS4G_ERR_INVALID_ARG for sizes outside these rules or a read that would
+ * pass src_bytes. */
+int ds4g_probe_read(const void *src, int64_t src_bytes, int32_t step_rows, int64_t row_stride,
+                    int64_t read_bytes, int32_t blocks, uint32_t *out, void *stream);
+
+/* Calibration of the cost of a launch: enqueues n_kernels launches of
+ * `blocks` blocks on `stream` (capture it in a graph to price graph
+ * dispatch).  buf: device, 2 words, ping-ponged.  chained != 0: every thread
+ * of launch i reads the word launch i - 1 wrote and one thread writes it plus
+ * one (so launch i's loads depend on launch i - 1); otherwise one thread of
+ * each launch writes 1.  DS4G_ERR_INVALID_ARG for a non-positive size or
+ * NULL buf. */
+int ds4g_probe_chain(int32_t blocks, int32_t n_kernels, int32_t chained, uint32_t *buf,
+                     void *stream);
+
 /* Static text for a ds4g_status value. */
 const char *ds4g_status_string(int status);
 

@@ -23,7 +23,7 @@ EXPORTS = ("ds4g_workspace_bytes", "ds4g_f16_images_bytes", "ds4g_make_f16_image
            "ds4g_layer_supported", "ds4g_layer_prefill",
            "ds4g_layer_prefill_trace",
            "ds4g_layer_decode", "ds4g_layer_decode_noalloc", "ds4g_layer_decode_batch",
-           "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_probe_mfma",
+           "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_probe_mfma", "ds4g_probe_read", "ds4g_probe_chain",
            "ds4g_status_string")
 
 
@@ -142,6 +142,11 @@ def _load() -> ctypes.CDLL:
                                ctypes.c_int32, P, P]
     lib.ds4g_probe_mfma.restype = ctypes.c_int
     lib.ds4g_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
+    lib.ds4g_probe_read.restype = ctypes.c_int
+    lib.ds4g_probe_read.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int32, P, P]
+    lib.ds4g_probe_chain.restype = ctypes.c_int
+    lib.ds4g_probe_chain.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P]
     lib.ds4g_status_string.restype = ctypes.c_char_p
     lib.ds4g_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -318,6 +323,23 @@ def probe_mfma(blocks: int, iters: int, out, stream=None) -> None:
     """ds4g_probe_mfma: blocks x 4 waves of iters x 8 bf16 32x32x16 MFMAs."""
     _check(lib.ds4g_probe_mfma(blocks, iters, out.data_ptr(), _stream(stream)),
            "ds4g_probe_mfma")
+
+
+def probe_read(src, step_rows: int, row_stride: int, read_bytes: int, blocks: int, out,
+               stream=None) -> None:
+    """ds4g_probe_read: read read_bytes of src (a device tensor) as units of
+    step_rows rows of row_stride bytes, in 32 KB steps; out: uint32-sized
+    device tensor of blocks * 256 elements."""
+    _check(lib.ds4g_probe_read(src.data_ptr(), src.numel() * src.element_size(), step_rows,
+                               row_stride, read_bytes, blocks, out.data_ptr(), _stream(stream)),
+           "ds4g_probe_read")
+
+
+def probe_chain(blocks: int, n_kernels: int, chained: bool, buf, stream=None) -> None:
+    """ds4g_probe_chain: n_kernels launches, each reading the previous one's
+    word when chained (buf: device tensor of at least 2 int32)."""
+    _check(lib.ds4g_probe_chain(blocks, n_kernels, int(chained), buf.data_ptr(),
+                                _stream(stream)), "ds4g_probe_chain")
 
 
 def alloc_workspace(nbytes: int, device="cuda"):

@@ -280,3 +280,28 @@ def test_decode_noalloc_rejects_before_touching_the_device():
     assert call(_cfg(), rg=ds4g.KvRing(0x1000, 0, 0x1000)) == ds4g.ERR_INVALID_ARG
     assert call(_cfg(head_dim=96)) == ds4g.ERR_UNSUPPORTED
     assert call(_cfg(hidden=16384)) == ds4g.ERR_UNSUPPORTED     # refused by the dry run
+
+
+def test_probes_reject_before_launch():
+    L = ds4g.lib
+    GiB = 1 << 30
+    src, out = 0x10000, 0x20000
+
+    def read(step_rows=128, stride=8192, nbytes=GiB, src_bytes=GiB, blocks=512, s=src, o=out):
+        return L.ds4g_probe_read(s, src_bytes, step_rows, stride, nbytes, blocks, o, None)
+    assert read(s=None) == ds4g.ERR_INVALID_ARG
+    assert read(o=None) == ds4g.ERR_INVALID_ARG
+    assert read(blocks=0) == ds4g.ERR_INVALID_ARG
+    for bad_rows in (0, 2, 3, 96, 4096):
+        assert read(step_rows=bad_rows) == ds4g.ERR_INVALID_ARG, bad_rows
+    assert read(stride=8000) == ds4g.ERR_INVALID_ARG            # narrower than a row
+    assert read(stride=8200) == ds4g.ERR_INVALID_ARG            # not a multiple of 16
+    assert read(nbytes=128 * 8192 + 16) == ds4g.ERR_INVALID_ARG  # not whole units
+    assert read(s=src + 8) == ds4g.ERR_INVALID_ARG               # misaligned
+    # the padded walk needs (rows - 1) * stride + 8192 bytes of source
+    rows = GiB // 8192
+    need = (rows - 1) * 8320 + 8192
+    assert read(stride=8320, src_bytes=need - 1) == ds4g.ERR_INVALID_ARG
+    assert L.ds4g_probe_chain(0, 4, 1, out, None) == ds4g.ERR_INVALID_ARG
+    assert L.ds4g_probe_chain(64, 0, 1, out, None) == ds4g.ERR_INVALID_ARG
+    assert L.ds4g_probe_chain(64, 4, 1, None, None) == ds4g.ERR_INVALID_ARG
