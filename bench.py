@@ -277,6 +277,17 @@ def calibration_probes(dev) -> dict:
                         "32MB_again": round(float(med[4]), 2)}
     del src
 
+    # the matrix cores on register operands: near-constant and random data
+    blocks, iters = 1024, 400
+    buf = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+    ds4g.probe_mfma(blocks, iters, buf)
+    us_c = timed_us(lambda: ds4g.probe_mfma(blocks, iters, buf), 3)
+    ds4g.probe_mfma_random(blocks, iters // 8, 12345, buf)
+    us_r = timed_us(lambda: ds4g.probe_mfma_random(blocks, iters // 8, 12345, buf), 3)
+    fl = blocks * 4 * iters * 8 * 2.0 * 32 * 32 * 16
+    res["mfma_loop_bf16_pflops"] = {"near_constant_operands": round(fl / (us_c * 1e-6) / 1e15, 3),
+                                    "random_operands": round(fl / (us_r * 1e-6) / 1e15, 3)}
+
     # the vendor GEMM on two shapes (bf16, fp32 accumulate), random operands
     vendor = {}
     gen = torch.Generator(device=dev)

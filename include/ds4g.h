@@ -327,6 +327,15 @@ int ds4g_embed(int32_t vocab, int32_t hidden, int32_t wdtype, const void *table,
  * DS4G_ERR_INVALID_ARG for a non-positive size or NULL out. */
 int ds4g_probe_mfma(int32_t blocks, int32_t iters, float *out, void *stream);
 
+/* ds4g_probe_mfma on random operands: each wave draws 8 A and 8 B operand
+ * sets of bf16 values with random signs and mantissas (|v| in [0.5, 1)) from
+ * `seed` and its position, and every one of the iters x 64 MFMAs per wave
+ * pairs a different A and B set, so the matrix cores switch as in a GEMM on
+ * random data.  blocks x 4 waves; out: device, blocks*4 floats.  Errors as
+ * for ds4g_probe_mfma. */
+int ds4g_probe_mfma_random(int32_t blocks, int32_t iters, uint32_t seed, float *out,
+                           void *stream);
+
 /* Calibration of the HBM read rate of an access shape.  src: device buffer
  * of src_bytes (16-byte aligned), read as rows of row_stride bytes (>= 8192,
  * a multiple of 16) of which the first 8192 are read.  read_bytes (a

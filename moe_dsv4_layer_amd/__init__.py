@@ -23,7 +23,7 @@ EXPORTS = ("ds4g_workspace_bytes", "ds4g_f16_images_bytes", "ds4g_make_f16_image
            "ds4g_layer_supported", "ds4g_layer_prefill",
            "ds4g_layer_prefill_trace",
            "ds4g_layer_decode", "ds4g_layer_decode_noalloc", "ds4g_layer_decode_batch",
-           "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_probe_mfma", "ds4g_probe_read", "ds4g_probe_chain",
+           "ds4g_lmhead_sample", "ds4g_lmhead_sample_ex", "ds4g_embed", "ds4g_probe_mfma", "ds4g_probe_mfma_random", "ds4g_probe_read", "ds4g_probe_chain",
            "ds4g_status_string")
 
 
@@ -142,6 +142,8 @@ def _load() -> ctypes.CDLL:
                                ctypes.c_int32, P, P]
     lib.ds4g_probe_mfma.restype = ctypes.c_int
     lib.ds4g_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
+    lib.ds4g_probe_mfma_random.restype = ctypes.c_int
+    lib.ds4g_probe_mfma_random.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, P, P]
     lib.ds4g_probe_read.restype = ctypes.c_int
     lib.ds4g_probe_read.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
                                     ctypes.c_int64, ctypes.c_int32, P, P]
@@ -323,6 +325,13 @@ def probe_mfma(blocks: int, iters: int, out, stream=None) -> None:
     """ds4g_probe_mfma: blocks x 4 waves of iters x 8 bf16 32x32x16 MFMAs."""
     _check(lib.ds4g_probe_mfma(blocks, iters, out.data_ptr(), _stream(stream)),
            "ds4g_probe_mfma")
+
+
+def probe_mfma_random(blocks: int, iters: int, seed: int, out, stream=None) -> None:
+    """ds4g_probe_mfma_random: blocks x 4 waves of iters x 64 bf16 32x32x16
+    MFMAs on random operands."""
+    _check(lib.ds4g_probe_mfma_random(blocks, iters, seed, out.data_ptr(), _stream(stream)),
+           "ds4g_probe_mfma_random")
 
 
 def probe_read(src, step_rows: int, row_stride: int, read_bytes: int, blocks: int, out,

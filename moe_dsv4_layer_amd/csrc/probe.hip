@@ -5,6 +5,9 @@
 //    32x32x16 accumulators in registers and issues `iters` rounds of 8 MFMAs
 //    on operands that never leave registers; one store per wave keeps the
 //    work alive.  Dense flops per MFMA: 2 * 32 * 32 * 16.
+//  * mfma_random_kernel: the same loop on operands with random signs and
+//    mantissas (exponent fixed, |v| in [0.5, 1)): 8 operand sets per wave
+//    rotate so every MFMA sees new bits, as a GEMM on random data does.
 //  * read_probe_kernel: the HBM read rate of a given access shape (a
 //    contiguous stream, or the walk of an MFMA GEMM over a weight panel).
 //  * chain_probe_kernel: the cost of one more launch in a stream or graph,
@@ -35,6 +38,47 @@ __global__ void __launch_bounds__(256) mfma_loop_kernel(int iters, float* out) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
   }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += acc[j][lane & 15];
+  if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+}
+
+__device__ __forceinline__ unsigned probe_mix(unsigned x) {   // xorshift32
+  x ^= x << 13;
+  x ^= x >> 17;
+  x ^= x << 5;
+  return x;
+}
+
+__global__ void __launch_bounds__(256) mfma_random_kernel(int iters, unsigned seed, float* out) {
+  probe_f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+  unsigned x = probe_mix(seed ^ (blockIdx.x * 256u + threadIdx.x) * 2654435761u) | 1u;
+  u32x4_t a[8], b[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x = probe_mix(x);
+      a[j][e] = (x & 0x807F807Fu) | 0x3F003F00u;   // two bf16: random sign, mantissa
+      x = probe_mix(x);
+      b[j][e] = (x & 0x807F807Fu) | 0x3F003F00u;
+    }
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(probe_bf16x8, a[(j + r) & 7]),
+            __builtin_bit_cast(probe_bf16x8, b[(j + 3 * r) & 7]), acc[j], 0, 0, 0);
+  }
+  const int lane = threadIdx.x & 63;
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) s += acc[j][lane & 15];
@@ -120,6 +164,15 @@ extern "C" int ds4g_probe_chain(int32_t blocks, int32_t n_kernels, int32_t chain
   for (int i = 0; i < n_kernels; ++i)
     hipLaunchKernelGGL(ds4g::chain_probe_kernel, dim3(blocks), dim3(256), 0,
                        (hipStream_t)stream, w + (i & 1), w + ((i + 1) & 1), (int)chained);
+  return hipGetLastError() == hipSuccess ? DS4G_OK : DS4G_ERR_HIP;
+}
+
+extern "C" int ds4g_probe_mfma_random(int32_t blocks, int32_t iters, uint32_t seed, float* out,
+                                      void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out) return DS4G_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(ds4g::mfma_random_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     iters, seed, out);
   return hipGetLastError() == hipSuccess ? DS4G_OK : DS4G_ERR_HIP;
 }
 

@@ -305,3 +305,6 @@ def test_probes_reject_before_launch():
     assert L.ds4g_probe_chain(0, 4, 1, out, None) == ds4g.ERR_INVALID_ARG
     assert L.ds4g_probe_chain(64, 0, 1, out, None) == ds4g.ERR_INVALID_ARG
     assert L.ds4g_probe_chain(64, 4, 1, None, None) == ds4g.ERR_INVALID_ARG
+    assert L.ds4g_probe_mfma_random(0, 4, 1, out, None) == ds4g.ERR_INVALID_ARG
+    assert L.ds4g_probe_mfma_random(64, 0, 1, out, None) == ds4g.ERR_INVALID_ARG
+    assert L.ds4g_probe_mfma_random(64, 4, 1, None, None) == ds4g.ERR_INVALID_ARG
