@@ -586,22 +586,50 @@ gemm_dma_kernel(GemmArgs g) {
   const int live = __builtin_amdgcn_readfirstlane(min(FM, max(0, (vrows - wm * TM + 31) >> 5)));
   auto run = [&](auto live_c) {
     constexpr int LIVE = decltype(live_c)::value;
+    // The fragments of k step ks + 1 are read from LDS while the MFMAs of
+    // step ks run (two fragment buffers), one read issued after each MFMA:
+    // left to itself the scheduler put each read right before its first
+    // use and the MFMAs waited on LDS latency.  Each accumulator still sums
+    // its k steps in order, so the result does not change.
     auto compute = [&](int st) {
       const u32x4_t* As = &smem[st][0];
       const u32x4_t* Bs = &smem[st][BM * CPR];
+      u32x4_t af[2][LIVE > 0 ? LIVE : 1], bfr[2][FN];
+      auto load = [&](int ks, int b) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t af[LIVE > 0 ? LIVE : 1], bfr[FN];
-#pragma unroll
-        for (int i = 0; i < LIVE; ++i) af[i] = As[swz<CPR>(wm * TM + i * 32 + lr, ks * 2 + lg)];
+        for (int i = 0; i < LIVE; ++i) af[b][i] = As[swz<CPR>(wm * TM + i * 32 + lr, ks * 2 + lg)];
         if (LIVE > 0) {
 #pragma unroll
-          for (int j = 0; j < FN; ++j) bfr[j] = Bs[swz<CPR>(wn * TN + j * 32 + lr, ks * 2 + lg)];
+          for (int j = 0; j < FN; ++j) bfr[b][j] = Bs[swz<CPR>(wn * TN + j * 32 + lr, ks * 2 + lg)];
         }
+      };
+      load(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) load(ks + 1, (ks + 1) & 1);
 #pragma unroll
         for (int i = 0; i < LIVE; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma16<F16>(af[i], bfr[j], acc[i][j]);
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = mfma16<F16>(af[ks & 1][i], bfr[ks & 1][j], acc[i][j]);
+      }
+      if constexpr (LIVE > 0) {   // the order the scheduler keeps (masks: 0x100 LDS read, 0x008 MFMA)
+        constexpr int NL = LIVE + FN, NM = LIVE * FN, NI = NL < NM ? NL : NM;
+        __builtin_amdgcn_sched_group_barrier(0x100, NL, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + 1 < KS) {
+#pragma unroll
+            for (int t = 0; t < NI; ++t) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if (NL > NM) __builtin_amdgcn_sched_group_barrier(0x100, NL - NM, 0);
+            if (NM > NL) __builtin_amdgcn_sched_group_barrier(0x008, NM - NL, 0);
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+          }
+        }
       }
     };
 #pragma unroll
