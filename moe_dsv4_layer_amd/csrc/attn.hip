@@ -613,19 +613,31 @@ attn_prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             *reinterpret_cast<const attn_f16x8*>(&v), pf[st], oacc[dt], 0, 0, 0);
       }
     }
-    // lane holds dims dt*32 + 8g + 4hf + (0..3) of its column
-    if (col_ok) {
+    // lane holds dims dt*32 + 8g + 4hf + (0..3) of its column;
+    // lane ^ 32 holds the other 4 dims of each 8-dim group: swap halves so
+    // that every lane stores whole 16-byte groups (two per output tile)
+    {
       const float inv = 1.f / sm;
-      uint16_t* orow = o + (t * H + head) * DH + 4 * hf;
 #pragma unroll
-      for (int dt = 0; dt < DTILE; ++dt)
+      for (int dt = 0; dt < DTILE; ++dt) {
+        unsigned pk[4][2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          uint2 w;
-          w.x = pack_f16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv);
-          w.y = pack_f16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g) = w;
+          pk[g][0] = pack_f16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv);
+          pk[g][1] = pack_f16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
         }
+        const int ga = hf ? 0 : 1, gb = hf ? 2 : 3;
+        const unsigned r0 = __shfl_xor((int)pk[ga][0], 32, kWave), r1 = __shfl_xor((int)pk[ga][1], 32, kWave);
+        const unsigned r2 = __shfl_xor((int)pk[gb][0], 32, kWave), r3 = __shfl_xor((int)pk[gb][1], 32, kWave);
+        if (col_ok) {
+          uint16_t* orow = o + (t * H + head) * DH;
+          const int g0 = hf ? 1 : 0, g1 = hf ? 3 : 2;
+          const u32x4_t w0 = hf ? u32x4_t{r0, r1, pk[1][0], pk[1][1]} : u32x4_t{pk[0][0], pk[0][1], r0, r1};
+          const u32x4_t w1 = hf ? u32x4_t{r2, r3, pk[3][0], pk[3][1]} : u32x4_t{pk[2][0], pk[2][1], r2, r3};
+          *reinterpret_cast<u32x4_t*>(orow + dt * 32 + 8 * g0) = w0;
+          *reinterpret_cast<u32x4_t*>(orow + dt * 32 + 8 * g1) = w1;
+        }
+      }
     }
     }
 #pragma unroll

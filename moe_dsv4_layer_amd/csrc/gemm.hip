@@ -34,6 +34,10 @@
 #endif
 // LDS stages and k-step width of the 256x256 tiles (2 x 64 or 4 x 32: the
 // same 128 KB of LDS)
+// 128 x 256 tiles for an output of 129..256 columns over many rows (1: on)
+#ifndef DS4G_WIDE_ROUTER
+#define DS4G_WIDE_ROUTER 1
+#endif
 #ifndef DS4G_BIG_S
 #define DS4G_BIG_S 2
 #endif
@@ -864,6 +868,12 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
       return launch_dma_cfg<256, 256, DS4G_BIG_WM, DS4G_BIG_WN, DS4G_BIG_S, DS4G_BIG_BK>(g, st);
     }
     if (g.M <= 64) return launch_dma_cfg<64, 256, 1, 4, 3>(g, st);
+    // Output 129..256 columns wide (the router's experts) over many rows: one
+    // 128 x 256 tile spans every column, so each row block of A is read once
+    // rather than by two blocks on different XCDs (16 994 rows: 200 -> 162 us
+    // in isolation).  With few rows the 128 x 128 grid's extra blocks win.
+    if (DS4G_WIDE_ROUTER && nout > 128 && nout <= 256 && (g.M + 127) / 128 * nsplit >= 512)
+      return launch_dma_cfg<128, 256, 2, 4, 3>(g, st);
     const long blocks = ((g.M + 127) / 128) * ((nout + 127) / 128) * nsplit;
     // one block per CU either way: spend the LDS on a deeper pipeline
     if (blocks <= 256) return launch_dma_cfg<128, 128, 2, 2, 3>(g, st);
