@@ -786,16 +786,21 @@ int ds4g_lmhead_sample_ex(int32_t hidden, int32_t vocab, int32_t wdtype, const v
   if (ws_bytes < sample_ws_bytes(vocab)) return DS4G_ERR_WORKSPACE;
   return dry_then_run((hipStream_t)stream, [&](Exec st) {
   int rc = 0;
+  // the GEMV also leaves its blocks' largest logits for the sampler and
+  // clears the sampler's histogram and arrival count
+  const SampleScratch sc = sample_scratch(ws, vocab);
   {
     GemvArgs g{};
     g.W = w_lm; g.N = vocab; g.K = hidden; g.x = x; g.gamma = final_norm; g.eps = rms_eps;
     g.out = logits;
+    g.blockmax = sc.bmax; g.blockarg = sc.barg; g.zero = sc.zero; g.zero_words = sc.zero_words;
     rc |= (wdtype == DS4G_BF16) ? launch_gemv<uint16_t>(g, st) : launch_gemv<float>(g, st);
   }
   SampleArgs sa{};
   sa.logits = logits; sa.V = vocab; sa.temperature = temperature; sa.top_p = top_p;
   sa.min_p = min_p; sa.temperature_dev = params->temperature_dev;
   sa.rng = rng_state; sa.token = token; sa.ws = ws;
+  sa.nbm = gemv_grid(vocab, hidden);
   rc |= launch_sample(sa, st);
   if (embed_table)
     rc |= launch_embed(embed_table, wdtype == DS4G_BF16, token, 1, vocab, hidden, x_next, st);

@@ -70,6 +70,9 @@ gemv_kernel(GemvArgs a) {
   };
   int r0 = blockIdx.x * rows_per_block;
   if (r0 < N) load_rows(r0);
+  if (a.zero)
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < a.zero_words; i += gridDim.x * 256)
+      a.zero[i] = 0u;
 
   // x slice in registers, optionally normalised
   float xv[CPL][8];
@@ -117,6 +120,10 @@ gemv_kernel(GemvArgs a) {
     }
   }
 
+  // largest output this thread wrote and its row (rows ascend, so the first
+  // of equal values is the lowest row)
+  float bm = -INFINITY;
+  int bi = 0x7fffffff;
   for (; r0 < N; r0 += stride) {
     const int rbase = r0 + rgroup * RB;
     // the residual of the rows this thread writes goes out with the weights,
@@ -146,7 +153,9 @@ gemv_kernel(GemvArgs a) {
         float v = acc[0];
 #pragma unroll
         for (int r = 1; r < RB; ++r) if (lane == r) v = acc[r];
-        a.out[rbase + lane] = a.accumulate ? res + v : v;
+        v = a.accumulate ? res + v : v;
+        a.out[rbase + lane] = v;
+        if (v > bm) { bm = v; bi = rbase + lane; }
       }
     } else {
       __syncthreads();
@@ -159,31 +168,61 @@ gemv_kernel(GemvArgs a) {
         float v = 0.f;
 #pragma unroll
         for (int p = 0; p < KSPLIT; ++p) v += red[rgroup * KSPLIT + p][lane];
-        a.out[rbase + lane] = a.accumulate ? res + v : v;
+        v = a.accumulate ? res + v : v;
+        a.out[rbase + lane] = v;
+        if (v > bm) { bm = v; bi = rbase + lane; }
       }
     }
   }
+  if (a.blockmax) {
+    __shared__ float wm[4];
+    __shared__ int wi[4];
+    wave_argmax(bm, bi);
+    if (lane == 0) { wm[wid] = bm; wi[wid] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int k = 1; k < 4; ++k)
+        if (wm[k] > bm || (wm[k] == bm && wi[k] < bi)) { bm = wm[k]; bi = wi[k]; }
+      a.blockmax[blockIdx.x] = bm;
+      a.blockarg[blockIdx.x] = bi;
+    }
+  }
+}
 
+// The GEMV instance for K: (KSPLIT, CPL, RB) by the number of 8-element
+// chunks of a row.
+#define DS4G_GEMV_SHAPES(X)                                          \
+  if (nchunk <= 64) X(1, 1, 2)          /* K <= 512 */               \
+  if (nchunk <= 128) X(1, 2, 2)         /* K <= 1024 */              \
+  if (nchunk <= 256) X(4, 1, 2)         /* K <= 2048 */              \
+  if (nchunk <= 512) X(4, 2, 2)         /* K <= 4096 */              \
+  if (nchunk <= 1024) X(4, 4, DS4G_GEMV_RB_K8K)   /* K <= 8192 */    \
+  if (nchunk <= 2048) X(4, 8, 1)        /* K <= 16384 */
+#define DS4G_GEMV_GRID(KS, R)                                        \
+  const int rpb = R * (4 / KS);                                      \
+  int grid = (N + rpb - 1) / rpb;                                    \
+  if (grid > DS4G_GEMV_GRID_MAX) grid = DS4G_GEMV_GRID_MAX;
+
+int gemv_grid(int N, int K) {
+  const int nchunk = K / 8;
+#define DS4G_GEMV(KS, C, R) { DS4G_GEMV_GRID(KS, R) return grid; }
+  DS4G_GEMV_SHAPES(DS4G_GEMV)
+#undef DS4G_GEMV
+  return 0;
 }
 
 template <typename WT>
 int launch_gemv(const GemvArgs& a, Exec st) {
   const int nchunk = a.K / 8;
   const int N = a.N;
-#define DS4G_GEMV(KS, C, R)                                                            \
-  {                                                                                    \
-    const int rpb = R * (4 / KS);                                                      \
-    int grid = (N + rpb - 1) / rpb;                                                    \
-    if (grid > DS4G_GEMV_GRID_MAX) grid = DS4G_GEMV_GRID_MAX;                          \
+#define DS4G_GEMV(KS, C, R)                                                    \
+  {                                                                            \
+    DS4G_GEMV_GRID(KS, R)                                                      \
     DS4G_LAUNCH((gemv_kernel<WT, KS, C, R>), dim3(grid), dim3(256), 0, st, a); \
-    return 0;                                                                          \
+    return 0;                                                                  \
   }
-  if (nchunk <= 64) DS4G_GEMV(1, 1, 2)          // K <= 512
-  if (nchunk <= 128) DS4G_GEMV(1, 2, 2)         // K <= 1024
-  if (nchunk <= 256) DS4G_GEMV(4, 1, 2)         // K <= 2048
-  if (nchunk <= 512) DS4G_GEMV(4, 2, 2)         // K <= 4096
-  if (nchunk <= 1024) DS4G_GEMV(4, 4, DS4G_GEMV_RB_K8K)   // K <= 8192
-  if (nchunk <= 2048) DS4G_GEMV(4, 8, 1)        // K <= 16384
+  DS4G_GEMV_SHAPES(DS4G_GEMV)
 #undef DS4G_GEMV
   return -1;
 }

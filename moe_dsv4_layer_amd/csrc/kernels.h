@@ -96,9 +96,19 @@ struct GemvArgs {
   float* out;
   int accumulate;
   float* router_in;     // optional copy of xs (block 0)
+  // optional (the lm_head launch feeds the sampler with them): per block,
+  // the largest output it wrote and its lowest row (INT_MAX when every
+  // output was NaN or -inf), one entry per block of gemv_grid(N, K); and
+  // zero_words 32-bit words at zero to clear
+  float* blockmax;
+  int* blockarg;
+  uint32_t* zero;
+  int zero_words;
 };
 template <typename WT>
 int launch_gemv(const GemvArgs& a, Exec st);
+// blocks of the launch_gemv grid for N rows of K (0 when K is too long)
+int gemv_grid(int N, int K);
 
 // out[m, n] = sum_k W[n, k] X[m, k] for the M <= 8 rows of a batched decode
 // call: W [N, K] bf16 (row stride K), X [M, K] bf16 or fp16 (x_f16; row
@@ -212,8 +222,18 @@ struct SampleArgs {
   uint64_t* rng;
   int* token;
   void* ws;             // sampler workspace
+  int nbm;              // blocks of the lm_head GEMV that wrote the maxima
 };
 size_t sample_ws_bytes(int V);
+// What the lm_head GEMV writes for the sampler inside its workspace: the
+// words to clear and the per-block maxima (GemvArgs::zero / blockmax).
+struct SampleScratch {
+  uint32_t* zero;
+  int zero_words;
+  float* bmax;
+  int* barg;
+};
+SampleScratch sample_scratch(void* ws, int V);
 int launch_embed(const void* table, int wdtype_bf16, const int* ids, int T, int vocab, int hidden,
                  float* x, Exec st);
 int launch_sample(const SampleArgs& s, Exec st);

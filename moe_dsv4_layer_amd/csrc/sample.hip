@@ -10,249 +10,141 @@
 // the low 16 bits of the crossing bucket -- with bucket masses kept as 64-bit
 // fixed-point integers (q * 2^45), so every sum is exact and independent of
 // the order atomics land in.  Equal weights at the cut are kept in index
-// order.  The roulette is a two-level prefix sum (1024-entry segments, then
+// order.  The roulette is a two-level prefix sum (4096-entry segments, then
 // the entries of one segment).  Every step is deterministic.
+//
+// Launches.  The lm_head GEMV before the sampler leaves, per block, its
+// largest logit and that logit's lowest row, and clears the level-1 histogram.  Then
+// one launch per grid-wide dependency: (1) weights and the level-1 histogram
+// (every block reduces the GEMV's maxima to the global maximum itself);
+// (2) the level-2 histogram of the crossing level-1 bucket (every block finds
+// that bucket itself from the level-1 histogram); (3) per segment, the mass
+// and counts above and at the exact cut (every block finds the cut itself
+// from the level-2 histogram); (4) one block: the draw, the segment and the
+// entry.  A decision that every block needs is recomputed by every block from
+// a few KB in L2 rather than handed over through memory: on this chip a
+// grid-wide hand-off inside a launch (device-scope release, arrival count,
+// acquire) costs several times the 1.7 us of a launch boundary in a graph.
 #include "dev.h"
 #include "kernels.h"
 
 namespace ds4g {
 
 namespace {
-constexpr int SEG = 1024;          // entries per segment / per block
-constexpr int NB1 = 16384;         // level-1 buckets (q <= 1 => key1 <= 0x3F80)
-constexpr int NB2 = 65536;         // level-2 buckets
+constexpr int SB = 1024;           // threads per sampler block
+constexpr int SEG = 4096;          // entries per block and per roulette segment (4 per thread)
+constexpr int NBM = 2048;          // lm_head GEMV blocks at most (block maxima)
+constexpr int NB2 = 65536;         // level-2 buckets (low 16 bits)
+constexpr int NG2 = NB2 / 1024;    // level-2 groups of 1024 buckets
 constexpr double FX = 35184372088832.0;   // 2^45
-// level-1 keys below KLO (q < 2^-45, exponent field < 82) have no fixed-point
-// mass: fx(q) = 0 there, so their histogram entries stay zero
+// level-1 keys (top 16 bits of q) below KLO (q < 2^-45, exponent field < 82)
+// have no fixed-point mass: fx(q) = 0 there, so they need no bucket
 constexpr int KLO = 82 << 7;
 constexpr int NKEY = 0x3F80 + 1 - KLO;   // keys KLO..0x3F80 (q <= 1)
-constexpr int QSEGS = 4;                 // segments per samp_q block
+constexpr int MAX_SEGS = (1 << 18) / SEG;   // V <= 2^18: one pick thread per segment
 
 __device__ __forceinline__ uint64_t fx(float q) { return (uint64_t)((double)q * FX); }
 
+// Decisions the last kernels share (written by block 0 of the kernel that
+// makes them, read by later launches).
 struct SampState {
-  float M;              // max logit
-  uint32_t b1;          // level-1 crossing bucket
-  unsigned long long above1;   // mass of buckets above b1
-  double target;        // top_p * total mass
-  unsigned long long total;
-  uint32_t vstar;       // bits of the cut weight q*
-  int m;                // equal-to-q* entries kept (in index order)
-  unsigned long long above; // mass strictly above q*
-  double u;             // the uniform draw; r = u * (kept mass) is formed in S7
-  int all;              // top_p >= 1: keep everything
+  uint32_t b1;               // level-1 crossing key (q bits >> 16)
+  int found;                 // the level-1 crossing exists (some mass)
+  unsigned long long above1; // mass of keys above b1
+  double target;             // top_p * total mass (at least 0.5)
+  uint32_t vstar;            // bits of the cut weight q*
+  int m;                     // entries equal to q* that are kept (index order)
 };
 
 struct SampWs {
-  float* bmax; int* barg; float* q;
-  unsigned long long* h1; unsigned long long* h2; unsigned int* c2;
-  unsigned long long* g2;   // level-2 mass per group of 1024 descending positions
-  unsigned long long* seg_gt; int* seg_gtn; int* seg_tie;
+  unsigned long long* h1;   // [NKEY] level-1 mass per key (cleared by the lm_head launch)
+  unsigned long long* h2;   // [NB2] level-2 mass per bucket    } cleared by
+  unsigned int* c2;         // [NB2] level-2 entries per bucket } the weight
+  unsigned long long* g2;   // [NG2] level-2 mass per group     } launch
+  float* bmax;              // [NBM] per lm_head block: largest logit
+  int* barg;                // [NBM] and its lowest row
+  float* q;                 // [V] weights
+  unsigned long long* seg_gt; int* seg_gtn; int* seg_tie;   // per segment
   SampState* st;
 };
 
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// h1, h2, c2 and g2, contiguous from the start of the workspace
+constexpr size_t kH2Off = align256((size_t)NKEY * 8);
+constexpr size_t kC2Off = kH2Off + (size_t)NB2 * 8;
+constexpr size_t kG2Off = kC2Off + (size_t)NB2 * 4;
+constexpr size_t kZeroBytes = kG2Off + (size_t)NG2 * 8;
 
-__host__ __device__ inline SampWs carve(void* base, int V) {
-  const int nb = (V + SEG - 1) / SEG;
+__host__ __device__ inline SampWs carve(void* base, int V, size_t* total = nullptr) {
+  const int ns = (V + SEG - 1) / SEG;
   char* p = static_cast<char*>(base);
   SampWs w;
-  size_t o = 0;
-  w.bmax = (float*)(p + o); o = align256(o + nb * sizeof(float));
-  w.barg = (int*)(p + o); o = align256(o + nb * sizeof(int));
+  w.h1 = (unsigned long long*)p;
+  w.h2 = (unsigned long long*)(p + kH2Off);
+  w.c2 = (unsigned int*)(p + kC2Off);
+  w.g2 = (unsigned long long*)(p + kG2Off);
+  size_t o = align256(kZeroBytes);
+  w.bmax = (float*)(p + o); o = align256(o + NBM * sizeof(float));
+  w.barg = (int*)(p + o); o = align256(o + NBM * sizeof(int));
   w.q = (float*)(p + o); o = align256(o + (size_t)V * sizeof(float));
-  w.h1 = (unsigned long long*)(p + o); o = align256(o + NB1 * 8);
-  w.h2 = (unsigned long long*)(p + o); o = align256(o + NB2 * 8);
-  w.c2 = (unsigned int*)(p + o); o = align256(o + NB2 * 4);
-  w.g2 = (unsigned long long*)(p + o); o = align256(o + (NB2 / 1024) * 8);
-  w.seg_gt = (unsigned long long*)(p + o); o = align256(o + nb * 8);
-  w.seg_gtn = (int*)(p + o); o = align256(o + nb * 4);
-  w.seg_tie = (int*)(p + o); o = align256(o + nb * 4);
+  w.seg_gt = (unsigned long long*)(p + o); o = align256(o + ns * 8);
+  w.seg_gtn = (int*)(p + o); o = align256(o + ns * 4);
+  w.seg_tie = (int*)(p + o); o = align256(o + ns * 4);
   w.st = (SampState*)(p + o); o = align256(o + sizeof(SampState));
+  if (total) *total = o;
   return w;
 }
-size_t carve_bytes(int V) {
-  const int nb = (V + SEG - 1) / SEG;
-  size_t o = 0;
-  o = align256(o + nb * sizeof(float));
-  o = align256(o + nb * sizeof(int));
-  o = align256(o + (size_t)V * sizeof(float));
-  o = align256(o + NB1 * 8);
-  o = align256(o + NB2 * 8);
-  o = align256(o + NB2 * 4);
-  o = align256(o + (NB2 / 1024) * 8);
-  o = align256(o + nb * 8);
-  o = align256(o + nb * 4);
-  o = align256(o + nb * 4);
-  o = align256(o + sizeof(SampState));
-  return o;
-}
 
-// block-wide inclusive scan of one u64 per thread (blockDim 1024)
-__device__ unsigned long long block_incl_scan_u64(unsigned long long v, unsigned long long* red) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+// inclusive scans of one value per lane / per thread (blockDim SB; red holds
+// one value per wave)
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const unsigned long long y = __shfl_up(v, o, 64);
     if (lane >= o) v += y;
   }
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan_int(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+__device__ unsigned long long block_incl_scan_u64(unsigned long long v, unsigned long long* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_incl_scan_u64(v);
   __syncthreads();
   if (lane == 63) red[wid] = v;
   __syncthreads();
   unsigned long long base = 0;
   for (int w = 0; w < wid; ++w) base += red[w];
-  (void)nw;
   __syncthreads();
   return v + base;
 }
-}  // namespace
-
-size_t sample_ws_bytes(int V) { return carve_bytes(V); }
-
-// S1: per-segment max and its first index; clear the histograms.
-__global__ void __launch_bounds__(256)
-samp_max_kernel(const float* __restrict__ logits, int V, SampWs w) {
-  const int nb = gridDim.x;
+__device__ int block_incl_scan_int(int v, int* red) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  __shared__ float bv[4];
-  __shared__ int bi[4];
-  float m = -INFINITY;
-  int mi = blockIdx.x * SEG;   // a segment of NaN / -inf logits still names a token
-  for (int i = blockIdx.x * SEG + threadIdx.x; i < min(V, (blockIdx.x + 1) * SEG); i += 256) {
-    const float l = logits[i];
-    if (l > m) { m = l; mi = i; }
-  }
-  wave_argmax(m, mi);
-  if (lane == 0) { bv[wid] = m; bi[wid] = mi; }
+  v = wave_incl_scan_int(v);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int k = 1; k < 4; ++k)
-      if (bv[k] > m || (bv[k] == m && bi[k] < mi)) { m = bv[k]; mi = bi[k]; }
-    w.bmax[blockIdx.x] = m;
-    w.barg[blockIdx.x] = mi;
-  }
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < NB1; i += nb * 256) w.h1[i] = 0;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < NB2; i += nb * 256) { w.h2[i] = 0; w.c2[i] = 0; }
-}
-
-// The temperature of a call: a host value, or one read from device memory
-// each time (tdev), so that a captured graph can switch between sampling and
-// argmax without being captured again.
-__device__ __forceinline__ bool sampling(float temperature, const float* tdev) {
-  const float t = tdev ? *tdev : temperature;
-  return t > 0.f;
-}
-
-// argmax over the segment results (temperature <= 0)
-__global__ void __launch_bounds__(64)
-samp_argmax_kernel(int nb, SampWs w, int* token, float temperature, const float* tdev) {
-  if (sampling(temperature, tdev)) return;
-  float m = -INFINITY;
-  int mi = 0x7fffffff;
-  for (int b = threadIdx.x; b < nb; b += 64) {
-    const float v = w.bmax[b];
-    const int i = w.barg[b];
-    if (v > m || (v == m && i < mi)) { m = v; mi = i; }
-  }
-  wave_argmax(m, mi);
-  if (threadIdx.x == 0) *token = mi;
-}
-
-// the largest logit, from the segment maxima (block-wide: every thread;
-// red holds one float per wave)
-__device__ __forceinline__ float global_max(const SampWs& w, int nb, float* red) {
-  float m = -INFINITY;
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) m = fmaxf(m, w.bmax[b]);
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  if (lane == 63) red[wid] = v;
   __syncthreads();
-  m = red[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = fmaxf(m, red[i]);
-  return m;
-}
-
-// S2: q = exp((l - M) / T); level-1 histogram of fixed-point mass.  A block
-// of 1024 takes QSEGS segments and sums their masses per key in LDS first, so
-// that equal keys (a narrow logit spread puts thousands of weights in one
-// key) cost one global atomic per block instead of one per entry.
-__global__ void __launch_bounds__(1024)
-samp_q_kernel(const float* __restrict__ logits, int V, int nb, float temperature,
-              const float* tdev, SampWs w) {
-  if (!sampling(temperature, tdev)) return;
-  if (tdev) temperature = *tdev;
-  __shared__ unsigned long long hist[NKEY];
-  __shared__ float red[16];
-  for (int k = threadIdx.x; k < NKEY; k += blockDim.x) hist[k] = 0;
-  const float M = global_max(w, nb, red);   // ends in a barrier: hist is clear
-  if (blockIdx.x == 0 && threadIdx.x == 0) w.st->M = M;
-  const int lo = blockIdx.x * QSEGS * SEG, hi = min(V, lo + QSEGS * SEG);
-  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
-    float q = expf((logits[i] - M) / temperature);
-    q = (q == q) ? fminf(q, 1.f) : 0.f;   // a NaN logit weighs nothing; keys stay <= 0x3F80
-    w.q[i] = q;
-    const int key = (int)(__float_as_uint(q) >> 16) - KLO;
-    if (key >= 0) atomicAdd(&hist[key], (unsigned long long)fx(q));
-  }
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += red[w];
   __syncthreads();
-  for (int k = threadIdx.x; k < NKEY; k += blockDim.x) {
-    const unsigned long long v = hist[k];
-    if (v) atomicAdd(&w.h1[KLO + k], v);
-  }
+  return v + base;
 }
 
-// S3 (one block of 1024): total mass, target, and the level-1 bucket where the
-// descending cumulative mass reaches the target.
-__global__ void __launch_bounds__(1024)
-samp_level1_kernel(float top_p, SampWs w, float temperature, const float* tdev) {
-  if (!sampling(temperature, tdev)) return;
-  __shared__ unsigned long long red[16];
-  constexpr int PER = NB1 / 1024;
-  // position i in descending bucket order: bucket NB1-1-i
-  unsigned long long loc[PER];
-  unsigned long long s = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    loc[j] = w.h1[NB1 - 1 - (threadIdx.x * PER + j)];
-    s += loc[j];
-  }
-  const unsigned long long inc = block_incl_scan_u64(s, red);
-  __shared__ unsigned long long tot;
-  if (threadIdx.x == 1023) tot = inc;
-  __syncthreads();
-  double target = (double)top_p * (double)tot;
-  if (target < 0.5) target = 0.5;   // keep at least one token
-  const bool all = top_p >= 1.0f;
-  if (threadIdx.x == 0) {
-    w.st->total = tot;
-    w.st->target = target;
-    w.st->all = all ? 1 : 0;
-  }
-  if (all) return;
-  unsigned long long run = inc - s;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const unsigned long long nxt = run + loc[j];
-    if ((double)run < target && (double)nxt >= target) {
-      w.st->b1 = NB1 - 1 - (threadIdx.x * PER + j);
-      w.st->above1 = run;
-    }
-    run = nxt;
-  }
-}
-
-// S4: level-2 histogram inside bucket b1.
-__global__ void __launch_bounds__(256)
-samp_hist2_kernel(int V, SampWs w, float temperature, const float* tdev) {
-  if (!sampling(temperature, tdev) || w.st->all) return;
-  const uint32_t b1 = w.st->b1;
-  for (int i = blockIdx.x * SEG + threadIdx.x; i < min(V, (blockIdx.x + 1) * SEG); i += 256) {
-    const float q = w.q[i];
-    const uint32_t bits = __float_as_uint(q);
-    if ((bits >> 16) == b1) {
-      atomicAdd(&w.h2[bits & 0xFFFF], (unsigned long long)fx(q));
-      atomicAdd(&w.c2[bits & 0xFFFF], 1u);
-    }
-  }
+// wave sum of an int on the DPP lane network (as wave_sum); every lane gets it
+__device__ __forceinline__ int wave_sum_int_dpp(int v) {
+#define DS4G_DPP_I(ctrl, rm, bc) v += __builtin_amdgcn_update_dpp(0, v, ctrl, rm, 0xF, bc)
+  DS4G_DPP_I(0x111, 0xF, true); DS4G_DPP_I(0x112, 0xF, true); DS4G_DPP_I(0x114, 0xF, true);
+  DS4G_DPP_I(0x118, 0xF, true); DS4G_DPP_I(0x142, 0xA, false); DS4G_DPP_I(0x143, 0xC, false);
+#undef DS4G_DPP_I
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ uint64_t splitmix64_next(uint64_t* s) {
@@ -262,245 +154,425 @@ __device__ __forceinline__ uint64_t splitmix64_next(uint64_t* s) {
   return z ^ (z >> 31);
 }
 
-// min-p: every weight below min(min_p, 1) is dropped (the largest weight
-// is exactly 1).  When that threshold lies above the top-p cut q*, it becomes
-// the cut and every entry equal to it is kept; otherwise top-p decides.
-__device__ __forceinline__ void apply_min_p(SampState* st, float min_p) {
-  if (!(min_p > 0.f)) return;
-  const float thr = fminf(min_p, 1.f);
-  if (thr > __uint_as_float(st->vstar)) {
-    st->vstar = __float_as_uint(thr);
-    st->m = 0x7fffffff;
+// The temperature of a call: a host value, or one read from device memory
+// each time (tdev), so that a captured graph can switch between sampling and
+// argmax without being captured again.
+__device__ __forceinline__ float call_temperature(float temperature, const float* tdev) {
+  return tdev ? *tdev : temperature;
+}
+
+// The largest logit and its first index, from the lm_head blocks' maxima
+// (block-wide, every thread gets both).  INT_MAX when every logit is NaN or
+// -inf.
+__device__ __forceinline__ void global_argmax(const SampWs& w, int nbm, float& m, int& mi,
+                                              float* redf, int* redi) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  m = -INFINITY;
+  mi = 0x7fffffff;
+  for (int b = threadIdx.x; b < nbm; b += blockDim.x) {
+    const float v = w.bmax[b];
+    const int i = w.barg[b];
+    if (v > m || (v == m && i < mi)) { m = v; mi = i; }
   }
-}
-
-// S5a: level-2 mass per group of 1024 descending positions (group g: buckets
-// NB2-1-1024g down to NB2-1024-1024g, contiguous), one block per group.
-__global__ void __launch_bounds__(256)
-samp_l2sum_kernel(SampWs w, float temperature, const float* tdev) {
-  if (!sampling(temperature, tdev) || w.st->all) return;
-  __shared__ unsigned long long ws[4];
-  const unsigned long long* hb = w.h2 + (NB2 - 1024 - blockIdx.x * 1024) + threadIdx.x * 4;
-  const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(hb);
-  const ulonglong2 b = *reinterpret_cast<const ulonglong2*>(hb + 2);
-  unsigned long long s = a.x + a.y + b.x + b.y;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
+  wave_argmax(m, mi);
+  if (lane == 0) { redf[wid] = m; redi[wid] = mi; }
   __syncthreads();
-  if (threadIdx.x == 0) w.g2[blockIdx.x] = ws[0] + ws[1] + ws[2] + ws[3];
+  m = redf[0];
+  mi = redi[0];
+  for (int k = 1; k < (int)(blockDim.x >> 6); ++k)
+    if (redf[k] > m || (redf[k] == m && redi[k] < mi)) { m = redf[k]; mi = redi[k]; }
 }
 
-// S5 (one block of 1024): exact cut weight q*, how many equal-to-q* entries
-// are kept (top-p, then min-p), and the generator draw u.
-__global__ void __launch_bounds__(1024)
-samp_level2_kernel(SampWs w, uint64_t* rng, float min_p, float temperature, const float* tdev) {
-  if (!sampling(temperature, tdev)) return;
-  __shared__ unsigned long long red[16];
-  SampState* st = w.st;
-  if (st->all) {
-    if (threadIdx.x == 0) {
-      st->vstar = 0u;
-      st->m = 0x7fffffff;   // every entry equal to q* = 0 is kept too
-      st->above = st->total;
-      apply_min_p(st, min_p);
-      const uint64_t z = splitmix64_next(rng);
-      st->u = (double)(z >> 40) * (1.0 / 16777216.0);
+// The level-1 crossing (block-wide, every thread): the total mass, the
+// target, and the key where the descending cumulative mass reaches it.
+// Returns whether a crossing exists (false when no weight has mass).
+__device__ bool level1_cut(const SampWs& w, float top_p, uint32_t* b1,
+                           unsigned long long* above1, double* target,
+                           unsigned long long* red, unsigned long long* sh) {
+  constexpr int PER = (NKEY + SB - 1) / SB;
+  const int tid = threadIdx.x;
+  unsigned long long loc[PER], s = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int k = NKEY - 1 - (tid * PER + j);
+    loc[j] = (k >= 0) ? w.h1[k] : 0ull;
+    s += loc[j];
+  }
+  const unsigned long long inc = block_incl_scan_u64(s, red);
+  if (tid == SB - 1) sh[0] = inc;
+  if (tid == 0) sh[1] = ~0ull;
+  __syncthreads();
+  double tg = (double)top_p * (double)sh[0];
+  if (tg < 0.5) tg = 0.5;   // keep at least one token
+  *target = tg;
+  unsigned long long run = inc - s;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const unsigned long long nxt = run + loc[j];
+    if ((double)run < tg && (double)nxt >= tg) {
+      sh[1] = (unsigned long long)(KLO + (NKEY - 1 - (tid * PER + j)));
+      sh[2] = run;
     }
+    run = nxt;
+  }
+  __syncthreads();
+  const bool found = sh[1] != ~0ull;
+  *b1 = (uint32_t)sh[1];
+  *above1 = sh[2];
+  __syncthreads();
+  return found;
+}
+
+// The exact cut (block-wide, every thread): bits of q* and how many entries
+// equal to it are kept, from the level-1 decision and the level-2 histogram
+// (top-p), then min-p.
+// st: the level-1 decision; gs (wave 0): lane l holds the mass of level-2
+// group NG2 - 1 - l.
+__device__ void exact_cut(const SampWs& w, const SampState& st, unsigned long long gs,
+                          float top_p, float min_p, uint32_t* vstar, int* m,
+                          unsigned long long* red, unsigned long long* sh) {
+  const int tid = threadIdx.x, wid = tid >> 6;
+  uint32_t vs = 0u;          // top_p >= 1: every entry, those equal to 0 too
+  int mk = 0x7fffffff;
+  if (top_p < 1.0f) {
+    // the group of 1024 level-2 buckets that holds the crossing (descending)
+    if (tid == 0) sh[0] = ~0ull;
+    __syncthreads();
+    if (wid == 0) {
+      const int lane = tid & 63;
+      const unsigned long long run0 = st.above1 + wave_incl_scan_u64(gs) - gs;
+      if ((double)run0 < st.target && (double)(run0 + gs) >= st.target) {
+        sh[0] = (unsigned long long)(NG2 - 1 - lane);
+        sh[1] = run0;
+      }
+    }
+    __syncthreads();
+    const int grp = (int)sh[0];
+    const unsigned long long grun = sh[1];
+    // that group's buckets, one per thread (descending), prefix-summed
+    const uint32_t b2 = (grp >= 0 && grp < NG2) ? (uint32_t)(grp * 1024 + 1023 - tid) : 0u;
+    const unsigned long long hv = (grp >= 0 && grp < NG2) ? w.h2[b2] : 0ull;
+    const unsigned long long run = grun + block_incl_scan_u64(hv, red) - hv;   // mass before b2
+    if (tid == 0) { sh[2] = 0ull; sh[3] = 0x7fffffffull; }
+    __syncthreads();
+    if (grp >= 0 && grp < NG2 && (double)run < st.target && (double)(run + hv) >= st.target) {
+      const uint32_t vbits = (st.b1 << 16) | b2;
+      const unsigned long long qf = fx(__uint_as_float(vbits));
+      const unsigned int cnt = w.c2[b2];
+      // the fewest equal-to-q* entries (in index order) that reach the target
+      long long mm = (long long)ceil((st.target - (double)run) / (double)qf);
+      if (mm < 1) mm = 1;
+      if (mm > (long long)cnt) mm = cnt;
+      while (mm > 1 && (double)(run + (unsigned long long)(mm - 1) * qf) >= st.target) --mm;
+      while (mm < (long long)cnt && (double)(run + (unsigned long long)mm * qf) < st.target) ++mm;
+      sh[2] = vbits;
+      sh[3] = (unsigned long long)mm;
+    }
+    __syncthreads();
+    vs = (uint32_t)sh[2];
+    mk = (int)sh[3];
+    __syncthreads();
+  }
+  // min-p: weights below min(min_p, 1) are dropped (the largest weight is
+  // exactly 1); when that threshold lies above the top-p cut it becomes the
+  // cut, and every entry equal to it is kept
+  if (min_p > 0.f) {
+    const float thr = fminf(min_p, 1.f);
+    if (thr > __uint_as_float(vs)) { vs = __float_as_uint(thr); mk = 0x7fffffff; }
+  }
+  *vstar = vs;
+  *m = mk;
+}
+}  // namespace
+
+size_t sample_ws_bytes(int V) {
+  size_t total = 0;
+  carve(nullptr, V, &total);
+  return total;
+}
+
+SampleScratch sample_scratch(void* ws, int V) {
+  const SampWs w = carve(ws, V);
+  SampleScratch s;
+  s.zero = reinterpret_cast<uint32_t*>(w.h1);
+  s.zero_words = NKEY * 2;   // h1 (the weight launch clears the level-2 histogram)
+  s.bmax = w.bmax;
+  s.barg = w.barg;
+  return s;
+}
+
+// argmax over the lm_head blocks' maxima (host temperature <= 0)
+__global__ void __launch_bounds__(SB)
+samp_argmax_kernel(int nbm, SampWs w, int* token) {
+  __shared__ float redf[16];
+  __shared__ int redi[16];
+  float m;
+  int mi;
+  global_argmax(w, nbm, m, mi, redf, redi);
+  if (threadIdx.x == 0) *token = (mi == 0x7fffffff) ? 0 : mi;   // every logit NaN / -inf: 0
+}
+
+// (1) q = exp((l - M) / T) for this block's SEG entries, and their level-1
+// masses: summed per key in LDS first, so that equal keys (a narrow logit
+// spread puts thousands of weights in one key) cost one global atomic per
+// block instead of one per entry.  A device temperature <= 0: block 0 writes
+// the argmax and every later kernel returns at once.
+__global__ void __launch_bounds__(SB)
+samp_q_kernel(const float* __restrict__ logits, int V, int nbm, float temperature,
+              const float* tdev, SampWs w, int* token) {
+  __shared__ unsigned long long hist[NKEY];
+  __shared__ float redf[16];
+  __shared__ int redi[16];
+  const int tid = threadIdx.x;
+  // this block's logits are requested before anything waits on memory
+  const int lo = blockIdx.x * SEG, hi = min(V, lo + SEG);
+  float lg[SEG / SB];
+#pragma unroll
+  for (int j = 0; j < SEG / SB; ++j) {
+    const int i = lo + tid + j * SB;
+    lg[j] = (i < hi) ? logits[i] : 0.f;
+  }
+  for (int k = tid; k < NKEY; k += SB) hist[k] = 0;
+  float M;
+  int mi;
+  global_argmax(w, nbm, M, mi, redf, redi);   // its barrier also covers the clearing
+  const float t = call_temperature(temperature, tdev);
+  if (!(t > 0.f)) {
+    if (blockIdx.x == 0 && tid == 0) *token = (mi == 0x7fffffff) ? 0 : mi;
     return;
   }
-  const double target = st->target;
-  const unsigned long long a1 = st->above1;
-  // the group of 1024 positions that holds the crossing (the cumulative mass
-  // is non-decreasing and level 1 put the target inside bucket b1): wave 0
-  // scans the 64 group sums
-  __shared__ int grp;
-  __shared__ unsigned long long grun;
-  if (threadIdx.x == 0) grp = -1;
-  __syncthreads();
-  if (threadIdx.x < NB2 / 1024) {
-    const int lane = threadIdx.x;
-    const unsigned long long gs = w.g2[lane];
-    unsigned long long cum = gs;
+  {   // clear the level-2 histogram for the next launch
+    uint32_t* z = reinterpret_cast<uint32_t*>(w.h2);
+    const int nz = (int)((kZeroBytes - kH2Off) / 4);
+    for (int i = blockIdx.x * SB + tid; i < nz; i += gridDim.x * SB) z[i] = 0u;
+  }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const unsigned long long y = __shfl_up(cum, o, 64);
-      if (lane >= o) cum += y;
-    }
-    const unsigned long long run0 = a1 + cum - gs;
-    if ((double)run0 < target && (double)(run0 + gs) >= target) {
-      grp = lane;
-      grun = run0;
-    }
+  for (int j = 0; j < SEG / SB; ++j) {
+    const int i = lo + tid + j * SB;
+    if (i >= hi) break;
+    float q = expf((lg[j] - M) / t);
+    q = (q == q) ? fminf(q, 1.f) : 0.f;   // a NaN logit weighs nothing; keys stay <= 0x3F80
+    w.q[i] = q;
+    const int key = (int)(__float_as_uint(q) >> 16) - KLO;
+    if (key >= 0) atomicAdd(&hist[key], (unsigned long long)fx(q));
   }
   __syncthreads();
-  if (grp < 0) return;
-  // the group's positions, one per thread (descending), prefix-summed
-  const uint32_t b2 = NB2 - 1 - (grp * 1024 + threadIdx.x);
-  const unsigned long long hv = w.h2[b2];
-  const unsigned long long run = grun + block_incl_scan_u64(hv, red) - hv;   // mass before b2
-  if ((double)run < target && (double)(run + hv) >= target) {
-    const uint32_t vbits = (st->b1 << 16) | b2;
-    const unsigned long long qf = fx(__uint_as_float(vbits));
-    const unsigned int cnt = w.c2[b2];
-    // smallest m >= 1 with run + m*qf >= target
-    long long mm = (long long)ceil((target - (double)run) / (double)qf);
-    if (mm < 1) mm = 1;
-    if (mm > (long long)cnt) mm = cnt;
-    while (mm > 1 && (double)(run + (unsigned long long)(mm - 1) * qf) >= target) --mm;
-    while (mm < (long long)cnt && (double)(run + (unsigned long long)mm * qf) < target) ++mm;
-    st->vstar = vbits;
-    st->m = (int)mm;
-    st->above = run;
-    apply_min_p(st, min_p);
-    const uint64_t z = splitmix64_next(rng);
-    st->u = (double)(z >> 40) * (1.0 / 16777216.0);
+  for (int k = tid; k < NKEY; k += SB) {
+    const unsigned long long v = hist[k];
+    if (v) atomicAdd(&w.h1[k], v);
   }
 }
 
-// S6: per segment, mass strictly above q*, how many such entries, and how
+// (2) every block: the level-1 crossing key b1 (block 0 records it for the
+// later launches); then the level-2 histogram (mass, count, group mass) of
+// this block's entries in bucket b1.
+__global__ void __launch_bounds__(SB)
+samp_hist2_kernel(int V, float top_p, float temperature, const float* tdev, SampWs w) {
+  if (!(call_temperature(temperature, tdev) > 0.f) || top_p >= 1.0f) return;
+  __shared__ unsigned long long red[16], sh[4];
+  const int lo = blockIdx.x * SEG, hi = min(V, lo + SEG);
+  float qv[SEG / SB];   // requested before the level-1 histogram is read
+#pragma unroll
+  for (int j = 0; j < SEG / SB; ++j) {
+    const int i = lo + threadIdx.x + j * SB;
+    qv[j] = (i < hi) ? w.q[i] : 0.f;
+  }
+  uint32_t b1;
+  unsigned long long above1;
+  double target;
+  const bool found = level1_cut(w, top_p, &b1, &above1, &target, red, sh);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    SampState* st = w.st;
+    st->b1 = b1; st->found = found ? 1 : 0; st->above1 = above1; st->target = target;
+  }
+  if (!found) return;
+#pragma unroll
+  for (int j = 0; j < SEG / SB; ++j) {
+    const int i = lo + threadIdx.x + j * SB;
+    if (i >= hi) break;
+    const float q = qv[j];
+    const uint32_t bits = __float_as_uint(q);
+    if ((bits >> 16) == b1) {
+      const unsigned long long f = fx(q);
+      atomicAdd(&w.h2[bits & 0xFFFF], f);
+      atomicAdd(&w.c2[bits & 0xFFFF], 1u);
+      atomicAdd(&w.g2[(bits & 0xFFFF) >> 10], f);
+    }
+  }
+}
+
+// (3) every block: the exact cut (block 0 records it); then, for this
+// block's segment, the mass strictly above q*, how many such entries, and how
 // many entries equal q*.
-__global__ void __launch_bounds__(256)
-samp_segsum_kernel(int V, SampWs w, float temperature, const float* tdev) {
-  if (!sampling(temperature, tdev)) return;
-  __shared__ unsigned long long ss[4];
-  __shared__ int sn[4], st_[4];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const float qs = __uint_as_float(w.st->vstar);
+__global__ void __launch_bounds__(SB)
+samp_segsum_kernel(int V, float top_p, float min_p, float temperature, const float* tdev,
+                   SampWs w) {
+  if (!(call_temperature(temperature, tdev) > 0.f)) return;
+  __shared__ unsigned long long red[16], sh[4];
+  __shared__ int sn[16], st_[16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // everything this block reads that no decision depends on, requested first
+  const SampState sst = *w.st;
+  const unsigned long long gs = (wid == 0) ? w.g2[NG2 - 1 - lane] : 0ull;
+  const int lo = blockIdx.x * SEG, hi = min(V, lo + SEG);
+  float qv[SEG / SB];
+#pragma unroll
+  for (int j = 0; j < SEG / SB; ++j) {
+    const int i = lo + tid + j * SB;
+    qv[j] = (i < hi) ? w.q[i] : 0.f;
+  }
+  if (top_p < 1.0f && !sst.found) return;
+  uint32_t vstar;
+  int mk;
+  exact_cut(w, sst, gs, top_p, min_p, &vstar, &mk, red, sh);
+  if (blockIdx.x == 0 && tid == 0) { w.st->vstar = vstar; w.st->m = mk; }
+  const float qs = __uint_as_float(vstar);
   unsigned long long s = 0;
   int n = 0, t = 0;
-  for (int i = blockIdx.x * SEG + threadIdx.x; i < min(V, (blockIdx.x + 1) * SEG); i += 256) {
-    const float q = w.q[i];
+#pragma unroll
+  for (int j = 0; j < SEG / SB; ++j) {
+    const int i = lo + tid + j * SB;
+    if (i >= hi) break;
+    const float q = qv[j];
     if (q > qs) { s += fx(q); ++n; }
     else if (q == qs) ++t;
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    s += __shfl_xor(s, o, 64);
-    n += __shfl_xor(n, o, 64);
-    t += __shfl_xor(t, o, 64);
-  }
-  if (lane == 0) { ss[wid] = s; sn[wid] = n; st_[wid] = t; }
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  n = wave_sum_int_dpp(n);
+  t = wave_sum_int_dpp(t);
+  if (lane == 0) { red[wid] = s; sn[wid] = n; st_[wid] = t; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    w.seg_gt[blockIdx.x] = ss[0] + ss[1] + ss[2] + ss[3];
-    w.seg_gtn[blockIdx.x] = sn[0] + sn[1] + sn[2] + sn[3];
-    w.seg_tie[blockIdx.x] = st_[0] + st_[1] + st_[2] + st_[3];
+  if (tid == 0) {
+    unsigned long long ss = 0;
+    int nn = 0, tt = 0;
+    for (int k = 0; k < SB / 64; ++k) { ss += red[k]; nn += sn[k]; tt += st_[k]; }
+    w.seg_gt[blockIdx.x] = ss;
+    w.seg_gtn[blockIdx.x] = nn;
+    w.seg_tie[blockIdx.x] = tt;
   }
 }
 
-// S7 (one block of 1024): the kept mass K (exact, per segment in fixed point),
-// r = u * K, then the segment and the entry where the running kept mass
-// (vocabulary order) first reaches r.
-__global__ void __launch_bounds__(1024)
-samp_pick_kernel(int V, int nb, SampWs w, int* token, float temperature, const float* tdev) {
-  if (!sampling(temperature, tdev)) return;
+// (4) one block: the draw u, the kept mass K (exact, per segment in fixed
+// point), r = u * K, then the segment and the entry where the running kept
+// mass (vocabulary order) first reaches r.
+__global__ void __launch_bounds__(SB)
+samp_pick_kernel(int V, int ns, int nbm, float top_p, uint64_t* rng, SampWs w, int* token,
+                 float temperature, const float* tdev) {
+  if (!(call_temperature(temperature, tdev) > 0.f)) return;
   __shared__ unsigned long long red[16];
-  __shared__ int tie_base_s, seg_s;
-  __shared__ unsigned long long cum_before_s, kept_s;
-  __shared__ int wtie[16];
-  const SampState& st = *w.st;
-  const float qs = __uint_as_float(st.vstar);
+  __shared__ int redi[16];
+  __shared__ int seg_s, tok_s, tie_base_s;
+  __shared__ unsigned long long cum_before_s;
+  __shared__ double r_s;
+  __shared__ float redf[16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  // what level A reads, requested at once: the cut, the segment sums, the
+  // generator state
+  const SampState sst = *w.st;
+  const int b = lane;   // wave 0: one segment per lane (ns <= 64)
+  const int tie = (tid < 64 && b < ns) ? w.seg_tie[b] : 0;
+  const unsigned long long sgt = (tid < 64 && b < ns) ? w.seg_gt[b] : 0ull;
+  const int sgn = (tid < 64 && b < ns) ? w.seg_gtn[b] : 0;
+  const uint64_t rs = (tid == 0) ? *rng : 0ull;
+  if (top_p < 1.0f && !sst.found) {   // no weight has mass: the argmax, no draw
+    float m;
+    int mi;
+    global_argmax(w, nbm, m, mi, redf, redi);
+    if (tid == 0) *token = (mi == 0x7fffffff) ? 0 : mi;
+    return;
+  }
+  const float qs = __uint_as_float(sst.vstar);
   const unsigned long long qf = fx(qs);
-  const int m = st.m;
-  // level A: segments (nb <= 1024), one per thread
-  const int b = threadIdx.x;
-  int tie = (b < nb) ? w.seg_tie[b] : 0;
-  // exclusive scan of ties
-  int tinc = tie;
-  {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int mk = sst.m;
+  if (tid < 64) {
+    double u = 0.0;
+    if (tid == 0) {
+      uint64_t st = rs;
+      const uint64_t z = splitmix64_next(&st);
+      *rng = st;
+      u = (double)(z >> 40) * (1.0 / 16777216.0);
+    }
+    u = __shfl(u, 0, 64);
+    // level A: the kept mass per segment (ties kept in index order) and its
+    // running sum
+    const int tie_before = wave_incl_scan_int(tie) - tie;
+    long long kt = (long long)mk - tie_before;
+    if (kt < 0) kt = 0;
+    if (kt > tie) kt = tie;
+    const unsigned long long segk = sgt + (unsigned long long)kt * qf;
+    const int segn = sgn + (int)kt;
+    const unsigned long long cinc = wave_incl_scan_u64(segk);
+    const unsigned long long kept = __shfl(cinc, 63, 64);
+    const double r = u * (double)kept;
+    // the first segment with kept entries whose cumulative kept mass reaches r
+    const uint64_t hit = __ballot(b < ns && segn > 0 && (double)cinc >= r);
+    const int f = hit ? __builtin_ctzll(hit) : 0x7fffffff;
+    if (tid == 0) { seg_s = f; tok_s = 0x7fffffff; r_s = r; }
+    if (hit && lane == f) { cum_before_s = cinc - segk; tie_base_s = tie_before; }
+  }
+  __syncthreads();
+  const double r = r_s;
+  const int sg = seg_s;
+  if (sg != 0x7fffffff) {
+    // level B: that segment's entries in index order, 4 consecutive per
+    // thread: the first kept one whose running kept mass reaches r
+    const int i0 = sg * SEG + 4 * tid;
+    float q[4];
+    int ties = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(tinc, o, 64);
-      if (lane >= o) tinc += y;
+    for (int j = 0; j < 4; ++j) {
+      q[j] = (i0 + j < V) ? w.q[i0 + j] : 0.f;
+      ties += (i0 + j < V && q[j] == qs) ? 1 : 0;
     }
-    if (lane == 63) wtie[wid] = tinc;
-    __syncthreads();
-    int base = 0;
-    for (int w2 = 0; w2 < wid; ++w2) base += wtie[w2];
-    tinc += base;
-    __syncthreads();
-  }
-  const int tie_before = tinc - tie;
-  long long kt = (long long)m - tie_before;
-  if (kt < 0) kt = 0;
-  if (kt > tie) kt = tie;
-  const unsigned long long segk = (b < nb) ? w.seg_gt[b] + (unsigned long long)kt * qf : 0ull;
-  const int segn = (b < nb) ? w.seg_gtn[b] + (int)kt : 0;
-  const unsigned long long cinc = block_incl_scan_u64(segk, red);
-  if (b == 0) seg_s = nb - 1;
-  if (b == nb - 1) kept_s = cinc;
-  __syncthreads();
-  const double r = st.u * (double)kept_s;
-  // first segment with kept entries whose inclusive cumulative mass >= r
-  const bool hit = (b < nb) && segn > 0 && (double)cinc >= r;
-  // smallest such b: reduce with atomicMin in LDS
-  if (hit) atomicMin(&seg_s, b);
-  __syncthreads();
-  if (b == seg_s) { cum_before_s = cinc - segk; tie_base_s = tie_before; }
-  __syncthreads();
-  // level B: entries of the chosen segment, one per thread
-  const int sb = seg_s;
-  const int i = sb * SEG + threadIdx.x;
-  const float q = (i < V) ? w.q[i] : 0.f;
-  const int is_tie = (i < V && q == qs) ? 1 : 0;
-  // rank of this tie among the segment's ties
-  int tr = is_tie;
-  {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int rank = tie_base_s + block_incl_scan_int(ties, redi) - ties;
+    bool kept[4];
+    unsigned long long ms[4], lsum = 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(tr, o, 64);
-      if (lane >= o) tr += y;
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = i0 + j < V;
+      const bool is_tie = ok && q[j] == qs;
+      kept[j] = ok && (q[j] > qs || (is_tie && rank < mk));
+      rank += is_tie ? 1 : 0;
+      ms[j] = kept[j] ? ((q[j] > qs) ? fx(q[j]) : qf) : 0ull;
+      lsum += ms[j];
     }
-    __syncthreads();
-    if (lane == 63) wtie[wid] = tr;
-    __syncthreads();
-    int base = 0;
-    for (int w2 = 0; w2 < wid; ++w2) base += wtie[w2];
-    tr += base;
-  }
-  const int tie_rank = tie_base_s + tr - is_tie;
-  const bool kept = (i < V) && ((q > qs) || (is_tie && tie_rank < m));
-  const unsigned long long mass = kept ? ((q > qs) ? fx(q) : qf) : 0ull;
-  const unsigned long long run = cum_before_s + block_incl_scan_u64(mass, red);
-  __shared__ int tok;
-  if (threadIdx.x == 0) tok = 0x7fffffff;
-  __syncthreads();
-  if (kept && (double)run >= r) atomicMin(&tok, i);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (tok == 0x7fffffff) {   // defensive: never leave an out-of-range id
-      float bm = -INFINITY;
-      int bi = 0;
-      for (int k = 0; k < nb; ++k)
-        if (w.bmax[k] > bm) { bm = w.bmax[k]; bi = w.barg[k]; }
-      tok = bi;
+    unsigned long long cum = cum_before_s + block_incl_scan_u64(lsum, red) - lsum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kept[j]) {
+        cum += ms[j];
+        if ((double)cum >= r) { atomicMin(&tok_s, i0 + j); break; }
+      }
     }
-    *token = tok;
   }
+  __syncthreads();
+  int tk = tok_s;
+  if (tk == 0x7fffffff) {   // defensive (r < K always meets a kept entry): never an invalid id
+    float m;
+    int mi;
+    global_argmax(w, nbm, m, mi, redf, redi);
+    tk = (mi == 0x7fffffff) ? 0 : mi;
+  }
+  if (tid == 0) *token = tk;
 }
 
 int launch_sample(const SampleArgs& s, Exec st) {
-  const int nb = (s.V + SEG - 1) / SEG;
-  if (nb > 1024 || s.V > (1 << 18)) return -1;
-  SampWs w = carve(s.ws, s.V);
+  if (s.V <= 0 || s.V > MAX_SEGS * SEG || s.nbm <= 0 || s.nbm > NBM) return -1;
+  const SampWs w = carve(s.ws, s.V);
+  const int ns = (s.V + SEG - 1) / SEG;
   const float T = s.temperature;
   const float* td = s.temperature_dev;
-  DS4G_LAUNCH(samp_max_kernel, dim3(nb), dim3(256), 0, st, s.logits, s.V, w);
-  // a host temperature picks the path here; a device one, inside every kernel
-  if (td || !(T > 0.f))
-    DS4G_LAUNCH(samp_argmax_kernel, dim3(1), dim3(64), 0, st, nb, w, s.token, T, td);
-  if (!td && !(T > 0.f)) return 0;
-  DS4G_LAUNCH(samp_q_kernel, dim3((nb + QSEGS - 1) / QSEGS), dim3(1024), 0, st, s.logits,
-                     s.V, nb, T, td, w);
-  DS4G_LAUNCH(samp_level1_kernel, dim3(1), dim3(1024), 0, st, s.top_p, w, T, td);
-  DS4G_LAUNCH(samp_hist2_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
-  DS4G_LAUNCH(samp_l2sum_kernel, dim3(NB2 / 1024), dim3(256), 0, st, w, T, td);
-  DS4G_LAUNCH(samp_level2_kernel, dim3(1), dim3(1024), 0, st, w, s.rng, s.min_p, T, td);
-  DS4G_LAUNCH(samp_segsum_kernel, dim3(nb), dim3(256), 0, st, s.V, w, T, td);
-  DS4G_LAUNCH(samp_pick_kernel, dim3(1), dim3(1024), 0, st, s.V, nb, w, s.token, T, td);
+  if (!td && !(T > 0.f)) {
+    DS4G_LAUNCH(samp_argmax_kernel, dim3(1), dim3(SB), 0, st, s.nbm, w, s.token);
+    return 0;
+  }
+  DS4G_LAUNCH(samp_q_kernel, dim3(ns), dim3(SB), 0, st, s.logits, s.V, s.nbm, T, td, w, s.token);
+  DS4G_LAUNCH(samp_hist2_kernel, dim3(ns), dim3(SB), 0, st, s.V, s.top_p, T, td, w);
+  DS4G_LAUNCH(samp_segsum_kernel, dim3(ns), dim3(SB), 0, st, s.V, s.top_p, s.min_p, T, td, w);
+  DS4G_LAUNCH(samp_pick_kernel, dim3(1), dim3(SB), 0, st, s.V, ns, s.nbm, s.top_p, s.rng, w,
+              s.token,
+              T, td);
   return 0;
 }
 
