@@ -458,7 +458,9 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
                               DS4G_TILE_M_MAX);
   RouteArgs ra{};
   ra.logits = at<float>(ws, L.lpart); ra.nsplit = rsplit;
-  ra.logits_sum = at<float>(ws, L.logits); ra.T = T; ra.E = E; ra.k = k;
+  // the summed logits only when the caller asked for them
+  ra.logits_sum = (routing && routing->router_logits) ? at<float>(ws, L.logits) : nullptr;
+  ra.T = T; ra.E = E; ra.k = k;
   ra.topk_idx = at<int>(ws, L.tidx); ra.topk_w = at<float>(ws, L.tw);
   ra.count = at<int>(ws, L.count); ra.offset = at<int>(ws, L.offset);
   ra.rank = at<int>(ws, L.rank); ra.perm = at<int>(ws, L.perm);
@@ -509,7 +511,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
     copy_out(routing->topk_w, ra.topk_w, (size_t)T * k * 4, st);
     copy_out(routing->perm, ra.perm, (size_t)T * k * 4, st);
     copy_out(routing->router_in, at<void>(ws, L.yf), (size_t)T * d * 4, st);
-    copy_out(routing->router_logits, ra.logits_sum, (size_t)T * E * 4, st);
+    if (ra.logits_sum) copy_out(routing->router_logits, ra.logits_sum, (size_t)T * E * 4, st);
   }
   return rc;
 }

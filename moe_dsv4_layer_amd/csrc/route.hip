@@ -104,10 +104,13 @@ template int launch_rmsnorm_rows<float>(const float*, int, int, const float*, fl
                                         uint16_t*, uint16_t*, uint16_t*, Exec);
 
 // ------------------------------------------------------------ top-k per token
-// One wave per token: k rounds of a wave arg-max (lower index wins ties) over
-// the E logits, and the softmax probability of each pick.
+// One wave per token: the k largest of the E logits (lower index wins ties)
+// and the softmax probability of each pick, by route_wave (each lane sorts
+// its logits once; a round is two DPP reductions and a register shift), the
+// selection decode's gate/up blocks make.
 // The logits arrive as nsplit partial sums (split-K GEMM); they are added in
-// split order, so the result does not depend on scheduling.
+// split order, so the result does not depend on scheduling.  lsum (the
+// summed logits) is written only when a caller asked for them.
 __global__ void __launch_bounds__(256)
 topk_kernel(const float* __restrict__ logits, int nsplit, float* __restrict__ lsum, int T, int E,
             int k, int* __restrict__ idx, float* __restrict__ wts) {
@@ -135,45 +138,13 @@ topk_kernel(const float* __restrict__ logits, int nsplit, float* __restrict__ ls
         for (int i = 0; i < 8; ++i) v[i] += p[zz][i];
       }
   }
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = lane + 64 * i;
-    float a = -INFINITY;
-    if (e < E) {
-      a = v[i];
-      lsum[(long)t * E + e] = a;
-      if (a != a) a = -INFINITY;   // a NaN score ranks below every number
-    }
-    v[i] = a;
-    m = fmaxf(m, v[i]);
-  }
-  m = wave_max(m);
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (lane + 64 * i < E) sum += expf(v[i] - m);
-  sum = wave_sum(sum);
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
-    }
-    wave_argmax(bv, bi);
-    // k < E leaves a candidate every round, so bi < E; the clamp keeps an
-    // index that addresses expert weights inside [0, E) whatever the scores
-    if (lane == 0) {
-      idx[(long)t * k + r] = min(max(bi, 0), E - 1);
-      wts[(long)t * k + r] = expf(bv - m) / sum;
-    }
-    // a chosen expert becomes NaN: neither > nor == picks it again
+  if (lsum) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (lane + 64 * i == bi) v[i] = __builtin_nanf("");
+      if (lane + 64 * i < E) lsum[(long)t * E + lane + 64 * i] = v[i];
   }
+  // route_wave takes a NaN score as -inf and keeps every index in [0, E)
+  route_wave(v, E, k, idx + (long)t * k, wts + (long)t * k);
 }
 
 // ------------------------------------------------------------ block scans

@@ -91,6 +91,37 @@ def test_sampler_teacher_forced(temperature, top_p):
     assert agree >= 22
 
 
+@pytest.mark.parametrize("hidden,vocab,temperature,top_p", [(1024, 262144, 0.9, 0.95),
+                                                             (512, 4099, 0.7, 0.9),
+                                                             (512, 4099, 1.3, 1.0)])
+def test_sampler_vocab_limits_teacher_forced(hidden, vocab, temperature, top_p):
+    # the largest vocabulary the call accepts (2^18: 64 weight blocks, 64
+    # roulette segments) and a vocabulary that is not a multiple of the
+    # 4096-entry block (a ragged last block and segment)
+    shape, hw, ws = _setup(hidden, vocab, synth.BF16, 83)
+    state = synth.rng_seed(1004) ^ vocab
+    agree = amb = 0
+    for i in range(12):
+        x = synth.hidden(1, hidden, 83, stream=i, device="cuda").reshape(-1) * (1 + i % 3)
+        st_in = state
+        logits, tok, state = _run(hw, shape, vocab, x, temperature, top_p, st_in, ws)
+        assert 0 <= tok < vocab
+        g = oracle.SplitMix64(st_in)
+        u = g.next_f32()
+        assert _u64(state) == g.state, "generator must advance by exactly one draw"
+        ref = oracle.sample(logits, temperature, top_p, u)
+        if tok == ref["token"]:
+            agree += 1
+            continue
+        assert sampler_excused(ref, logits, temperature), (i, tok, ref)
+        amb += 1
+    log(f"sampler V={vocab} T={temperature} p={top_p}: {agree} equal, {amb} on a boundary")
+    assert agree >= 11
+    # argmax at temperature 0 over the same vocabulary
+    logits, tok, _ = _run(hw, shape, vocab, x, 0.0, top_p, None, ws)
+    assert tok == oracle.argmax(logits)
+
+
 def test_sampler_small_vocab_grid():
     # tiny vocabulary, many draws: the token histogram must follow the kept mass
     shape, hw, ws = _setup(256, 1024, synth.F32, 79)
