@@ -74,7 +74,7 @@ ImageLayout image_layout(const ds4g_layer_cfg& c, size_t base) {
 
 struct Layout {
   size_t xn, c, qkv, q, kc, vc, o, yf, ys, logits, lpart, tidx, tw, rank, perm, gather, pos_of,
-      count, offset, tiles, ntiles, z, zs, part, skp, rope, img[3], inv[3], total;
+      count, chunk, offset, tiles, ntiles, z, zs, part, skp, rope, img[3], inv[3], total;
 };
 
 // Byte offsets of every workspace buffer for T tokens.  fp32-sized slots are
@@ -108,6 +108,7 @@ Layout layout(const ds4g_layer_cfg& c, int T, bool images) {
   L.gather = take((size_t)T * k * 4);
   L.pos_of = take((size_t)T * k * 4);
   L.count = take(E * 4);
+  L.chunk = take((size_t)((T * k + kRankChunk - 1) / kRankChunk) * E * 4);
   L.offset = take((E + 1) * 4);
   L.tiles = take((E + (size_t)T * k + 1) * 4);
   L.ntiles = take(4);
@@ -464,6 +465,7 @@ int prefill_impl(const ds4g_layer_cfg& c, const ds4g_layer_weights& w, ds4g_kv_r
   ra.topk_idx = at<int>(ws, L.tidx); ra.topk_w = at<float>(ws, L.tw);
   ra.count = at<int>(ws, L.count); ra.offset = at<int>(ws, L.offset);
   ra.rank = at<int>(ws, L.rank); ra.perm = at<int>(ws, L.perm);
+  ra.chunk = at<int>(ws, L.chunk);
   ra.gather = at<int>(ws, L.gather); ra.pos_of = at<int>(ws, L.pos_of);
   ra.tiles = at<int>(ws, L.tiles); ra.ntiles = at<int>(ws, L.ntiles); ra.tile_m = tile_m;
   ra.out_count = routing ? routing->expert_count : nullptr;

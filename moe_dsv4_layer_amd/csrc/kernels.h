@@ -196,7 +196,9 @@ struct RouteArgs {
   float* topk_w;        // [T, k]
   int* count;           // [E]
   int* offset;          // [E+1]
-  int* rank;            // [T, k] rank of entry inside its expert
+  int* rank;            // [T, k] rank of entry inside its expert within its chunk
+  int* chunk;           // [ceil(T*k / kRankChunk), E] per chunk: entries of each expert,
+                        // then the entries of that expert in earlier chunks
   int* perm;            // [T*k]
   int* gather;          // [T*k] token of each permuted row
   int* pos_of;          // [T*k] permuted row of entry t*k+j
@@ -206,6 +208,8 @@ struct RouteArgs {
   // optional user copies
   int* out_count; int* out_offset;
 };
+// entries ranked per chunk (one 1024-thread block each)
+constexpr int kRankChunk = 1024;
 int launch_route(const RouteArgs& r, Exec st);
 // x[t] += sum_j w[t,j] part[pos_of[t*k+j]] (fixed j order); part is fp32, or bf16
 // when part_bf16 (the bf16 path rounds each routed expert output to bf16).

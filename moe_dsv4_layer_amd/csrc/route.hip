@@ -185,45 +185,97 @@ __device__ int block_excl_scan(int* a, int n, int* wsum /*[4]*/) {
 }
 
 // ------------------------------------------------------------ expert ranks
-// Block e walks the tokens in order, 1024 at a time; a token that chose e
-// gets the number of earlier tokens that chose e (a ballot prefix count);
-// count[e] = total.  The next chunk's expert ids are loaded before the
-// current chunk is counted, and the per-wave counts alternate between two LDS
-// rows, so each chunk costs one barrier.
-__global__ void __launch_bounds__(1024)
-expert_rank_kernel(const int* __restrict__ idx, int T, int k, int* __restrict__ rank,
-                   int* __restrict__ count) {
-  __shared__ int wsum[2][16];
-  const int e = blockIdx.x;
+// The permutation orders the T*k entries by (expert, entry index), so the
+// rank of entry i inside its expert is the number of earlier entries with
+// the same expert.  It is counted per chunk of kRankChunk entries, then the
+// chunks are added in chunk order; every count is exact, so the result is
+// the same however the blocks run.
+//
+// Chunk c (one block, one entry per thread): the lanes of a wave holding the
+// same expert are found with one ballot per bit of the expert id; an entry's
+// rank in the chunk is the count of its expert in earlier waves plus the
+// lanes of its group below it.  chunk[c][e] = the chunk's entries of e.
+__global__ void __launch_bounds__(kRankChunk)
+rank_chunk_kernel(const int* __restrict__ idx, int n, int E, int* __restrict__ rank,
+                  int* __restrict__ chunk) {
+  constexpr int NW = kRankChunk / 64;
+  extern __shared__ int wcs[];   // [NW][E]: sized by the launch, so the block fits beside
+                                 // the shared expert's GEMM blocks on the second stream
+  auto wc = [&](int w, int x) -> int& { return wcs[w * E + x]; };
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int nv[8];
-  auto load = [&](int t) __attribute__((always_inline)) {
+  const int i = blockIdx.x * kRankChunk + threadIdx.x;
+  const int e = (i < n) ? idx[i] : -1;
+  for (int j = threadIdx.x; j < NW * E; j += kRankChunk) wcs[j] = 0;
+  // lanes whose expert equals this lane's
+  uint64_t same = __ballot(e >= 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) nv[j] = (t < T && j < k) ? idx[(long)t * k + j] : -1;
-  };
-  load(threadIdx.x);
-  int base = 0;
-  for (int t0 = 0, it = 0; t0 < T; t0 += 1024, ++it) {
-    int slot = -1;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (nv[j] == e) slot = j;
-    if (t0 + 1024 < T) load(t0 + 1024 + threadIdx.x);
-    const unsigned long long b = __ballot(slot >= 0);
-    const int before = __popcll(b & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[it & 1][wid] = __popcll(b);
-    __syncthreads();
-    int wbase = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-      const int c = wsum[it & 1][w];
-      wbase += (w < wid) ? c : 0;
-      tot += c;
-    }
-    if (slot >= 0) rank[(long)(t0 + threadIdx.x) * k + slot] = base + wbase + before;
-    base += tot;
+  for (int b = 0; b < 9; ++b) {   // E <= 512
+    const bool bit = (e >> b) & 1;
+    const uint64_t mb = __ballot(bit);
+    same &= bit ? mb : ~mb;
   }
-  if (threadIdx.x == 0) count[e] = base;
+  const uint64_t below = same & ((1ull << lane) - 1ull);
+  __syncthreads();
+  if (e >= 0 && below == 0) wc(wid, e) = __popcll(same);   // the group's lowest lane
+  __syncthreads();
+  // per expert: exclusive prefix over the waves, and the chunk's total
+  for (int x = threadIdx.x; x < E; x += kRankChunk) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int t = wc(w, x);
+      wc(w, x) = run;
+      run += t;
+    }
+    chunk[(long)blockIdx.x * E + x] = run;
+  }
+  __syncthreads();
+  if (e >= 0) rank[i] = wc(wid, e) + __popcll(below);
+}
+
+// Per expert: the chunk counts turned into the entries of that expert in
+// earlier chunks (added in chunk order), and the expert's total.  A block
+// takes EPB experts; thread (expert, group g) takes a contiguous run of the
+// chunks, all its loads in flight at once; the runs' sums are combined in
+// group order through LDS.
+constexpr int kPrefixEPB = 64;
+__global__ void __launch_bounds__(1024)
+rank_prefix_kernel(int* __restrict__ chunk, int nchunk, int E, int* __restrict__ count) {
+  __shared__ int gsum[1024];
+  const int epb = min(E, kPrefixEPB);
+  const int G = 1024 / epb;                      // groups per expert
+  const int el = threadIdx.x % epb, gidx = threadIdx.x / epb;
+  const int e = blockIdx.x * epb + el;
+  const bool on = gidx < G && e < E;
+  const int per = (nchunk + G - 1) / G;
+  const int c0 = gidx * per, c1 = min(nchunk, c0 + per);
+  int s = 0;
+  if (on) {
+    for (int c = c0; c < c1; c += 8) {   // 8 loads in flight
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (c + u < c1) ? chunk[(long)(c + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+  }
+  gsum[threadIdx.x] = s;
+  __syncthreads();
+  if (!on) return;
+  int run = 0;
+  for (int g = 0; g < gidx; ++g) run += gsum[g * epb + el];
+  if (gidx == G - 1) count[e] = run + s;
+  for (int c = c0; c < c1; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (c + u < c1) ? chunk[(long)(c + u) * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c + u < c1) {
+        chunk[(long)(c + u) * E + e] = run;
+        run += v[u];
+      }
+  }
 }
 
 // ------------------------------------------------------------ scatter + tiles
@@ -244,7 +296,7 @@ route_scatter_kernel(RouteArgs r) {
   const int ent = blockIdx.x * 256 + threadIdx.x;
   if (ent < nent) {
     const int e = r.topk_idx[ent];
-    const int p = off[e] + r.rank[ent];
+    const int p = off[e] + r.chunk[(long)(ent / kRankChunk) * E + e] + r.rank[ent];
     r.perm[p] = ent;
     r.gather[p] = ent / r.k;
     r.pos_of[ent] = p;
@@ -270,9 +322,13 @@ int launch_route(const RouteArgs& r, Exec st) {
   if (r.E > 512 || r.k > 8) return -1;
   DS4G_LAUNCH(topk_kernel, dim3((r.T + 3) / 4), dim3(256), 0, st, r.logits, r.nsplit,
                      r.logits_sum, r.T, r.E, r.k, r.topk_idx, r.topk_w);
-  DS4G_LAUNCH(expert_rank_kernel, dim3(r.E), dim3(1024), 0, st, r.topk_idx, r.T, r.k,
-                     r.rank, r.count);
   const int nent = r.T * r.k;
+  const int nchunk = (nent + kRankChunk - 1) / kRankChunk;
+  DS4G_LAUNCH(rank_chunk_kernel, dim3(nchunk), dim3(kRankChunk),
+              (size_t)(kRankChunk / 64) * r.E * sizeof(int), st, r.topk_idx, nent, r.E, r.rank,
+              r.chunk);
+  DS4G_LAUNCH(rank_prefix_kernel, dim3((r.E + kPrefixEPB - 1) / kPrefixEPB), dim3(1024), 0, st,
+              r.chunk, nchunk, r.E, r.count);
   DS4G_LAUNCH(route_scatter_kernel, dim3((nent + 255) / 256), dim3(256), 0, st, r);
   return 0;
 }
