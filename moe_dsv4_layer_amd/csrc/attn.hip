@@ -146,29 +146,32 @@ attn_window_kernel(const float* __restrict__ q, const uint16_t* __restrict__ kc,
 
 // ---------------------------------------------------------------------------
 // ring_commit: copy the cached (k, v) of the last min(T, W) tokens into their
-// ring slots (one block per token row, 16-byte copies).  Runs after every
-// reader of the old ring contents.  *pos is advanced by ring_advance.
-__global__ void __launch_bounds__(64)
+// ring slots, then advance *pos by T.  One block: every thread reads *pos
+// before the barrier, thread 0 advances it after (so no reader sees the new
+// value); 16-byte copies, at most W rows of dh fp16 for k and for v.  Runs
+// after every reader of the old ring contents.
+__global__ void __launch_bounds__(1024)
 ring_commit_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, int T,
                    int W, int dh, uint16_t* __restrict__ ring_k, uint16_t* __restrict__ ring_v,
-                   const int64_t* __restrict__ pos) {
+                   int64_t* __restrict__ pos) {
+  const int64_t p = *pos;
   const int first = T > W ? T - W : 0;
-  const int t = first + blockIdx.x;
-  const int slot = (int)((*pos + t) % W);
-  for (int c = threadIdx.x; c < dh / 8; c += blockDim.x) {
+  const int cnt = T - first, cpr = dh / 8;   // rows, 16-byte chunks per row
+  for (int u = threadIdx.x; u < cnt * cpr; u += blockDim.x) {
+    const int t = first + u / cpr, c = u % cpr;
+    const int slot = (int)((p + t) % W);
     reinterpret_cast<uint4*>(ring_k + (long)slot * dh)[c] =
         reinterpret_cast<const uint4*>(kc + (long)t * dh)[c];
     reinterpret_cast<uint4*>(ring_v + (long)slot * dh)[c] =
         reinterpret_cast<const uint4*>(vc + (long)t * dh)[c];
   }
+  __syncthreads();
+  if (threadIdx.x == 0) *pos = p + T;
 }
-__global__ void ring_advance_kernel(int64_t* pos, int T) { *pos += T; }
 
 static void ring_commit(const AttnArgs& a, Exec st) {
-  const int cnt = a.T < a.W ? a.T : a.W;
-  DS4G_LAUNCH(ring_commit_kernel, dim3(cnt), dim3(64), 0, st, a.kc, a.vc, a.T, a.W, a.dh,
-                     a.ring_k, a.ring_v, a.pos);
-  DS4G_LAUNCH(ring_advance_kernel, dim3(1), dim3(1), 0, st, a.pos, a.T);
+  DS4G_LAUNCH(ring_commit_kernel, dim3(1), dim3(1024), 0, st, a.kc, a.vc, a.T, a.W, a.dh,
+              a.ring_k, a.ring_v, a.pos);
 }
 
 int launch_attention(const AttnArgs& a, Exec st) {
