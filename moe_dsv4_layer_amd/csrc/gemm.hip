@@ -44,6 +44,10 @@
 #ifndef DS4G_BIG_BK
 #define DS4G_BIG_BK 64
 #endif
+// 320 x 256 tiles for the residual-epilogue GEMMs over many rows (1: on)
+#ifndef DS4G_TALL_RESID
+#define DS4G_TALL_RESID 1
+#endif
 // Dense GEMMs with at least this many 128x128 tiles run in the XCD-contiguous
 // tile order of the grouped GEMMs (0: never; measured no faster at 2048 or
 // 16994 rows).
@@ -649,6 +653,7 @@ gemm_dma_kernel(GemmArgs g) {
     }
   };
   if (live == FM) run(std::integral_constant<int, FM>{});
+  else if (FM >= 5 && live == 4) run(std::integral_constant<int, (FM >= 5 ? 4 : 0)>{});
   else if (FM >= 4 && live == 3) run(std::integral_constant<int, (FM >= 4 ? 3 : 0)>{});
   else if (FM >= 3 && live == 2) run(std::integral_constant<int, (FM >= 3 ? 2 : 0)>{});
   else if (FM >= 2 && live == 1) run(std::integral_constant<int, (FM >= 2 ? 1 : 0)>{});
@@ -808,6 +813,17 @@ int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long
   return 0;
 }
 
+#if DS4G_TALL_RESID
+// 320 x 256 tiles, residual epilogue only (the staged 16-bit epilogue would
+// need more LDS than a CU has)
+static int launch_tall_resid(const GemmArgs& g, Exec st) {
+  const dim3 grid((g.N + 255) / 256, (g.M + 319) / 320, 1), block(512);
+  if (g.f16) DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_RESID, true, 64, false>), grid, block, 0, st, g);
+  else DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_RESID, false, 64, false>), grid, block, 0, st, g);
+  return 0;
+}
+#endif
+
 int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
   const bool dual = (g0.epi == EPI_SWIGLU_BF16 || g0.epi == EPI_SWIGLU_F32);
   GemmArgs g = g0;
@@ -842,6 +858,25 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
     }
     const long nout = dual ? g.N * 2L : g.N;           // B rows per output row
     const long big_blocks = ((g.M + 255) / 256) * ((nout + 255) / 256) * nsplit;
+#if DS4G_TALL_RESID
+    // residual epilogue (W_o, the shared down) over many rows: 320 x 256 tiles,
+    // a tenth fewer operand bytes per flop than 256 x 256
+    if (g.epi == EPI_RESID && !g.tiles && nsplit == 1 && !dual && g.M >= 4096) {
+      const long nt = (nout + 255) / 256, mt = (g.M + 319) / 320;
+      const int mb = (int)((mt * nt / 256) * 256 / nt) * 320;   // rows in whole rounds
+      if (mb > 0 && mb < g.M && (mt * nt) % 256 != 0) {
+        GemmArgs hi = g, lo = g;
+        hi.M = mb;
+        lo.M = g.M - mb;
+        lo.A = static_cast<const uint16_t*>(g.A) + (long)mb * g.lda;
+        lo.C = static_cast<char*>(g.C) + (size_t)mb * g.ldc * 4;
+        const int r = launch_tall_resid(hi, st);
+        if (r) return r;
+        return launch_gemm(lo, mfma, wdtype_bf16, st);
+      }
+      return launch_tall_resid(g, st);
+    }
+#endif
     if (big_blocks >= 512) {
       // Rows past the last whole round of 256x256 tiles (one per CU) run as
       // 128x128 tiles, a quarter of the work each, when they would fill less
