@@ -48,6 +48,11 @@ DECODE_TRAFFIC_SOURCES = ("api.hip", "attn.hip", "decode.hip", "dev.h", "kernels
 DECODE_TRAFFIC_SHA1 = "72dc84a50bd64bd2bb599b36c3c5665116a4a335"
 
 
+def progress(msg: str) -> None:
+    """One line on stderr per section, so a long run shows its steps."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def decode_traffic():
     import hashlib
     h = hashlib.sha1()
@@ -359,6 +364,7 @@ def bench_stack43(decode_steps: int) -> dict:
            "weight_bytes": int(sum(t.numel() * t.element_size() for w in layers for t in w.values())
                                + sum(t.numel() * t.element_size() for t in head.values()))}
     # ---- prefill of 512 tokens, then graph-replayed decode steps
+    progress("43-layer stack: prefill 512, decode")
     ids = torch.as_tensor(synth.token_ids(wl.prompt, wl.vocab, wl.seed), device="cuda")
     for rep in range(2):
         st.reset()
@@ -424,6 +430,7 @@ def bench_stack43(decode_steps: int) -> dict:
     out["decode_hbm_frac"] = round(b / (ms_tok * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     out["positions_after"] = int(st.pos[0].item())
     # ---- 16994-token prefill, and the 148-token suffix from a snapshot at 16846
+    progress("43-layer stack: prefill 16994, resume 148")
     ids = torch.as_tensor(synth.token_ids(wr.prompt, wl.vocab, wr.seed), device="cuda")
     P = wr.snapshot_at
     st.reset()
@@ -533,6 +540,7 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     # ------------------------------------------------------------ setup
+    progress("setup")
     layers = []
     w_cpu = None
     for l in range(args.weight_sets):
@@ -598,6 +606,7 @@ def main() -> int:
     dec_bytes = layer_decode_bytes(s)
     # ------------------------------------------------------------ decode timing
     if "decode" in want:
+        progress("decode")
         nl = len(layers)
         steps = args.steps
         if graph is not None:
@@ -621,6 +630,7 @@ def main() -> int:
 
     # ------------------------------------------------------------ prefill timing
     if "prefill" in want:
+        progress("prefill")
         # every call: fresh N(0, 1) rows at positions 0..2047 from an empty ring
         # (the input copy and position reset sit outside the timed events)
         hp = synth.hidden(T_pre, s.hidden, synth.WORKLOADS["layer_prefill_2048"].seed, device=dev)
@@ -659,6 +669,7 @@ def main() -> int:
     # ------------------------------------------------------------ batched decode
     batch = {}
     if "batch" in want:
+        progress("batched decode")
         # one token of each of B sequences per call (rings at position 128; the
         # projections, router and experts run over the B rows, weights read once)
         for B in (8, 32, 128):
@@ -686,6 +697,7 @@ def main() -> int:
 
     # ------------------------------------------------------------ lm_head + sampler
     if "lmhead" in want:
+        progress("lm_head + sampler")
         V = 129280
         hw = synth.head_weights(s, V, 1004, device=dev)
         logits = torch.empty(V, dtype=torch.float32, device=dev)
@@ -757,14 +769,17 @@ def main() -> int:
                                 "hbm_frac": round(lm_bytes / (us_lm * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                                   4)}
     if "stack" in want:
+        progress("43-layer stack")
         del layers, xs, ws
         torch.cuda.empty_cache()
         rec["stack43"] = bench_stack43(args.stack_decode_steps)
     if "cpu" in want:
+        progress("cpu baseline")
         rec["cpu_baseline"] = cpu_baseline(s, w_cpu, h_all, args.cpu_tokens)
         rec["cpu_baseline_prefill"] = cpu_baseline_prefill(
             s, w_cpu, args.cpu_prefill_tokens, synth.WORKLOADS["layer_prefill_2048"].seed)
     if "peaks" in want:
+        progress("peaks")
         rec["measured_peaks"] = measured_peaks(dev)
         if "roofline" in rec:
             rec["measured_peaks"]["roofline_frac_vs_copy"] = round(
