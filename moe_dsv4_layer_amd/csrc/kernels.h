@@ -208,8 +208,9 @@ struct RouteArgs {
   // optional user copies
   int* out_count; int* out_offset;
 };
-// entries ranked per chunk (one 1024-thread block each)
-constexpr int kRankChunk = 1024;
+// entries ranked per chunk (one block of kRankChunk threads each: little LDS,
+// so it fits beside the shared expert's GEMM blocks on the second stream)
+constexpr int kRankChunk = 256;
 int launch_route(const RouteArgs& r, Exec st);
 // x[t] += sum_j w[t,j] part[pos_of[t*k+j]] (fixed j order); part is fp32, or bf16
 // when part_bf16 (the bf16 path rounds each routed expert output to bf16).
