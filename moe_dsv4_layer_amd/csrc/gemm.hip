@@ -44,6 +44,10 @@
 #ifndef DS4G_BIG_BK
 #define DS4G_BIG_BK 64
 #endif
+// dense GEMMs may run 256 x 256 tiles from this many of them (one per CU)
+#ifndef DS4G_BIG_MIN_BLOCKS
+#define DS4G_BIG_MIN_BLOCKS 256
+#endif
 // 320 x 256 tiles for the residual-epilogue GEMMs over many rows (1: on)
 #ifndef DS4G_TALL_RESID
 #define DS4G_TALL_RESID 1
@@ -877,15 +881,22 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
       return launch_tall_resid(g, st);
     }
 #endif
-    if (big_blocks >= 512) {
-      // Rows past the last whole round of 256x256 tiles (one per CU) run as
-      // 128x128 tiles, a quarter of the work each, when they would fill less
-      // than half of one more round of big tiles.  Every element keeps its K
-      // order, so the split changes no bit of the result.
-      const long nt = (nout + 255) / 256, mt = (g.M + 255) / 256;
-      const long rem = (mt * nt) % 256;
-      const int mb = (int)((mt * nt / 256) * 256 / nt) * 256;   // rows in whole rounds
-      if (nsplit == 1 && g.epi != EPI_ROPE_QKV && rem > 0 && rem <= 128 && mb > 0 && mb < g.M) {
+    // Rows past the last whole round of 256x256 tiles (one per CU) run as
+    // 128x128 tiles, a quarter of the work each, when they would fill less
+    // than half of one more round of big tiles.  Every element keeps its K
+    // order, so the split changes no bit of the result.
+    const long bnt = (nout + 255) / 256, bmt = (g.M + 255) / 256;
+    const long brem = (bmt * bnt) % 256;
+    const int bmb = (int)((bmt * bnt / 256) * 256 / bnt) * 256;   // rows in whole rounds
+    const bool bsplit = nsplit == 1 && g.epi != EPI_ROPE_QKV && brem > 0 && brem <= 128 &&
+                        bmb > 0 && bmb < g.M;
+    // 256x256 tiles from 512 of them; from 256 when the rows past the whole
+    // round split off as above, or when split-K slices fill the round (the
+    // prefill router: 268 blocks of 256x256 beat 532 of 128x256)
+    if (big_blocks >= 512 || (big_blocks >= DS4G_BIG_MIN_BLOCKS && (bsplit || nsplit > 1))) {
+      const long nt = bnt;
+      const int mb = bmb;
+      if (bsplit) {
         GemmArgs hi = g, lo = g;
         hi.M = mb;
         lo.M = g.M - mb;

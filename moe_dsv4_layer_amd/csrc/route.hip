@@ -238,12 +238,14 @@ rank_chunk_kernel(const int* __restrict__ idx, int n, int E, int* __restrict__ r
 // takes EPB experts; thread (expert, group g) takes a contiguous run of the
 // chunks, all its loads in flight at once; the runs' sums are combined in
 // group order through LDS.
-constexpr int kPrefixEPB = 64;
-__global__ void __launch_bounds__(1024)
+// 256-thread blocks: beside the shared expert's GEMM blocks (8 waves, most
+// of a CU's registers) a 16-wave block would wait for an empty CU.
+constexpr int kPrefixEPB = 16;
+__global__ void __launch_bounds__(256)
 rank_prefix_kernel(int* __restrict__ chunk, int nchunk, int E, int* __restrict__ count) {
-  __shared__ int gsum[1024];
+  __shared__ int gsum[256];
   const int epb = min(E, kPrefixEPB);
-  const int G = 1024 / epb;                      // groups per expert
+  const int G = 256 / epb;                       // groups per expert
   const int el = threadIdx.x % epb, gidx = threadIdx.x / epb;
   const int e = blockIdx.x * epb + el;
   const bool on = gidx < G && e < E;
@@ -327,7 +329,7 @@ int launch_route(const RouteArgs& r, Exec st) {
   DS4G_LAUNCH(rank_chunk_kernel, dim3(nchunk), dim3(kRankChunk),
               (size_t)(kRankChunk / 64) * r.E * sizeof(int), st, r.topk_idx, nent, r.E, r.rank,
               r.chunk);
-  DS4G_LAUNCH(rank_prefix_kernel, dim3((r.E + kPrefixEPB - 1) / kPrefixEPB), dim3(1024), 0, st,
+  DS4G_LAUNCH(rank_prefix_kernel, dim3((r.E + kPrefixEPB - 1) / kPrefixEPB), dim3(256), 0, st,
               r.chunk, nchunk, r.E, r.count);
   DS4G_LAUNCH(route_scatter_kernel, dim3((nent + 255) / 256), dim3(256), 0, st, r);
   return 0;
