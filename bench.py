@@ -43,9 +43,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 # 12 steps; FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0, the factors that make a
 # 1 GiB device copy read 1 GiB and write 1 GiB).  Valid only for the decode
 # sources it was measured on: any change to them reports traffic as null.
-DECODE_TRAFFIC_BYTES = 274010564
+DECODE_TRAFFIC_BYTES = 274010879
 DECODE_TRAFFIC_SOURCES = ("api.hip", "attn.hip", "decode.hip", "dev.h", "kernels.h")
-DECODE_TRAFFIC_SHA1 = "d4a6a216f717d55bfc5bf371088def39b531cfed"
+DECODE_TRAFFIC_SHA1 = "1e70354a962e40d8443d93259f381d8069a2a69c"
 
 
 def progress(msg: str) -> None:
