@@ -817,6 +817,9 @@ int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long
   return 0;
 }
 
+#ifndef DS4G_TALL_ONE_ROUND   // 320 x 256 for 16-bit outputs that then fit one round (1: on)
+#define DS4G_TALL_ONE_ROUND 1
+#endif
 #if DS4G_TALL_RESID
 // 320 x 256 tiles, residual epilogue only (the staged 16-bit epilogue would
 // need more LDS than a CU has)
@@ -879,6 +882,27 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
         return launch_gemm(lo, mfma, wdtype_bf16, st);
       }
       return launch_tall_resid(g, st);
+    }
+#endif
+#if DS4G_TALL_ONE_ROUND
+    // fp16 / SwiGLU outputs (QKV-A, the shared gate/up) whose rows need one
+    // round and a few tiles more at 256 x 256 but fit one round at 320 x 256:
+    // every row in one launch, stored directly (the staged epilogue does not
+    // fit LDS beside a 320-row ring)
+    if ((g.epi == EPI_F16 || g.epi == EPI_SWIGLU_BF16) && !g.tiles && nsplit == 1 &&
+        g.M >= 4096) {
+      const long nt = (nout + 255) / 256;
+      if (((g.M + 319) / 320) * nt <= 256 && ((g.M + 255) / 256) * nt > 256) {
+        const dim3 grid((unsigned)((g.N + (dual ? 127 : 255)) / (dual ? 128 : 256)),
+                        (unsigned)((g.M + 319) / 320), 1), block(512);
+        if (g.epi == EPI_F16 && g.f16)
+          DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_F16, true, 64, false>), grid, block, 0, st, g);
+        else if (g.epi == EPI_F16)
+          DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_F16, false, 64, false>), grid, block, 0, st, g);
+        else
+          DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_SWIGLU_BF16, false, 64, false>), grid, block, 0, st, g);
+        return 0;
+      }
     }
 #endif
     // Rows past the last whole round of 256x256 tiles (one per CU) run as
