@@ -817,7 +817,7 @@ int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long
   return 0;
 }
 
-#ifndef DS4G_TALL_ONE_ROUND   // 320 x 256 for 16-bit outputs that then fit one round (1: on)
+#ifndef DS4G_TALL_ONE_ROUND   // 320 x 256 for fp16 / fp32 outputs that then fit one round (1: on)
 #define DS4G_TALL_ONE_ROUND 1
 #endif
 #if DS4G_TALL_RESID
@@ -885,22 +885,24 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
     }
 #endif
 #if DS4G_TALL_ONE_ROUND
-    // fp16 / SwiGLU outputs (QKV-A, the shared gate/up) whose rows need one
+    // fp16 and fp32 outputs (QKV-A, the split-K router) whose rows need one
     // round and a few tiles more at 256 x 256 but fit one round at 320 x 256:
     // every row in one launch, stored directly (the staged epilogue does not
-    // fit LDS beside a 320-row ring)
-    if ((g.epi == EPI_F16 || g.epi == EPI_SWIGLU_BF16) && !g.tiles && nsplit == 1 &&
-        g.M >= 4096) {
+    // fit LDS beside a 320-row ring).  Not the shared gate/up: beside the
+    // router on the second stream its 225-VGPR blocks left no room on their
+    // CUs for the small routing kernels, and the layer was slower.
+    if (((g.epi == EPI_F16 && nsplit == 1) || (g.epi == EPI_F32 && !g.f16)) && !dual &&
+        !g.tiles && g.M >= 4096) {
       const long nt = (nout + 255) / 256;
-      if (((g.M + 319) / 320) * nt <= 256 && ((g.M + 255) / 256) * nt > 256) {
-        const dim3 grid((unsigned)((g.N + (dual ? 127 : 255)) / (dual ? 128 : 256)),
-                        (unsigned)((g.M + 319) / 320), 1), block(512);
-        if (g.epi == EPI_F16 && g.f16)
+      if (((g.M + 319) / 320) * nt * nsplit <= 256 && ((g.M + 255) / 256) * nt * nsplit > 256) {
+        const dim3 grid((unsigned)((g.N + 255) / 256), (unsigned)((g.M + 319) / 320),
+                        (unsigned)nsplit), block(512);
+        if (g.epi == EPI_F32)
+          DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_F32, false, 64, false>), grid, block, 0, st, g);
+        else if (g.f16)
           DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_F16, true, 64, false>), grid, block, 0, st, g);
-        else if (g.epi == EPI_F16)
-          DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_F16, false, 64, false>), grid, block, 0, st, g);
         else
-          DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_SWIGLU_BF16, false, 64, false>), grid, block, 0, st, g);
+          DS4G_LAUNCH((gemm_dma_kernel<320, 256, 2, 4, 2, EPI_F16, false, 64, false>), grid, block, 0, st, g);
         return 0;
       }
     }
