@@ -236,11 +236,12 @@ rank_chunk_kernel(const int* __restrict__ idx, int n, int E, int* __restrict__ r
 // Per expert: the chunk counts turned into the entries of that expert in
 // earlier chunks (added in chunk order), and the expert's total.  A block
 // takes EPB experts; thread (expert, group g) takes a contiguous run of the
-// chunks, all its loads in flight at once; the runs' sums are combined in
-// group order through LDS.
+// chunks, loaded 8 at a time with all 8 in flight (the first 8 stay in
+// registers for the second pass, so a run of up to 8 chunks is read once);
+// the runs' sums are combined in group order through LDS.
 // 256-thread blocks: beside the shared expert's GEMM blocks (8 waves, most
 // of a CU's registers) a 16-wave block would wait for an empty CU.
-constexpr int kPrefixEPB = 16;
+constexpr int kPrefixEPB = 4;
 __global__ void __launch_bounds__(256)
 rank_prefix_kernel(int* __restrict__ chunk, int nchunk, int E, int* __restrict__ count) {
   __shared__ int gsum[256];
@@ -251,12 +252,19 @@ rank_prefix_kernel(int* __restrict__ chunk, int nchunk, int E, int* __restrict__
   const bool on = gidx < G && e < E;
   const int per = (nchunk + G - 1) / G;
   const int c0 = gidx * per, c1 = min(nchunk, c0 + per);
+  int first[8];
   int s = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) first[u] = 0;
   if (on) {
     for (int c = c0; c < c1; c += 8) {   // 8 loads in flight
       int v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = (c + u < c1) ? chunk[(long)(c + u) * E + e] : 0;
+      if (c == c0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) first[u] = v[u];
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u) s += v[u];
     }
@@ -269,8 +277,13 @@ rank_prefix_kernel(int* __restrict__ chunk, int nchunk, int E, int* __restrict__
   if (gidx == G - 1) count[e] = run + s;
   for (int c = c0; c < c1; c += 8) {
     int v[8];
+    if (c == c0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (c + u < c1) ? chunk[(long)(c + u) * E + e] : 0;
+      for (int u = 0; u < 8; ++u) v[u] = first[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (c + u < c1) ? chunk[(long)(c + u) * E + e] : 0;
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (c + u < c1) {
