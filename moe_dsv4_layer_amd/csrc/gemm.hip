@@ -295,6 +295,10 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, f32x16 (&acc)[F
     return;
   }
   if (EPI == EPI_RESID) {
+    // C += acc as one fp32 add per element done in L2 (no-return atomic):
+    // one tile owns each element, so it is a single read-modify-write with
+    // the rounding of the load / add / store it replaces, and the wave does
+    // not wait for C to arrive
     float* C = static_cast<float*>(g.C);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -302,16 +306,13 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, f32x16 (&acc)[F
       if (col >= g.N) continue;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        float old[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = min(row0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3), row1 - 1);
-          old[e] = C[(long)row * g.ldc + col];
-        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = row0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-          if (row < row1) C[(long)row * g.ldc + col] = old[e] + acc[i][j][e];
+          if (row < row1)
+            __builtin_amdgcn_global_atomic_fadd_f32(
+                (__attribute__((address_space(1))) float*)(C + (long)row * g.ldc + col),
+                acc[i][j][e]);
         }
       }
     }
