@@ -818,8 +818,8 @@ int launch_splitk_reduce(const float* part, const float* part2, int nsplit, long
   return 0;
 }
 
-#ifndef DS4G_TALL_ONE_ROUND   // 320 x 256 for fp16 / fp32 outputs that then fit one round (1: on)
-#define DS4G_TALL_ONE_ROUND 1
+#ifndef DS4G_TALL_SINGLE_PASS   // 320 x 256 for fp16 / fp32 outputs that then fit one round (1: on)
+#define DS4G_TALL_SINGLE_PASS 1
 #endif
 #if DS4G_TALL_RESID
 // 320 x 256 tiles, residual epilogue only (the staged 16-bit epilogue would
@@ -885,7 +885,7 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
       return launch_tall_resid(g, st);
     }
 #endif
-#if DS4G_TALL_ONE_ROUND
+#if DS4G_TALL_SINGLE_PASS
     // fp16 and fp32 outputs (QKV-A, the split-K router) whose rows need one
     // round and a few tiles more at 256 x 256 but fit one round at 320 x 256:
     // every row in one launch, stored directly (the staged epilogue does not

@@ -238,8 +238,8 @@ def _routing_bufs(T, k, device="cuda"):
 
 
 def _window_rows(label, s, got_out, xin, r, gpu_topk, rows):
-    """Per-row parity of oracle window rows (survey protocol for the
-    43-layer stacks): a row whose expert set differs from the oracle's must
+    """Per-row parity of oracle window rows of the 43-layer stacks, whose
+    prompts are not redrawn for margins: a row whose expert set differs from the oracle's must
     have an oracle router margin below 1e-3 (a near-tie; listed, and left
     out of the error figures); every other row's layer increment must be
     within the layer tolerance.  Returns (rel_l2 over the kept rows, flips)."""
