@@ -258,8 +258,10 @@ def _window_rows(label, s, got_out, xin, r, gpu_topk, rows):
 
 def test_stack43_16994_chunked_and_oracle_windows(stack43):
     """The 16994-token prefill's own tile shapes: the one-shot prefill runs
-    W_o and the shared expert on 256x256 tiles and the routed experts on
-    256-row tiles; 2048-token chunks run 128x128 and 64-row tiles.  Every
+    W_o and the shared down on 320x256 tiles over their whole rounds, QKV-A
+    and the split-K router in one pass of 320x256 tiles, QKV-B and the shared
+    gate/up on 256x256 tiles (with 128x128 remainders) and the routed experts
+    on 256-row tiles; 2048-token chunks run 128x128 and 64-row tiles.  Every
     output element sums its K products in one order whatever the tiling, so
     the two must agree bit for bit (final hidden state and every ring).
 
