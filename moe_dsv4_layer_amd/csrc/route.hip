@@ -111,23 +111,26 @@ template int launch_rmsnorm_rows<float>(const float*, int, int, const float*, fl
 // The logits arrive as nsplit partial sums (split-K GEMM); they are added in
 // split order, so the result does not depend on scheduling.  lsum (the
 // summed logits) is written only when a caller asked for them.
+// NV = E/64 rounded up to a power of two: only the logits a lane holds take
+// registers, so more waves fit beside the GEMM blocks of the second stream.
+template <int NV>
 __global__ void __launch_bounds__(256)
 topk_kernel(const float* __restrict__ logits, int nsplit, float* __restrict__ lsum, int T, int E,
             int k, int* __restrict__ idx, float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  // the partial sums of all 8 experts of a lane, 4 splits at a time, are
+  // the partial sums of all NV experts of a lane, 4 splits at a time, are
   // loaded before any is added; the adds run in split order
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = 0.f;
   for (int z0 = 0; z0 < nsplit; z0 += 4) {
-    float p[4][8];
+    float p[4][NV];
 #pragma unroll
     for (int zz = 0; zz < 4; ++zz)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NV; ++i) {
         const int e = lane + 64 * i;
         p[zz][i] = (z0 + zz < nsplit && e < E) ? logits[((long)(z0 + zz) * T + t) * E + e] : 0.f;
       }
@@ -135,16 +138,17 @@ topk_kernel(const float* __restrict__ logits, int nsplit, float* __restrict__ ls
     for (int zz = 0; zz < 4; ++zz)
       if (z0 + zz < nsplit) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] += p[zz][i];
+        for (int i = 0; i < NV; ++i) v[i] += p[zz][i];
       }
   }
   if (lsum) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NV; ++i)
       if (lane + 64 * i < E) lsum[(long)t * E + lane + 64 * i] = v[i];
   }
-  // route_wave takes a NaN score as -inf and keeps every index in [0, E)
-  route_wave(v, E, k, idx + (long)t * k, wts + (long)t * k);
+  // route_topk (route_wave's selection at this NV) takes a NaN score as
+  // -inf and keeps every index in [0, E)
+  route_topk<NV>(v, E, k, idx + (long)t * k, wts + (long)t * k);
 }
 
 // ------------------------------------------------------------ block scans
@@ -335,8 +339,14 @@ route_scatter_kernel(RouteArgs r) {
 
 int launch_route(const RouteArgs& r, Exec st) {
   if (r.E > 512 || r.k > 8) return -1;
-  DS4G_LAUNCH(topk_kernel, dim3((r.T + 3) / 4), dim3(256), 0, st, r.logits, r.nsplit,
-                     r.logits_sum, r.T, r.E, r.k, r.topk_idx, r.topk_w);
+#define DS4G_TOPK(NV)                                                                     \
+  DS4G_LAUNCH(topk_kernel<NV>, dim3((r.T + 3) / 4), dim3(256), 0, st, r.logits, r.nsplit, \
+              r.logits_sum, r.T, r.E, r.k, r.topk_idx, r.topk_w)
+  if (r.E <= 64) DS4G_TOPK(1);
+  else if (r.E <= 128) DS4G_TOPK(2);
+  else if (r.E <= 256) DS4G_TOPK(4);
+  else DS4G_TOPK(8);
+#undef DS4G_TOPK
   const int nent = r.T * r.k;
   const int nchunk = (nent + kRankChunk - 1) / kRankChunk;
   DS4G_LAUNCH(rank_chunk_kernel, dim3(nchunk), dim3(kRankChunk),
