@@ -220,7 +220,8 @@ def test_support_matrix_sweep():
         c = _cfg(hidden=hidden, head_dim=dh, window=window, n_experts=E, top_k=k,
                  ffn_inter=inter, shared_inter=inter, wdtype=wd, rope_dim=rope, n_heads=heads)
         for T, mode in ((1, ds4g.MODE_DECODE), (1, ds4g.MODE_PREFILL), (300, ds4g.MODE_PREFILL),
-                        (16994, ds4g.MODE_PREFILL), (8, ds4g.MODE_DECODE_BATCH),
+                        (16994, ds4g.MODE_PREFILL), (20480, ds4g.MODE_PREFILL),
+                        (8, ds4g.MODE_DECODE_BATCH),
                         (128, ds4g.MODE_DECODE_BATCH)):
             st = ds4g.layer_supported(c, T, mode)
             want = _documented(c, T, mode)
