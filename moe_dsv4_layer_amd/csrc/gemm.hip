@@ -950,9 +950,12 @@ int launch_gemm(const GemmArgs& g0, bool mfma, int wdtype_bf16, Exec st) {
     const long blocks = ((g.M + 127) / 128) * ((nout + 127) / 128) * nsplit;
     // a short prefill (a few row tiles) fills few CUs: 64-row tiles give
     // twice the blocks, each streaming a quarter fewer operand bytes.  Not
-    // for SwiGLU: the shared gate/up runs on the second stream, where more
-    // blocks only crowd the routing kernels.
-    if (!dual && blocks <= 192 && g.M > 64 && g.M <= 1024) return launch_dma_cfg<64, 128, 2, 2, 3>(g, st);
+    // the shared expert's GEMMs (SwiGLU, and the residual add on bf16
+    // operands): they run on the second stream, where more blocks only
+    // crowd the kernels of the critical path.
+    const bool shared_expert = dual || (g.epi == EPI_RESID && !g.f16);
+    if (!shared_expert && blocks <= 192 && g.M > 64 && g.M <= 1024)
+      return launch_dma_cfg<64, 128, 2, 2, 3>(g, st);
     // one block per CU either way: spend the LDS on a deeper pipeline
     if (blocks <= 256) return launch_dma_cfg<128, 128, 2, 2, 3>(g, st);
     return launch_dma_cfg<128, 128, 2, 2, 2>(g, st);
