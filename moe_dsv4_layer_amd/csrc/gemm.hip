@@ -228,7 +228,7 @@ __device__ __forceinline__ void epi_store_t(const GemmArgs& g, int row, int col,
 // before any of them is stored, so the loads overlap instead of alternating
 // with the stores.  A column factor (colscale) multiplies the accumulator
 // first: a power of two, so it changes no bit of the significand.
-template <int EPI, int FM, int FN>
+template <int EPI, int FM, int FN, bool ATOMIC = true>
 __device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, f32x16 (&acc)[FM][FN],
                                               int row0, int row1, int col0, int lane) {
   constexpr bool DUAL = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_F32);
@@ -295,10 +295,12 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, f32x16 (&acc)[F
     return;
   }
   if (EPI == EPI_RESID) {
-    // C += acc as one fp32 add per element done in L2 (no-return atomic):
-    // one tile owns each element, so it is a single read-modify-write with
-    // the rounding of the load / add / store it replaces, and the wave does
-    // not wait for C to arrive
+    // C += acc.  ATOMIC: one fp32 add per element done in L2 (no-return
+    // atomic): one tile owns each element, so it is a single read-modify-write
+    // with the rounding of the load / add / store, and the wave does not wait
+    // for C to arrive.  It helps the shared down (beside the routed experts)
+    // and the short prefills' 64-row tiles; W_o's big fp16-operand tiles keep
+    // the load / add / store, which measured faster there.
     float* C = static_cast<float*>(g.C);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -306,13 +308,27 @@ __device__ __forceinline__ void mfma_epilogue(const GemmArgs& g, f32x16 (&acc)[F
       if (col >= g.N) continue;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        if constexpr (ATOMIC) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = row0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-          if (row < row1)
-            __builtin_amdgcn_global_atomic_fadd_f32(
-                (__attribute__((address_space(1))) float*)(C + (long)row * g.ldc + col),
-                acc[i][j][e]);
+          for (int e = 0; e < 16; ++e) {
+            const int row = row0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+            if (row < row1)
+              __builtin_amdgcn_global_atomic_fadd_f32(
+                  (__attribute__((address_space(1))) float*)(C + (long)row * g.ldc + col),
+                  acc[i][j][e]);
+          }
+        } else {
+          float old[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = min(row0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3), row1 - 1);
+            old[e] = C[(long)row * g.ldc + col];
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = row0 + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+            if (row < row1) C[(long)row * g.ldc + col] = old[e] + acc[i][j][e];
+          }
         }
       }
     }
@@ -672,7 +688,7 @@ gemm_dma_kernel(GemmArgs g) {
         ge, acc, reinterpret_cast<unsigned char*>(smem_all), ti.row0, ti.row1, ncol0, wm * TM,
         wn * (DUAL ? TN / 2 : TN), lane);
   } else {
-    mfma_epilogue<EPI, FM, FN>(ge, acc, ti.row0 + wm * TM, ti.row1,
+    mfma_epilogue<EPI, FM, FN, (!F16 || BM < 128)>(ge, acc, ti.row0 + wm * TM, ti.row1,
                                ncol0 + wn * (DUAL ? TN / 2 : TN), lane);
   }
 }
