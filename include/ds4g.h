@@ -29,9 +29,9 @@
  *     (DS4G_BF16: raw bf16 bits; DS4G_F32: float).  Expert stacks are
  *     [n_experts, out, in].  Gains (norm weights) are in wdtype too.
  *   - The residual stream x is fp32, updated in place; on the matrix-core
- *     path the residual adds of W_o and the shared down are device-memory
- *     float atomics (one per element), so x must be ordinary device memory
- *     (hipMalloc), not host or managed memory.
+ *     path some residual adds (the shared down, short prefills) are
+ *     device-memory float atomics (one per element), so x must be ordinary
+ *     device memory (hipMalloc), not host or managed memory.
  *   - The KV ring holds K (after RoPE) and V as fp16 (IEEE binary16)
  *     [window, head_dim]; position p lives in slot p % window; *pos (device
  *     int64) is the position of the next token and is advanced by every call.
