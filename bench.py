@@ -481,6 +481,72 @@ def bench_stack43(decode_steps: int) -> dict:
     return out
 
 
+def ab_prefill(ds4g, synth, torch, other: str, reps: int, tokens) -> dict:
+    """Two builds of the library in one process: the in-tree one (A) and
+    `other` (B, e.g. built with different launch-shape macros through
+    moe_dsv4_layer_amd/build.py's build(out=..., defines=[...])).  One
+    full-size layer prefill per token count (expert inter 512 for counts
+    above 2048, as in the 43-layer stack, else 1024), calls alternating
+    A B B A ..., medians of `reps` calls each, outputs compared bit for bit.
+    Separate processes on one box differ by 1-3% from run to run; this
+    resolves differences down to about 0.3-1%."""
+    import ctypes, dataclasses, shutil, tempfile
+    la = ds4g.lib
+    cp = os.path.join(tempfile.mkdtemp(), "libds4g_b.so")   # its own copy: its own handle
+    shutil.copy(other, cp)
+    lb = ctypes.CDLL(cp)
+    for fn in ("ds4g_workspace_bytes", "ds4g_layer_prefill"):
+        fa, fb = getattr(la, fn), getattr(lb, fn)
+        fb.restype, fb.argtypes = fa.restype, fa.argtypes
+    out = {}
+    try:
+        for T in tokens:
+            inter = 512 if T > 2048 else 1024
+            s = dataclasses.replace(synth.WORKLOADS["layer_decode"].layer, ffn_inter=inter)
+            cfg = ds4g.make_cfg(s)
+            w = synth.layer_weights(s, 1005, layer=0, device="cuda")
+            cw = ds4g.make_weights(w)
+            img = ds4g.make_f16_images(cfg, cw, "cuda")
+            cwi = ds4g.make_weights(w, img)
+            rk = torch.zeros((s.window, s.head_dim), dtype=torch.float16, device="cuda")
+            rv = torch.zeros_like(rk)
+            pos = torch.zeros(1, dtype=torch.int64, device="cuda")
+            ring = ds4g.make_ring(rk, rv, pos)
+            nb = max(la.ds4g_workspace_bytes(ctypes.byref(cfg), T, 0),
+                     lb.ds4g_workspace_bytes(ctypes.byref(cfg), T, 0))
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            h = synth.hidden(T, s.hidden, 1005, device="cuda")
+            x = torch.empty_like(h)
+            st = torch.cuda.current_stream()
+            res, last = {"A": [], "B": []}, {}
+            order = ["A", "B"]
+            for r in range(reps):
+                order += ["A", "B"] if r % 2 == 0 else ["B", "A"]
+            for i, who in enumerate(order):
+                ds4g.lib = la if who == "A" else lb
+                pos.zero_()
+                x.copy_(h)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                ds4g.layer_prefill(cfg, cwi, ring, x, T, ws)
+                e1.record(st)
+                torch.cuda.synchronize()
+                if i >= 2:
+                    res[who].append(e0.elapsed_time(e1))
+                last[who] = x.clone()
+            ds4g.lib = la
+            ma = sorted(res["A"])[len(res["A"]) // 2]
+            mb = sorted(res["B"])[len(res["B"]) // 2]
+            out[str(T)] = {"A_ms": round(ma, 4), "B_ms": round(mb, 4), "B_over_A": round(mb / ma, 4),
+                           "outputs_equal": bool(torch.equal(last["A"], last["B"]))}
+            progress(f"ab T={T}: {out[str(T)]}")
+            del w, cw, img, cwi, ws, h, x, last
+            torch.cuda.empty_cache()
+    finally:
+        ds4g.lib = la
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,6 +569,12 @@ def main() -> int:
     ap.add_argument("--probes", action="store_true",
                     help="only run the calibration probes (launch cost, read rate by access "
                          "shape, Infinity Cache reuse, the vendor GEMM) and print their JSON line")
+    ap.add_argument("--ab-lib", default="",
+                    help="only compare the in-tree library with this other build of it on "
+                         "one-layer prefills, alternating call by call in this process, and "
+                         "print their JSON line")
+    ap.add_argument("--ab-reps", type=int, default=10)
+    ap.add_argument("--ab-tokens", default="16994,2048,512,148")
     args = ap.parse_args()
     want = set(args.sections.split(","))
     if args.no_stack:
@@ -529,6 +601,11 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
                           "copies": 5}))
+        return 0
+    if args.ab_lib:
+        toks = [int(t) for t in args.ab_tokens.split(",") if t]
+        print(json.dumps({"ab_prefill": ab_prefill(ds4g, synth, torch, args.ab_lib, args.ab_reps,
+                                                   toks)}))
         return 0
     if args.probes:
         print(json.dumps({"probes": calibration_probes(dev),
